@@ -1,0 +1,222 @@
+"""Decode layer-step benchmark of the hybrid sparse-attention hot path on one MI355X.
+
+Workload (c4_decode_1m): 4 sequences x 1,048,576 tokens, 262,144 C4 entries
+each, 64 heads over a 576-wide latent (value 512), window 128, indexer
+64 heads x 128, top-512; synthetic seeded inputs resident in HBM.
+
+One step = one decode layer-step: indexer scores over every C4 key + radix
+top-512 select (hsa_index_topk), fused SWA + selected-C4 attention with
+split-KV merge (hsa_attn_decode), and, on every 4th step, the compression of
+the 4 just-completed 4-token blocks (hsa_compress).  Two copies of the
+indexer inputs alternate between steps so the 268 MB key stream is larger
+than the on-die cache across a pair of steps.
+
+Prints ONE JSON line (rank 0).  --gpus N > 1 is not supported: the path is
+measured on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "hybrid-attn decode layer-steps/s + achieved HBM GB/s (C4 top-512, 1M ctx)"
+HBM_PEAK_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "score_kernel_c4_decode_1m_pmc.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time over which the oracle layer-step is repeated")
+    return ap.parse_args()
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def score_kernel_sources():
+    c = os.path.join(ROOT, "hybrid_sparse_compressed_amd", "csrc")
+    return [os.path.join(c, f) for f in ("index_topk.hip", "hsa_common.hpp")]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the hot path on one GPU only; --gpus %d is not supported "
+              "(the multi-GPU sharding is a design note, not a built path)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hybrid_sparse_compressed_amd as hsa
+    from hybrid_sparse_compressed_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = "c4_decode_1m"
+    w = workloads.c4_decode(name, dev)
+    c = w["cfg"]
+    B, S, k, H, d_qk, d_v, W = c["B"], w["S"], c["k"], c["H"], c["d_qk"], c["d_v"], c["W"]
+    H_I, d_I = c["H_I"], c["d_I"]
+    # second copy of the indexer inputs (different seed), alternated per step
+    g2 = torch.Generator(device=dev).manual_seed(c["seed"] + 100)
+    k_idx2 = torch.randn(w["k_idx"].shape, generator=g2, device=dev).to(torch.bfloat16)
+    q_idx2 = torch.randn(w["q_idx"].shape, generator=g2, device=dev).to(torch.bfloat16)
+    workloads.plant_duplicate_rows(k_idx2, c["dup_frac"], workloads._Draw(c["seed"] + 100, dev))
+    sets = [(w["q_idx"], w["k_idx"]), (q_idx2, k_idx2)]
+    # decode-time compression of the block each sequence just completed
+    xb = torch.randn((B, 4, d_qk), generator=g2, device=dev).to(torch.bfloat16)
+    gb = torch.randn((B, 4, d_qk), generator=g2, device=dev).to(torch.bfloat16)
+    bb = (torch.randn((4, d_qk), generator=g2, device=dev) * 0.1).to(torch.bfloat16)
+    cb = torch.empty((B, 1, d_qk), dtype=torch.bfloat16, device=dev)
+
+    stream = torch.cuda.current_stream()
+    scores = torch.empty((B, S), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws_topk = torch.zeros(max(256, hsa.lib.hsa_index_topk_workspace_size(B, S, k)),
+                          dtype=torch.uint8, device=dev)
+    ws_attn = torch.zeros(max(256, hsa.lib.hsa_attn_decode_workspace_size(B, H, d_v, W + k)),
+                          dtype=torch.uint8, device=dev)
+
+    def step(i):
+        qi, ki = sets[i & 1]
+        if i % 4 == 3:
+            hsa.hsa_compress(xb, gb, bb, 4, out=cb)
+        hsa.hsa_index_topk(qi, ki, w["n_cand"], k, scores=scores, topk_idx=idx, workspace=ws_topk)
+        hsa.hsa_attn_decode(w["q"], w["swa_kv"], w["swa_len"], w["comp_kv"], w["comp_len"],
+                            w["scale"], d_v, comp_idx=idx, out=out, lse=lse, workspace=ws_attn)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    fams = {"compress": hsa.HSA_PROF_COMPRESS, "score": hsa.HSA_PROF_SCORE,
+            "select": hsa.HSA_PROF_SELECT, "attn": hsa.HSA_PROF_ATTN, "merge": hsa.HSA_PROF_MERGE}
+
+    # timed region (value): nothing but the steps between the two synchronisations
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+
+    # same steps again with the library's event pairs around every kernel launch
+    hsa.hsa_profile_read(hsa.HSA_PROF_SCORE, reset=True)
+    hsa.hsa_profile_enable(sum(fams.values()))
+    torch.cuda.synchronize()
+    ti = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    hsa.hsa_profile_enable(0)
+    ms_instr = (time.perf_counter() - ti) * 1000.0 / args.steps
+    breakdown = {}
+    for nm, f in fams.items():
+        tot, n = hsa.hsa_profile_read(f)
+        breakdown[nm] = {"avg_us": round(1000.0 * tot / n, 3) if n else None, "launches": n}
+
+    # roofline of the dominant kernel (indexer scoring): algorithmic bytes per launch
+    alg_bytes = B * S * d_I * 2 + B * H_I * d_I * 2
+    score_us = breakdown["score"]["avg_us"]
+    achieved = alg_bytes / (score_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        pmc = json.load(open(PMC_FILE))
+        if pmc.get("source_hash") == source_hash(score_kernel_sources()):
+            traffic = pmc.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "score_kernel (indexer scores + first-digit histogram)",
+                "alg_bytes_per_launch": alg_bytes}
+
+    step_bytes = (B * S * d_I * 2 + B * (W + k) * d_qk * 2 + B * H * d_qk * 2 + B * H * d_v * 2
+                  + B * H_I * d_I * 2 + B * k * 4)
+    value = 1000.0 / ms_per_step
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_instrumented": round(ms_instr, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1); 1% duplicated indexer key rows)",
+        "config": {"workload": name, "batch": B, "context": c["L"], "c4_entries": S, "heads": H,
+                   "latent": d_qk, "value_dim": d_v, "window": W, "topk": k,
+                   "indexer": "%dx%d" % (H_I, d_I)},
+        "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "alg_bytes_per_step": step_bytes,
+        "breakdown_us": breakdown,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, min_seconds):
+    """The oracle's whole decode layer-step (all sequences), repeated for ~min_seconds."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    c = w["cfg"]
+    k = c["k"]
+    q_idx, k_idx = w["q_idx"].cpu(), w["k_idx"].cpu()
+    q, swa, comp = w["q"].cpu(), w["swa_kv"].cpu(), w["comp_kv"].cpu()
+    n_cand = w["n_cand"].cpu().numpy()
+    swa_len, comp_len = w["swa_len"].cpu().numpy(), w["comp_len"].cpu().numpy()
+    reps, t = 0, time.perf_counter()
+    while True:
+        sc = oracle.index_scores(q_idx, k_idx, n_cand)
+        idx = oracle.topk(sc.astype(np.float32), n_cand, k)
+        oracle.attn_decode(q, swa, swa_len, comp, comp_len, w["scale"], c["d_v"], comp_idx=idx)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return {"value": round(reps / dt, 5), "unit": "layer-steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d repetition(s) of the whole c4_decode_1m layer-step (fp64 scores over all "
+                      "4 x 262,144 C4 keys, select, attention) in %.1f s" % (reps, dt)}
+
+
+if __name__ == "__main__":
+    main()

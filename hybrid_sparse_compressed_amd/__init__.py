@@ -1,0 +1,28 @@
+"""hybrid_sparse_compressed_amd -- MI355X (gfx950) hybrid sparse-attention hot path.
+
+The compute lives in libhsa_attn.so (hand-written HIP kernels behind a C ABI,
+declared in include/hsa_attn.h).  This package holds that library's sources
+(csrc/), its build script (build.py), a ctypes binding with the C entry
+points' names (_binding.py) and the seeded synthetic workload generators
+(workloads.py, which holds no arithmetic of the method).
+
+Touching any binding name (``hsa_compress`` ...) loads the library and raises
+ImportError if it has not been built; there is no fallback path.
+"""
+
+_BINDING_NAMES = (
+    "EXPORTED", "HSA_BF16", "HSA_F32", "HsaError", "Workspace", "hsa_attn_decode",
+    "hsa_attn_prefill", "hsa_compress", "hsa_index_topk", "lib", "strerror",
+    "hsa_profile_enable", "hsa_profile_read", "HSA_PROF_COMPRESS", "HSA_PROF_SCORE",
+    "HSA_PROF_SELECT", "HSA_PROF_ATTN", "HSA_PROF_MERGE",
+)
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import _binding
+
+        return getattr(_binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,253 @@
+"""ctypes binding of libhsa_attn.so.
+
+Argument marshalling only: these functions check tensor placement, dtype and
+contiguity, allocate outputs / workspaces with torch when the caller passes
+none, and call the C entry point of the same name on the current HIP stream.
+Every step of the computation runs in the library's kernels.  If the shared
+library is missing the import fails loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhsa_attn.so")
+
+HSA_OK, HSA_ERR_INVALID_ARG, HSA_ERR_UNSUPPORTED, HSA_ERR_WORKSPACE, HSA_ERR_HIP = range(5)
+HSA_F32, HSA_BF16 = 0, 1
+
+EXPORTED = (
+    "hsa_strerror", "hsa_version", "hsa_compress", "hsa_index_topk_workspace_size",
+    "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
+    "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_profile_enable",
+    "hsa_profile_read",
+)
+HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
+
+
+class HsaError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__("%s failed: %s (%d)" % (fn, strerror(code), code))
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libhsa_attn.so is not built (expected at %s); run "
+            "`python -m hybrid_sparse_compressed_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, U32, SZ, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t,
+                          ctypes.c_float)
+    I = ctypes.c_int
+    lib.hsa_strerror.argtypes = [I]
+    lib.hsa_strerror.restype = ctypes.c_char_p
+    lib.hsa_version.argtypes = []
+    lib.hsa_version.restype = I
+    lib.hsa_compress.argtypes = [I, P, P, P, P, I32, I32, I32, I32, P]
+    lib.hsa_compress.restype = I
+    lib.hsa_index_topk_workspace_size.argtypes = [I32, I32, I32]
+    lib.hsa_index_topk_workspace_size.restype = SZ
+    lib.hsa_index_topk.argtypes = [I, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, U32, P, SZ, P]
+    lib.hsa_index_topk.restype = I
+    lib.hsa_attn_decode_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.hsa_attn_decode_workspace_size.restype = SZ
+    lib.hsa_attn_decode.argtypes = [I, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                    F, P, SZ, P]
+    lib.hsa_attn_decode.restype = I
+    lib.hsa_attn_prefill_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.hsa_attn_prefill_workspace_size.restype = SZ
+    lib.hsa_attn_prefill.argtypes = [I, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
+                                     I32, I32, I32, F, P, SZ, P]
+    lib.hsa_attn_prefill.restype = I
+    lib.hsa_profile_enable.argtypes = [ctypes.c_uint]
+    lib.hsa_profile_enable.restype = I
+    lib.hsa_profile_read.argtypes = [ctypes.c_uint, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_longlong), I]
+    lib.hsa_profile_read.restype = I
+    return lib
+
+
+lib = _load()
+
+
+def strerror(code: int) -> str:
+    return lib.hsa_strerror(int(code)).decode()
+
+
+def _check(fn, code):
+    if code != HSA_OK:
+        raise HsaError(fn, code)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HSA_F32
+    if t.dtype == torch.bfloat16:
+        return HSA_BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libhsa_attn must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libhsa_attn must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        t = torch.as_tensor(t, dtype=torch.int32)
+    if t.dtype != torch.int32:
+        raise TypeError("index/length tensors must be int32")
+    return t.to(device).contiguous()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Workspace:
+    """A zero-filled device buffer reused across calls (per device and stream).
+
+    The top-k path needs its histogram and counters zeroed before the first
+    call; every call that completes leaves them zeroed again, so one
+    allocation serves all later calls made in stream order."""
+
+    _cache: dict = {}
+
+    @classmethod
+    def get(cls, nbytes: int, device, stream) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        key = (str(device), stream.cuda_stream if stream is not None else 0)
+        buf = cls._cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            cls._cache[key] = buf
+        return buf
+
+
+def hsa_compress(x, gate, bias, m, out=None, stream=None):
+    """out[b,i,:] = sum_j softmax_j(gate[b,m*i+j,:] + bias[j,:]) * x[b,m*i+j,:]."""
+    B, T, D = x.shape
+    if out is None:
+        out = torch.empty((B, T // m, D), dtype=x.dtype, device=x.device)
+    for t in (gate, bias, out):
+        if t.dtype != x.dtype:
+            raise TypeError("hsa_compress: all tensors must share one dtype")
+    if gate.shape != x.shape or tuple(bias.shape) != (m, D) or tuple(out.shape) != (B, T // m, D):
+        raise ValueError("hsa_compress: shape mismatch")
+    _check("hsa_compress", lib.hsa_compress(_dt(x), _ptr(x), _ptr(gate), _ptr(bias), _ptr(out),
+                                            B, T, D, m, _stream(stream)))
+    return out
+
+
+def hsa_index_topk(q_idx, k_idx, n_cand, k, q_seq=None, scores=None, topk_idx=None,
+                   workspace=None, stream=None, S_max=None):
+    """Indexer scores + top-k.  q_idx=None selects from the given `scores`.
+
+    q_idx: [Nq, H_I, d_I]; k_idx: [B, S_max, d_I]; n_cand: [Nq] int32.
+    Returns (scores [Nq, S_max] fp32, topk_idx [Nq, k] int32)."""
+    if q_idx is not None:
+        Nq, H_I, d_I = q_idx.shape
+        B, S_max, d2 = k_idx.shape
+        if d2 != d_I or k_idx.dtype != q_idx.dtype:
+            raise ValueError("hsa_index_topk: q_idx / k_idx mismatch")
+        dev = q_idx.device
+        dt = _dt(q_idx)
+    else:
+        if scores is None:
+            raise ValueError("hsa_index_topk: select-only mode needs scores")
+        Nq, S_max = scores.shape
+        B, H_I, d_I, dev, dt = 1, 1, 1, scores.device, HSA_F32
+    n_cand = _i32(n_cand, dev)
+    q_seq = _i32(q_seq, dev)
+    if scores is None:
+        scores = torch.empty((Nq, S_max), dtype=torch.float32, device=dev)
+    if scores.dtype != torch.float32 or tuple(scores.shape) != (Nq, S_max):
+        raise ValueError("hsa_index_topk: scores must be fp32 [Nq, S_max]")
+    if topk_idx is None:
+        topk_idx = torch.empty((Nq, k), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream() if stream is None else stream
+    need = lib.hsa_index_topk_workspace_size(Nq, S_max, k)
+    if workspace is None:
+        workspace = Workspace.get(need, dev, st)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hsa_index_topk", lib.hsa_index_topk(
+        dt, _ptr(q_idx), _ptr(k_idx), B, _ptr(q_seq), _ptr(n_cand), _ptr(scores),
+        _ptr(topk_idx), Nq, H_I, d_I, S_max, k, 0, _ptr(workspace), wsz, _stream(st)))
+    return scores, topk_idx
+
+
+def hsa_attn_decode(q, swa_kv, swa_len, comp_kv, comp_len, scale, d_v, comp_idx=None, out=None,
+                    lse=None, workspace=None, stream=None):
+    """One softmax over the SWA ring plus sparse (comp_idx) or dense compressed rows.
+
+    q: [B, H, d_qk]; swa_kv: [B, W, d_qk]; comp_kv: [B, S_max, d_qk]; comp_idx: [B, k]
+    int32 or None.  Returns (out [B, H, d_v], lse [B, H] fp32)."""
+    B, H, d_qk = q.shape
+    W = swa_kv.shape[1]
+    S_max = comp_kv.shape[1]
+    dev = q.device
+    swa_len, comp_len, comp_idx = _i32(swa_len, dev), _i32(comp_len, dev), _i32(comp_idx, dev)
+    k = 0 if comp_idx is None else comp_idx.shape[1]
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream() if stream is None else stream
+    need = lib.hsa_attn_decode_workspace_size(B, H, d_v, W + (k if comp_idx is not None else S_max))
+    if workspace is None:
+        workspace = Workspace.get(need, dev, st)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hsa_attn_decode", lib.hsa_attn_decode(
+        _dt(q), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_idx),
+        _ptr(comp_len), _ptr(out), _ptr(lse), B, H, d_qk, d_v, W, S_max, k, float(scale),
+        _ptr(workspace), wsz, _stream(st)))
+    return out, lse
+
+
+def hsa_attn_prefill(q, kv, comp_kv, q_start, W, m, scale, d_v, comp_idx=None, out=None,
+                     lse=None, stream=None):
+    """Chunked prefill: causal SWA window plus sparse (comp_idx) or dense visible rows.
+
+    q: [n_seq, n_q, H, d_qk]; kv: [n_seq, T, d_qk]; comp_kv: [n_seq, S_max, d_qk];
+    comp_idx: [n_seq*n_q, k] int32 or None.  Returns (out [n_seq, n_q, H, d_v], lse)."""
+    n_seq, n_q, H, d_qk = q.shape
+    T = kv.shape[1]
+    S_max = comp_kv.shape[1]
+    dev = q.device
+    comp_idx = _i32(comp_idx, dev)
+    k = 0 if comp_idx is None else comp_idx.shape[1]
+    if out is None:
+        out = torch.empty((n_seq, n_q, H, d_v), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((n_seq * n_q, H), dtype=torch.float32, device=dev)
+    _check("hsa_attn_prefill", lib.hsa_attn_prefill(
+        _dt(q), _ptr(q), _ptr(kv), _ptr(comp_kv), _ptr(comp_idx), _ptr(out), _ptr(lse), n_seq,
+        n_q, q_start, T, H, d_qk, d_v, W, S_max, k, m, float(scale), None, 0, _stream(stream)))
+    return out, lse
+
+
+def hsa_profile_enable(family_mask: int) -> None:
+    """Arm event timing for the kernel families in family_mask (0 disarms)."""
+    _check("hsa_profile_enable", lib.hsa_profile_enable(int(family_mask)))
+
+
+def hsa_profile_read(family: int, reset: bool = False):
+    """(total milliseconds, launch count) recorded so far for one kernel family."""
+    ms, n = ctypes.c_double(), ctypes.c_longlong()
+    _check("hsa_profile_read", lib.hsa_profile_read(int(family), ctypes.byref(ms), ctypes.byref(n),
+                                                    1 if reset else 0))
+    return ms.value, n.value

@@ -1,0 +1,147 @@
+// api.hip -- the extern "C" boundary of libhsa_attn.so.  Every entry point
+// validates its arguments on the host, returns a status code without
+// launching anything when they are rejected, and otherwise enqueues the
+// kernels on the caller's stream.  No exception crosses this boundary.
+#include "../../include/hsa_attn.h"
+#include "hsa_internal.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == HSA_F32 || dt == HSA_BF16; }
+int esize(int dt) { return dt == HSA_F32 ? 4 : 2; }
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int finish(hipError_t e) { return e == hipSuccess ? HSA_OK : HSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hsa_strerror(int status) {
+    switch (status) {
+        case HSA_OK: return "HSA_OK";
+        case HSA_ERR_INVALID_ARG: return "HSA_ERR_INVALID_ARG";
+        case HSA_ERR_UNSUPPORTED: return "HSA_ERR_UNSUPPORTED";
+        case HSA_ERR_WORKSPACE: return "HSA_ERR_WORKSPACE";
+        case HSA_ERR_HIP: return "HSA_ERR_HIP";
+        default: return "HSA_ERR_UNKNOWN";
+    }
+}
+
+int hsa_version(void) { return 100; }
+
+int hsa_compress(int dtype, const void* x, const void* gate, const void* bias, void* out,
+                 int32_t B, int32_t T, int32_t D, int32_t m, void* stream) {
+    try {
+        if (!dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!x || !gate || !bias || !out) return HSA_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(gate) || !aligned16(bias) || !aligned16(out))
+            return HSA_ERR_INVALID_ARG;
+        if (B < 1 || D < 1 || m < 1 || m > 1024 || T < m) return HSA_ERR_INVALID_ARG;
+        if ((D * esize(dtype)) % 16 != 0) return HSA_ERR_UNSUPPORTED;
+        return finish(hsa::launch_compress(dtype, x, gate, bias, out, B, T, D, m, as_stream(stream)));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+size_t hsa_index_topk_workspace_size(int32_t Nq, int32_t S_max, int32_t k) {
+    if (Nq < 1 || S_max < 1 || k < 1) return 0;
+    return hsa::topk_workspace_bytes(Nq, S_max, k);
+}
+
+int hsa_index_topk(int dtype, const void* q_idx, const void* k_idx, int32_t B,
+                   const int32_t* q_seq, const int32_t* n_cand, float* scores,
+                   int32_t* topk_idx, int32_t Nq, int32_t H_I, int32_t d_I, int32_t S_max,
+                   int32_t k, uint32_t flags, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    try {
+        if (flags != 0) return HSA_ERR_INVALID_ARG;
+        if (!n_cand || !scores || !topk_idx) return HSA_ERR_INVALID_ARG;
+        if (Nq < 1 || S_max < 1 || k < 1 || k > hsa::kTopkMaxK) return HSA_ERR_INVALID_ARG;
+        if (q_idx) {
+            if (!dtype_ok(dtype) || !k_idx || B < 1 || H_I < 1 || d_I < 1) return HSA_ERR_INVALID_ARG;
+            if (!aligned16(q_idx) || !aligned16(k_idx)) return HSA_ERR_INVALID_ARG;
+            if (!q_seq && Nq > B) return HSA_ERR_INVALID_ARG;
+            const int row_bytes = d_I * esize(dtype);
+            if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512) return HSA_ERR_UNSUPPORTED;
+        }
+        const size_t need = hsa::topk_workspace_bytes(Nq, S_max, k);
+        if (need > 0 && (!workspace || workspace_bytes < need)) return HSA_ERR_WORKSPACE;
+        return finish(hsa::launch_index_topk(dtype, q_idx, k_idx, B, q_seq, n_cand, scores,
+                                             topk_idx, Nq, H_I, d_I, S_max, k, workspace,
+                                             as_stream(stream)));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+size_t hsa_attn_decode_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t max_rows) {
+    if (B < 1 || H < 1 || d_v < 1 || max_rows < 1) return 0;
+    return hsa::decode_workspace_bytes(B, H, d_v, max_rows);
+}
+
+int hsa_attn_decode(int dtype, const void* q, const void* swa_kv, const int32_t* swa_len,
+                    const void* comp_kv, const int32_t* comp_idx, const int32_t* comp_len,
+                    void* out, float* lse, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                    int32_t W, int32_t S_max, int32_t k, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    try {
+        if (!dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!q || !swa_kv || !swa_len || !comp_len || !out) return HSA_ERR_INVALID_ARG;
+        if (S_max > 0 && !comp_kv) return HSA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(swa_kv) || !aligned16(out) || (comp_kv && !aligned16(comp_kv)))
+            return HSA_ERR_INVALID_ARG;
+        if (B < 1 || H < 1 || H > 1024 || d_qk < 1 || d_v < 1 || d_v > d_qk || W < 1 || S_max < 0)
+            return HSA_ERR_INVALID_ARG;
+        if (comp_idx && (k < 1 || k > (1 << 20))) return HSA_ERR_INVALID_ARG;
+        if (!(scale == scale)) return HSA_ERR_INVALID_ARG;
+        if (!hsa::attn_shape_supported(dtype, d_qk, d_v)) return HSA_ERR_UNSUPPORTED;
+        const int max_rows = W + (comp_idx ? k : S_max);
+        const size_t need = hsa::decode_workspace_bytes(B, H, d_v, max_rows);
+        if (need > 0 && (!workspace || workspace_bytes < need)) return HSA_ERR_WORKSPACE;
+        return finish(hsa::launch_attn_decode(dtype, q, swa_kv, swa_len, comp_kv, comp_idx,
+                                              comp_len, out, lse, B, H, d_qk, d_v, W, S_max,
+                                              comp_idx ? k : 0, scale, workspace,
+                                              as_stream(stream)));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+size_t hsa_attn_prefill_workspace_size(int32_t n_seq, int32_t n_q, int32_t H, int32_t d_v) {
+    (void)n_seq; (void)n_q; (void)H; (void)d_v;
+    return 0;
+}
+
+int hsa_attn_prefill(int dtype, const void* q, const void* kv, const void* comp_kv,
+                     const int32_t* comp_idx, void* out, float* lse, int32_t n_seq,
+                     int32_t n_q, int32_t q_start, int32_t T, int32_t H, int32_t d_qk,
+                     int32_t d_v, int32_t W, int32_t S_max, int32_t k, int32_t m, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace; (void)workspace_bytes;
+    try {
+        if (!dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!q || !kv || !out) return HSA_ERR_INVALID_ARG;
+        if (S_max > 0 && !comp_kv) return HSA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (comp_kv && !aligned16(comp_kv)))
+            return HSA_ERR_INVALID_ARG;
+        if (n_seq < 1 || n_q < 1 || q_start < 0 || T < 1 || (int64_t)q_start + n_q > T || H < 1 ||
+            H > 1024 || d_qk < 1 || d_v < 1 || d_v > d_qk || W < 1 || S_max < 0 || m < 1)
+            return HSA_ERR_INVALID_ARG;
+        if (comp_idx && (k < 1 || k > (1 << 20))) return HSA_ERR_INVALID_ARG;
+        if (!(scale == scale)) return HSA_ERR_INVALID_ARG;
+        if (!hsa::attn_shape_supported(dtype, d_qk, d_v)) return HSA_ERR_UNSUPPORTED;
+        if ((int64_t)n_q > 0x7fffffff || (int64_t)n_seq > 65535) return HSA_ERR_UNSUPPORTED;
+        return finish(hsa::launch_attn_prefill(dtype, q, kv, comp_kv, comp_idx, out, lse, n_seq,
+                                               n_q, q_start, T, H, d_qk, d_v, W, S_max,
+                                               comp_idx ? k : 0, m, scale, as_stream(stream)));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// hsa_common.hpp -- device helpers shared by the gfx950 kernels of
+// libhsa_attn.so: element widening/rounding, 16-byte vector loads, wave and
+// workgroup scans, and the order-preserving key used by the radix select.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hsa {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Storage tag for bf16 (raw 16-bit pattern); fp32 is stored as float.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kPer16B = 4;
+    // widen the 16 bytes at p into kPer16B floats
+    __device__ static __forceinline__ void load16(const void* p, float* v) {
+        f32x4 t = *reinterpret_cast<const f32x4*>(p);
+        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    }
+    __device__ static __forceinline__ void unpack(const u32x4& t, float* v) {
+        v[0] = __uint_as_float(t[0]); v[1] = __uint_as_float(t[1]);
+        v[2] = __uint_as_float(t[2]); v[3] = __uint_as_float(t[3]);
+    }
+    __device__ static __forceinline__ void store(void* base, size_t i, float f) {
+        reinterpret_cast<float*>(base)[i] = f;
+    }
+};
+template <> struct Elem<bf16_t> {
+    static constexpr int kPer16B = 8;
+    __device__ static __forceinline__ void unpack(const u32x4& t, float* v) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = __uint_as_float(t[w] << 16);
+            v[2 * w + 1] = __uint_as_float(t[w] & 0xffff0000u);
+        }
+    }
+    __device__ static __forceinline__ void load16(const void* p, float* v) {
+        unpack(*reinterpret_cast<const u32x4*>(p), v);
+    }
+    __device__ static __forceinline__ void store(void* base, size_t i, float f) {
+        reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16(f);
+    }
+};
+
+// ---- wave / workgroup primitives ------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t o = __shfl_up(v, d, kWave);
+        if (l >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a workgroup of NT threads (NT multiple of 64).
+// `tmp` must hold NT/64 + 1 words of LDS; the total is returned in *total.
+// Every thread of the workgroup must call it (it contains barriers).
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+    constexpr int NW = NT / kWave;
+    const int w = (int)threadIdx.x / kWave;
+    uint32_t inc = wave_incl_scan(v);
+    if (lane_id() == kWave - 1) tmp[w] = inc;
+    __syncthreads();
+    uint32_t base = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        uint32_t t = tmp[i];
+        base += (i < w) ? t : 0u;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return base + inc - v;
+}
+
+// ---- radix-select key -------------------------------------------------------
+// Order-preserving map fp32 -> u32: a > b (IEEE) iff key(a) > key(b); -0 and
+// +0 share one key; every NaN maps to 0, below -inf (0x007fffff).
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN
+    if (u == 0x80000000u) u = 0u;                      // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace hsa

@@ -1,0 +1,69 @@
+// hsa_internal.hpp -- launchers shared between the kernel translation units
+// and the C-ABI layer (api.hip).  Arguments are already validated by the
+// caller; every launcher enqueues on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hsa {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// ---- optional kernel timing (profile.hip) ----
+// Kernel families, same values as HSA_PROF_* in hsa_attn.h.
+constexpr unsigned kProfCompress = 1u, kProfScore = 2u, kProfSelect = 4u, kProfAttn = 8u,
+                   kProfMerge = 16u;
+// Records a HIP event on `st` when constructed and another when destroyed, if
+// the family is armed; wrap exactly one kernel launch in its scope.
+class ProfScope {
+  public:
+    ProfScope(unsigned family, hipStream_t st);
+    ~ProfScope();
+    ProfScope(const ProfScope&) = delete;
+    ProfScope& operator=(const ProfScope&) = delete;
+
+  private:
+    unsigned family_;
+    hipStream_t st_;
+    int slot_;
+};
+
+// ---- compressor ----
+hipError_t launch_compress(int dtype, const void* x, const void* g, const void* bias, void* out,
+                           int B, int T_len, int D, int m, hipStream_t st);
+
+// ---- indexer + top-k ----
+// Candidate lists up to this length are selected by one workgroup per query
+// with every key resident in LDS; longer ones use the multi-workgroup path
+// (histogram pass fused into scoring, then a filter + final select).
+constexpr int kRowSelectCap = 12288;
+constexpr int kTopkMaxK = 2048;
+size_t topk_workspace_bytes(int Nq, int S_max, int k);
+hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, int B,
+                             const int32_t* q_seq, const int32_t* n_cand, float* scores,
+                             int32_t* topk_idx, int Nq, int H_I, int d_I, int S_max, int k,
+                             void* ws, hipStream_t st);
+
+// ---- attention ----
+struct DecodePlan {
+    int max_rows;  // W + (sparse ? k : S_max)
+    int rows_per_split;
+    int n_split;
+};
+DecodePlan plan_decode(int B, int H, int max_rows);
+size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows);
+bool attn_shape_supported(int dtype, int d_qk, int d_v);
+hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
+                              const int32_t* swa_len, const void* comp_kv,
+                              const int32_t* comp_idx, const int32_t* comp_len, void* out,
+                              float* lse, int B, int H, int d_qk, int d_v, int W, int S_max,
+                              int k, float scale, void* ws, hipStream_t st);
+hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const void* comp_kv,
+                               const int32_t* comp_idx, void* out, float* lse, int n_seq,
+                               int n_q, int q_start, int T_len, int H, int d_qk, int d_v, int W,
+                               int S_max, int k, int m, float scale, hipStream_t st);
+
+}  // namespace hsa

@@ -1,0 +1,222 @@
+/*
+ * hsa_attn.h -- C ABI of the MI355X (gfx950) hybrid sparse-attention library
+ * (libhsa_attn.so): block KV compressor, indexer scores + top-k select, and the
+ * fused attention over the sliding window plus selected (C4) or all (C128)
+ * compressed rows.
+ *
+ * Pages cited (titles as published; sections named as on the page):
+ *   [KD] "DeepSeek-V4: optimizacion de inferencia y RL para modelos con
+ *        atencion hibrida y FP4" (kerneldigest.dev)
+ *   [LH] "DeepSeek-V4: SGLang va Miles mang den ho tro Day-0 cho suy luan
+ *        nhanh va Hoc tang cuong" (lehuy.net)
+ *   [NK] "与 SGLang 团队聊 DeepSeek V4:混合注意力的推理与 RL 训练适配"
+ *        (nolimitkun.github.io AI-KOL wiki)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *    tensors), row-major and contiguous, 16-byte aligned.  Index, length and
+ *    count arrays are int32 in device memory.
+ *  - dtype (HSA_F32 or HSA_BF16) is the storage type of every floating-point
+ *    tensor argument except `scores` and `lse`, which are always fp32.  All
+ *    arithmetic is fp32 (bf16 inputs are widened exactly; bf16 outputs are
+ *    rounded to nearest even).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call checks
+ *    its arguments on the host, enqueues its kernels on `stream` and returns
+ *    without synchronising.  Faults inside a kernel surface at the caller's
+ *    next synchronisation.
+ *  - Ownership: the caller owns every buffer, including the workspace.  The
+ *    library allocates no device memory and keeps no pointer after returning.
+ *  - Errors: a rejected call returns a nonzero hsa_status_code and launches
+ *    nothing.  HSA_ERR_HIP means a launch failed (hipGetLastError).  No C++
+ *    exception crosses this boundary.
+ *  - Outputs must not alias inputs, except `scores` in select-only mode.
+ *  - Identical inputs give bitwise-identical outputs (no floating-point
+ *    atomics; every reduction has a fixed order).
+ *  - Re-entrant; calls that share one workspace must not overlap in time.
+ */
+#ifndef HSA_ATTN_H
+#define HSA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HSA_OK = 0,
+    HSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad flag   */
+    HSA_ERR_UNSUPPORTED = 2, /* valid but not built (shape/dtype combination) */
+    HSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+    HSA_ERR_HIP = 4          /* a HIP launch reported an error                */
+} hsa_status_code;
+
+typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *hsa_strerror(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int hsa_version(void);
+
+/*
+ * hsa_compress -- block KV compressor.
+ *
+ * [NK "推理侧优化", Kernel fusion bullet]: the compression chain is
+ * read -> add -> softmax -> multiply -> write back, fused into one on-chip
+ * pass ([KD "Arquitectura del Sistema"], Flash Compressor).
+ * [NK "DeepSeek V4 的新架构"]: an entry is produced once every m = 4 (C4) or
+ * m = 128 (C128) tokens.
+ *
+ *   out[b, i, d] = sum_{j<m} softmax_j(gate[b, m*i+j, d] + bias[j, d]) * x[b, m*i+j, d]
+ *
+ * for every complete block i < T/m (a trailing partial block is ignored),
+ * softmax taken over j separately for each channel d.
+ *
+ *   x, gate : [B, T, D]   dtype     (x: token latents, gate: per-token gate logits)
+ *   bias    : [m, D]      dtype     (per-position-in-block bias, shared by all blocks)
+ *   out     : [B, T/m, D] dtype
+ *   Sizes   : B >= 1, T >= m, D >= 1 with D*sizeof(dtype) a multiple of 16, 1 <= m <= 1024.
+ */
+int hsa_compress(int dtype, const void *x, const void *gate, const void *bias, void *out,
+                 int32_t B, int32_t T, int32_t D, int32_t m, void *stream);
+
+/*
+ * hsa_index_topk -- indexer scores and exact top-k select.
+ *
+ * [KD "Flujo de Inferencia", step "Indexer (TopK)"]: top-k over the
+ * compressed-attention candidates; [KD "Arquitectura del Sistema"]: a
+ * radix-select reduction replaces a global sort; [LH "Toi uu hoa suy luan
+ * voi ShadowRadix va HiSparse"]: C4 keeps the top 512.
+ *
+ * Scores (score mode, q_idx != NULL):
+ *   scores[q, s] = sum_{h<H_I} sum_{e<d_I} q_idx[q, h, e] * k_idx[q_seq[q], s, e]
+ * for s < n_cand[q]; entries s >= n_cand[q] are left unspecified.  The sum
+ * over heads is formed first (it is linear), so each score is one fp32 dot
+ * product of length d_I; identical key rows give bitwise-identical scores.
+ *
+ * Select (always): candidates s < n_cand[q]; order = score descending, equal
+ * scores (IEEE, -0 == +0) by lower index first; NaN ranks below every
+ * number.  The first min(k, n_cand[q]) candidates are written to
+ * topk_idx[q, :] in ascending index order, followed by -1 padding up to k.
+ *
+ *   q_idx    : [Nq, H_I, d_I] dtype, or NULL for select-only mode (then
+ *              `scores` is an INPUT holding fp32 scores)
+ *   k_idx    : [B, S_max, d_I] dtype (ignored in select-only mode, may be NULL)
+ *   q_seq    : [Nq] int32 sequence of each query in [0, B), or NULL (query q
+ *              reads sequence q; then Nq <= B)
+ *   n_cand   : [Nq] int32 candidate count per query, clamped to [0, S_max]
+ *   scores   : [Nq, S_max] fp32, output (score mode) or input (select-only)
+ *   topk_idx : [Nq, k] int32 output
+ *   Sizes    : Nq >= 1, B >= 1, H_I >= 1, d_I*sizeof(dtype) in {128, 256, 512},
+ *              S_max >= 1, 1 <= k <= 2048.  flags must be 0 (reserved for a
+ *              weighted/activated head combination).
+ *   workspace: device memory of hsa_index_topk_workspace_size(Nq, S_max, k)
+ *              bytes.  It must be zero-filled before its first use; every
+ *              call that completes leaves it zero-filled again.
+ */
+size_t hsa_index_topk_workspace_size(int32_t Nq, int32_t S_max, int32_t k);
+int hsa_index_topk(int dtype, const void *q_idx, const void *k_idx, int32_t B,
+                   const int32_t *q_seq, const int32_t *n_cand, float *scores,
+                   int32_t *topk_idx, int32_t Nq, int32_t H_I, int32_t d_I, int32_t S_max,
+                   int32_t k, uint32_t flags, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/*
+ * hsa_attn_decode -- one query token per sequence, one joint softmax over the
+ * SWA ring plus the selected (sparse) or all (dense) compressed rows.
+ *
+ * [LH "Tich hop Kernel va Giai ma suy doan"]: SWA and the extra C4/C128
+ * attention in one unified kernel call; [LH "Toi uu hoa suy luan..."]: each
+ * layer pairs SWA with C4 (sparse top-512) or C128 (dense).
+ *
+ * Row set of sequence b:
+ *   SWA    : ring slots 0 .. swa_len[b]-1 of swa_kv[b] (swa_len clamped to [0, W])
+ *   sparse : comp_idx != NULL: rows comp_kv[b, i] for each listed i with
+ *            0 <= i < comp_len[b]; other entries (e.g. -1) are skipped
+ *   dense  : comp_idx == NULL: rows comp_kv[b, 0 .. comp_len[b]-1]
+ *   (comp_len clamped to [0, S_max])
+ * For head h:  l_r = scale * <q[b,h,:], row_r[0:d_qk]>;  lse = log sum_r exp(l_r);
+ *              out[b,h,:] = sum_r exp(l_r - lse) * row_r[0:d_v]
+ * (the value of a latent row is its first d_v channels).  An empty row set
+ * gives out = 0 and lse = -inf.
+ *
+ *   q        : [B, H, d_qk] dtype
+ *   swa_kv   : [B, W, d_qk] dtype ring (token t in slot t mod W)
+ *   swa_len  : [B] int32
+ *   comp_kv  : [B, S_max, d_qk] dtype (may be NULL when S_max == 0)
+ *   comp_idx : [B, k] int32 or NULL
+ *   comp_len : [B] int32
+ *   out      : [B, H, d_v] dtype;  lse: [B, H] fp32 natural log, or NULL
+ *   Sizes    : supported (d_qk, d_v): (128, 128) in fp32 and bf16, (576, 512) in
+ *              bf16 (other pairs: HSA_ERR_UNSUPPORTED); 1 <= H <= 1024;
+ *              1 <= W; 0 <= S_max; k >= 1 in sparse mode.
+ *   workspace: hsa_attn_decode_workspace_size(B, H, d_v, max_rows) bytes with
+ *              max_rows = W + (sparse ? k : S_max); contents need no init.
+ */
+size_t hsa_attn_decode_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t max_rows);
+int hsa_attn_decode(int dtype, const void *q, const void *swa_kv, const int32_t *swa_len,
+                    const void *comp_kv, const int32_t *comp_idx, const int32_t *comp_len,
+                    void *out, float *lse, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                    int32_t W, int32_t S_max, int32_t k, float scale, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * hsa_attn_prefill -- a chunk of n_q consecutive query positions per
+ * sequence, each with its own causal SWA window and its own compressed rows.
+ *
+ * [KD "Arquitectura del Sistema"]: long prefill; [NK "DeepSeek V4 的新架构"]:
+ * a compressed entry exists only once its whole block has arrived.
+ *
+ * Query i of sequence b sits at position p = q_start + i.  Its row set:
+ *   SWA     : tokens max(0, p-W+1) .. p of kv[b]
+ *   visible : compressed rows c < min((p+1)/m, S_max)
+ *   sparse  : comp_idx != NULL: the listed visible rows of query (b, i)
+ *             (row b*n_q + i of comp_idx; other entries skipped)
+ *   dense   : comp_idx == NULL: every visible row
+ * with the same joint softmax as hsa_attn_decode.
+ *
+ *   q        : [n_seq, n_q, H, d_qk] dtype
+ *   kv       : [n_seq, T, d_qk] dtype (token latents; q_start + n_q <= T)
+ *   comp_kv  : [n_seq, S_max, d_qk] dtype
+ *   comp_idx : [n_seq*n_q, k] int32 or NULL
+ *   out      : [n_seq, n_q, H, d_v] dtype;  lse: [n_seq*n_q, H] fp32 or NULL
+ *   Sizes    : as hsa_attn_decode, plus m >= 1 (4 for C4, 128 for C128).
+ *   workspace: hsa_attn_prefill_workspace_size(...) bytes (currently 0).
+ */
+size_t hsa_attn_prefill_workspace_size(int32_t n_seq, int32_t n_q, int32_t H, int32_t d_v);
+int hsa_attn_prefill(int dtype, const void *q, const void *kv, const void *comp_kv,
+                     const int32_t *comp_idx, void *out, float *lse, int32_t n_seq,
+                     int32_t n_q, int32_t q_start, int32_t T, int32_t H, int32_t d_qk,
+                     int32_t d_v, int32_t W, int32_t S_max, int32_t k, int32_t m, float scale,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Kernel timing (diagnostics, not on the hot path).
+ *
+ * hsa_profile_enable arms the kernel families in family_mask (OR of the
+ * HSA_PROF_* values; 0 disarms all).  While a family is armed, each launch of
+ * it is bracketed by two hipEventRecord calls on the launch stream (up to
+ * 8192 launches between reads; later ones go untimed).  hsa_profile_read
+ * waits for every recorded launch, adds their durations to per-family totals
+ * and returns the total milliseconds and launch count of `family` (a single
+ * HSA_PROF_* value); reset != 0 then clears all totals.  Not meant to be
+ * called while kernels are being captured into a graph.
+ */
+enum {
+    HSA_PROF_COMPRESS = 1, /* hsa_compress kernel                           */
+    HSA_PROF_SCORE = 2,    /* indexer scoring (+ first-digit histogram)     */
+    HSA_PROF_SELECT = 4,   /* top-k select kernels                          */
+    HSA_PROF_ATTN = 8,     /* attention kernels (decode split / prefill)    */
+    HSA_PROF_MERGE = 16    /* decode split merge                            */
+};
+int hsa_profile_enable(unsigned family_mask);
+int hsa_profile_read(unsigned family, double *total_ms, long long *launches, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_ATTN_H */

@@ -1,0 +1,119 @@
+"""GPU parity: indexer scores and the selection they lead to.
+
+Scores: each GPU score must lie within the fp32 error bound of the oracle's
+fp64 score, |err_s| <= (H_I + d_I) * 2^-24 * A_s with
+A_s = sum_e (sum_h |q_idx[h,e]|) * |k_idx[s,e]| (the heads are summed first,
+then one dot product of length d_I, both in fp32).  Equal key rows must give
+bitwise-equal scores.  Selection: the GPU set must overlap the oracle's set
+(oracle scores rounded to fp32, oracle select) by >= 99.9 %."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import note, to_np
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def _check_scores(got, ref, q_idx, k_idx, q_seq, n_cand):
+    g = got.detach().cpu().numpy().astype(np.float64)
+    qa = np.abs(to_np(q_idx)).sum(axis=1)  # [Nq, d_I]
+    ka = np.abs(to_np(k_idx))              # [B, S, d_I]
+    H_I, d_I = q_idx.shape[1], q_idx.shape[2]
+    worst = 0.0
+    for i in range(g.shape[0]):
+        n = int(n_cand[i])
+        b = int(q_seq[i]) if q_seq is not None else i
+        bound = (H_I + d_I) * U * (ka[b, :n] @ qa[i]) * 1.01 + 1e-30
+        err = np.abs(g[i, :n] - ref[i, :n])
+        assert np.all(err <= bound), "score %d: worst ratio %.3g" % (i, (err / bound).max())
+        worst = max(worst, float((err / bound).max()) if n else 0.0)
+    return worst
+
+
+def _overlap(got_idx, want_idx):
+    inter = tot = 0
+    for g, w in zip(got_idx, want_idx):
+        ws = set(int(v) for v in w if v >= 0)
+        gs = set(int(v) for v in g if v >= 0)
+        inter += len(ws & gs)
+        tot += len(ws)
+        assert len(gs) == len(ws)
+    return inter / max(tot, 1)
+
+
+def test_tiny_fp32_scores_and_selection(oracle):
+    import hybrid_sparse_compressed_amd as hsa
+    from hybrid_sparse_compressed_amd import workloads
+
+    w = workloads.tiny_fp32_decode("cpu")
+    note("index tiny_fp32_decode")
+    s, idx = hsa.hsa_index_topk(w["q_idx"].cuda(), w["k_idx"].cuda(), w["n_cand"], 64)
+    torch.cuda.synchronize()
+    ref = oracle.index_scores(w["q_idx"], w["k_idx"], w["n_cand"].numpy())
+    _check_scores(s, ref, w["q_idx"], w["k_idx"], None, w["n_cand"].numpy())
+    want = oracle.topk(ref.astype(np.float32), w["n_cand"].numpy(), 64)
+    assert _overlap(idx.cpu().numpy(), want) == 1.0
+
+
+@pytest.mark.parametrize("S_max,k", [(3000, 64), (20000, 100)])
+def test_ragged_queries_and_sequence_routing(oracle, S_max, k):
+    import hybrid_sparse_compressed_amd as hsa
+
+    g = torch.Generator().manual_seed(S_max)
+    B, Nq, H_I, d_I = 3, 12, 64, 128
+    q_idx = torch.randn(Nq, H_I, d_I, generator=g).to(torch.bfloat16)
+    k_idx = torch.randn(B, S_max, d_I, generator=g).to(torch.bfloat16)
+    q_seq = torch.randint(0, B, (Nq,), generator=g, dtype=torch.int32)
+    n_cand = torch.randint(0, S_max + 1, (Nq,), generator=g, dtype=torch.int32)
+    n_cand[0], n_cand[1], n_cand[2] = 0, k, S_max
+    note("index ragged S_max=%d k=%d" % (S_max, k))
+    s, idx = hsa.hsa_index_topk(q_idx.cuda(), k_idx.cuda(), n_cand, k, q_seq=q_seq)
+    torch.cuda.synchronize()
+    ref = oracle.index_scores(q_idx, k_idx, n_cand.numpy(), q_seq=q_seq.numpy())
+    _check_scores(s, ref, q_idx, k_idx, q_seq.numpy(), n_cand.numpy())
+    want = oracle.topk(ref.astype(np.float32), n_cand.numpy(), k)
+    assert _overlap(idx.cpu().numpy(), want) >= 0.999
+
+
+@pytest.mark.parametrize("name", ["c4_decode_64k", "c4_decode_1m"])
+def test_full_size_decode_selection(oracle, name):
+    """Full-size indexer + select; the oracle's rank-512 row is copied to three more
+    positions (one lower, two higher index) so a tie straddles the boundary."""
+    import hybrid_sparse_compressed_amd as hsa
+    from hybrid_sparse_compressed_amd import workloads
+
+    w = workloads.c4_decode(name, "cuda")
+    k, S = w["cfg"]["k"], w["S"]
+    q_idx_c, n_cand = w["q_idx"].cpu(), w["n_cand"].cpu().numpy()
+    k_c = w["k_idx"].cpu()
+    ref = oracle.index_scores(q_idx_c, k_c, n_cand)
+    sel = oracle.topk(ref.astype(np.float32), n_cand, k)
+    rng = np.random.default_rng(3)
+    for b in range(w["cfg"]["B"]):
+        chosen = sel[b]
+        kth = chosen[np.argmin(ref[b, chosen])]
+        lower = rng.integers(0, kth) if kth > 0 else kth
+        higher = rng.integers(kth + 1, S, size=2)
+        for p in [lower, *higher]:
+            k_c[b, p] = k_c[b, kth]
+    w["k_idx"].copy_(k_c)
+    ref = oracle.index_scores(q_idx_c, k_c, n_cand)
+    want = oracle.topk(ref.astype(np.float32), n_cand, k)
+    note("index full size %s" % name)
+    s, idx = hsa.hsa_index_topk(w["q_idx"], w["k_idx"], w["n_cand"], k)
+    torch.cuda.synchronize()
+    worst = _check_scores(s, ref, q_idx_c, k_c, None, n_cand)
+    ov = _overlap(idx.cpu().numpy(), want)
+    print("score error / bound (worst) = %.3g, selected-set overlap = %.6f" % (worst, ov))
+    assert ov >= 0.999
+    # planted duplicate rows score bitwise-equal on the GPU
+    sg = s.cpu().numpy()
+    for b in range(w["cfg"]["B"]):
+        rows = k_c[b].view(torch.int16).numpy()
+        _, first, inv = np.unique(rows, axis=0, return_index=True, return_inverse=True)
+        dup = np.nonzero(first[inv.ravel()] != np.arange(S))[0]
+        assert len(dup) > 0
+        np.testing.assert_array_equal(sg[b, dup], sg[b, first[inv.ravel()][dup]])

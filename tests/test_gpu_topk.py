@@ -1,0 +1,111 @@
+"""GPU parity: the radix-select top-k (select-only mode of hsa_index_topk) must
+be bit-exact against the oracle on identical fp32 scores, on both the
+LDS-resident path (n <= 12288) and the multi-workgroup path."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import note
+
+pytestmark = pytest.mark.gpu
+
+
+def _select(scores, n_cand, k):
+    import hybrid_sparse_compressed_amd as hsa
+
+    _, idx = hsa.hsa_index_topk(None, None, n_cand, k, scores=scores.cuda())
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def _plant_boundary_ties(oracle, s, n_cand, k, rng):
+    """Copy each row's rank-k value to positions on both sides of it, and place
+    the float neighbours (+-1 ulp) of that value nearby."""
+    s = s.copy()
+    sel = oracle.topk(s, n_cand, k)
+    for i in range(s.shape[0]):
+        n = int(n_cand[i])
+        if n <= k or n < 8:
+            continue
+        chosen = sel[i][sel[i] >= 0]
+        vals = s[i, chosen]
+        kth = chosen[np.argmin(vals)]
+        v = s[i, kth]
+        pos = rng.choice(n, size=min(6, n), replace=False)
+        s[i, pos[:3]] = v
+        s[i, pos[3:4]] = np.nextafter(v, np.float32(np.inf))
+        s[i, pos[4:5]] = np.nextafter(v, np.float32(-np.inf))
+        if len(pos) > 5:
+            s[i, pos[5]] = -0.0 if v == 0 else v
+    return s
+
+
+@pytest.mark.parametrize(
+    "Nq,S,k",
+    [(3, 1, 1), (4, 7, 3), (5, 64, 64), (6, 1000, 64), (4, 5000, 2048), (3, 12288, 512),
+     (3, 12289, 512), (4, 50000, 512), (2, 70000, 2048), (4, 262144, 512)],
+)
+def test_select_bit_exact(oracle, Nq, S, k):
+    from hybrid_sparse_compressed_amd import workloads
+
+    rng = np.random.default_rng(S + k)
+    scores = workloads.topk_scores(Nq, S, "cpu", seed=7 + S).numpy()
+    n_cand = np.full(Nq, S, dtype=np.int32)
+    if Nq >= 3:  # ragged candidate counts: fewer than k, exactly k, all
+        n_cand[0] = max(0, min(S, k // 2))
+        n_cand[1] = min(S, k)
+        n_cand[2] = max(0, S - 3)
+    scores = _plant_boundary_ties(oracle, scores, n_cand, k, rng)
+    note("topk select Nq=%d S=%d k=%d" % (Nq, S, k))
+    got = _select(torch.from_numpy(scores), torch.from_numpy(n_cand), k)
+    want = oracle.topk(scores, n_cand, k)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("S", [3000, 20000])
+def test_select_special_patterns(oracle, S):
+    k = 256
+    inc = np.arange(S, dtype=np.float32)
+    pats = [
+        np.full(S, 0.25, np.float32),                       # all equal
+        inc,                                                 # ascending
+        -inc,                                                # descending
+        np.where(np.arange(S) % 2 == 0, -0.0, 0.0).astype(np.float32),  # signed zeros
+        np.where(np.arange(S) % 97 == 0, np.inf, -np.inf).astype(np.float32),
+        np.round(np.random.default_rng(1).standard_normal(S)).astype(np.float32),  # few levels
+    ]
+    scores = np.stack(pats)
+    n_cand = np.full(len(pats), S, np.int32)
+    note("topk special patterns S=%d" % S)
+    got = _select(torch.from_numpy(scores), torch.from_numpy(n_cand), k)
+    np.testing.assert_array_equal(got, oracle.topk(scores, n_cand, k))
+    assert got[0].tolist() == list(range(k))
+    assert got[1].tolist() == list(range(S - k, S))
+
+
+def test_nan_ranks_below_numbers(oracle):
+    S, k = 20000, 128
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((2, S)).astype(np.float32)
+    s[:, rng.choice(S, 500, replace=False)] = np.nan
+    n_cand = np.full(2, S, np.int32)
+    note("topk NaN smoke")
+    got = _select(torch.from_numpy(s), torch.from_numpy(n_cand), k)
+    want = oracle.topk(np.nan_to_num(s, nan=-np.inf), n_cand, k)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_workspace_is_reusable_and_results_deterministic(oracle):
+    from hybrid_sparse_compressed_amd import workloads
+
+    k, S = 512, 100000
+    a = workloads.topk_scores(4, S, "cpu", seed=11).numpy()
+    b = workloads.topk_scores(4, S, "cpu", seed=12).numpy()
+    n_cand = np.full(4, S, np.int32)
+    note("topk workspace reuse")
+    r1 = _select(torch.from_numpy(a), torch.from_numpy(n_cand), k)
+    r2 = _select(torch.from_numpy(b), torch.from_numpy(n_cand), k)
+    r3 = _select(torch.from_numpy(a), torch.from_numpy(n_cand), k)
+    np.testing.assert_array_equal(r1, oracle.topk(a, n_cand, k))
+    np.testing.assert_array_equal(r2, oracle.topk(b, n_cand, k))
+    np.testing.assert_array_equal(r1, r3)
