@@ -118,19 +118,19 @@ def _stream(stream):
 
 
 class Workspace:
-    """A zero-filled device buffer reused across calls (per device and stream).
+    """Device buffers reused across calls, one per (purpose, device, stream).
 
-    The top-k path needs its histogram and counters zeroed before the first
-    call; every call that completes leaves them zeroed again, so one
-    allocation serves all later calls made in stream order."""
+    The top-k workspace must be zero-filled before its first use and every
+    completed call leaves it zero-filled again, so it is never shared with a
+    purpose that leaves data behind (the decode split partials)."""
 
     _cache: dict = {}
 
     @classmethod
-    def get(cls, nbytes: int, device, stream) -> torch.Tensor | None:
+    def get(cls, purpose: str, nbytes: int, device, stream) -> torch.Tensor | None:
         if nbytes == 0:
             return None
-        key = (str(device), stream.cuda_stream if stream is not None else 0)
+        key = (purpose, str(device), stream.cuda_stream if stream is not None else 0)
         buf = cls._cache.get(key)
         if buf is None or buf.numel() < nbytes:
             buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -182,7 +182,7 @@ def hsa_index_topk(q_idx, k_idx, n_cand, k, q_seq=None, scores=None, topk_idx=No
     st = torch.cuda.current_stream() if stream is None else stream
     need = lib.hsa_index_topk_workspace_size(Nq, S_max, k)
     if workspace is None:
-        workspace = Workspace.get(need, dev, st)
+        workspace = Workspace.get("topk", need, dev, st)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("hsa_index_topk", lib.hsa_index_topk(
         dt, _ptr(q_idx), _ptr(k_idx), B, _ptr(q_seq), _ptr(n_cand), _ptr(scores),
@@ -209,7 +209,7 @@ def hsa_attn_decode(q, swa_kv, swa_len, comp_kv, comp_len, scale, d_v, comp_idx=
     st = torch.cuda.current_stream() if stream is None else stream
     need = lib.hsa_attn_decode_workspace_size(B, H, d_v, W + (k if comp_idx is not None else S_max))
     if workspace is None:
-        workspace = Workspace.get(need, dev, st)
+        workspace = Workspace.get("attn_decode", need, dev, st)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("hsa_attn_decode", lib.hsa_attn_decode(
         _dt(q), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_idx),

@@ -70,6 +70,11 @@ __device__ inline QWs ws_of(uint8_t* ws, int q, int S_max, int k) {
     return w;
 }
 
+// Counters that other workgroups of the same launch update with atomics.
+__device__ inline uint32_t counter_load(const uint32_t* p) {
+    return __atomic_load_n(p, __ATOMIC_RELAXED);
+}
+
 __device__ inline int clamp_n(const int32_t* n_cand, int q, int S_max) {
     int n = n_cand[q];
     return n < 0 ? 0 : (n > S_max ? S_max : n);
@@ -354,10 +359,13 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     __threadfence();
 
     // counters read once and broadcast, so every branch below is uniform
-    __shared__ int cnt[2];
+    __shared__ int cnt[2], cnt_raw[2];
     if (tid == 0) {
-        cnt[0] = min((int)__atomic_load_n(&W.ctr[1], __ATOMIC_RELAXED), take);
-        cnt[1] = min((int)__atomic_load_n(&W.ctr[0], __ATOMIC_RELAXED), S_max);
+        const uint32_t a = counter_load(&W.ctr[1]), b = counter_load(&W.ctr[0]);
+        cnt[0] = min((int)min(a, (uint32_t)take), take);
+        cnt[1] = (int)min(b, (uint32_t)S_max);
+        cnt_raw[0] = (int)min(a, (uint32_t)k);      // entries written to sel (capacity k)
+        cnt_raw[1] = (int)min(b, (uint32_t)S_max);  // entries written to the short list
     }
     __syncthreads();
     const int nsel0 = cnt[0];
@@ -370,7 +378,10 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         const uint32_t* key = W.cand_key;
         const uint32_t* idx = W.cand_idx;
         if (nc <= kCandCap) {
-            for (int i = tid; i < nc; i += kThreads) { ck[i] = W.cand_key[i]; ci[i] = W.cand_idx[i]; }
+            for (int i = tid; i < nc; i += kThreads) {
+                ck[i] = W.cand_key[i];
+                ci[i] = W.cand_idx[i];
+            }
             __syncthreads();
             key = ck;
             idx = ci;
@@ -444,8 +455,13 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     }
     int32_t* o = out + (size_t)q * k;
     for (int i = tid; i < k; i += kThreads) o[i] = (i < filled) ? sel[i] : -1;
-    // leave this query's histogram and counters zeroed for the next call
+    // Leave every word this call wrote for this query zeroed again (histogram,
+    // counters, short list, selected list), so the whole workspace is zero
+    // whatever layout the next call uses.
+    __syncthreads();
     for (int i = tid; i < kBins; i += kThreads) W.hist[i] = 0;
+    for (int i = tid; i < cnt_raw[1]; i += kThreads) { W.cand_key[i] = 0; W.cand_idx[i] = 0; }
+    for (int i = tid; i < cnt_raw[0]; i += kThreads) W.sel[i] = 0;
     if (tid < 16) W.ctr[tid] = 0;
 }
 

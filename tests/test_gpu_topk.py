@@ -109,3 +109,41 @@ def test_workspace_is_reusable_and_results_deterministic(oracle):
     np.testing.assert_array_equal(r1, oracle.topk(a, n_cand, k))
     np.testing.assert_array_equal(r2, oracle.topk(b, n_cand, k))
     np.testing.assert_array_equal(r1, r3)
+
+
+def test_workspace_left_zero_across_layouts(oracle):
+    """Calls with different (Nq, S, k) share one workspace; each is exact and the
+    workspace is all-zero after every call."""
+    import hybrid_sparse_compressed_amd as hsa
+    from hybrid_sparse_compressed_amd import workloads
+
+    layouts = [(4, 100000, 512), (2, 30000, 64), (3, 13000, 2048), (4, 100000, 512)]
+    need = max(hsa.lib.hsa_index_topk_workspace_size(n, s, k) for n, s, k in layouts)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for j, (Nq, S, k) in enumerate(layouts):
+        s = workloads.topk_scores(Nq, S, "cpu", seed=40 + j).numpy()
+        n_cand = np.full(Nq, S, np.int32)
+        n_cand[0] = S - 17
+        note("topk layout %d: Nq=%d S=%d k=%d" % (j, Nq, S, k))
+        _, idx = hsa.hsa_index_topk(None, None, torch.from_numpy(n_cand), k,
+                                    scores=torch.from_numpy(s).cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(s, n_cand, k))
+        assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_default_workspace_not_shared_with_attention(oracle):
+    """The binding's cached top-k workspace must stay zero-filled even after an
+    attention call (whose split partials leave data in its own workspace)."""
+    import hybrid_sparse_compressed_amd as hsa
+    from hybrid_sparse_compressed_amd import workloads
+
+    w = workloads.c128_dense_decode("cuda", B=4)
+    note("attention call before top-k")
+    hsa.hsa_attn_decode(w["q"], w["swa_kv"], w["swa_len"], w["comp_kv"], w["comp_len"],
+                        w["scale"], 512)
+    S, k = 60000, 512
+    s = workloads.topk_scores(4, S, "cpu", seed=77).numpy()
+    n_cand = np.full(4, S, np.int32)
+    got = _select(torch.from_numpy(s), torch.from_numpy(n_cand), k)
+    np.testing.assert_array_equal(got, oracle.topk(s, n_cand, k))
