@@ -34,6 +34,7 @@ constexpr int kAttnThreads = 256;
 constexpr int kHeadsPerWave = 16;
 constexpr int kHeadsPerWG = 64;
 constexpr int kTile = 32;
+constexpr int kChunkRows = 256;  // rows whose list is built at once (one per thread)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -53,6 +54,22 @@ template <> struct Mma<float> {
     typedef float frag;
     __device__ static __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Element x of a 16-byte chunk, and a store of the x-th elements of two rows
+// (consecutive in the transposed tile) as one 2-element write.
+template <typename T> struct Pair;
+template <> struct Pair<bf16_t> {
+    __device__ static __forceinline__ void put(bf16_t* dst, const u32x4& a, const u32x4& b, int x) {
+        const uint32_t lo = (a[x >> 1] >> (16 * (x & 1))) & 0xffffu;
+        const uint32_t hi = (b[x >> 1] >> (16 * (x & 1))) & 0xffffu;
+        *reinterpret_cast<uint32_t*>(dst) = lo | (hi << 16);
+    }
+};
+template <> struct Pair<float> {
+    __device__ static __forceinline__ void put(float* dst, const u32x4& a, const u32x4& b, int x) {
+        *reinterpret_cast<uint2*>(dst) = uint2{a[x], b[x]};
     }
 };
 
@@ -94,9 +111,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     extern __shared__ __align__(16) unsigned char lds_raw[];
     T* Ks = reinterpret_cast<T*>(lds_raw);
     T* Vt = Ks + (size_t)kTile * L::kStrideK;
-    __shared__ long long row_off[kTile];  // element offset of the row in its source, -1 invalid
-    __shared__ int row_src[kTile];        // 0: window source, 1: compressed pool
-    __shared__ int tile_any;
+    __shared__ long long row_off[kChunkRows];  // element offset of the row in its source, -1 invalid
+    __shared__ int row_src[kChunkRows];        // 0: window source, 1: compressed pool
+    __shared__ int tile_any[kChunkRows / kTile];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int hl = lane & 15, quad = lane >> 4;
@@ -158,13 +175,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     const T* win = reinterpret_cast<const T*>(a.win);
     const T* comp = reinterpret_cast<const T*>(a.comp);
 
-    for (int t0 = vr0; t0 < vr1; t0 += kTile) {
-        // ---- row list of this tile
-        if (tid < kTile) {
-            const int vr = t0 + tid;
+    for (int c0 = vr0; c0 < vr1; c0 += kChunkRows) {
+        const int c1 = min(vr1, c0 + kChunkRows);
+        // ---- row list of this chunk: one thread per virtual row
+        {
+            const int vr = c0 + tid;
             long long off = -1;
             int src = 0;
-            if (vr < vr1) {
+            if (vr < c1) {
                 if (vr < a.W) {
                     if constexpr (PREFILL) {
                         const int tok = qpos - a.W + 1 + vr;
@@ -192,30 +210,48 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             row_off[tid] = off;
             row_src[tid] = src;
         }
-        if (tid == 0) tile_any = 0;
+        if (tid < kChunkRows / kTile) tile_any[tid] = 0;
         __syncthreads();
-        if (tid < kTile && row_off[tid] >= 0) tile_any = 1;  // benign race: all write 1
-        // ---- gather rows into LDS (row-major K, transposed V)
-        for (int c = tid; c < kTile * CPR; c += kAttnThreads) {
-            const int r = c / CPR, ch = c % CPR;
-            const long long off = row_off[r];
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (off >= 0) {
-                const T* base = row_src[r] ? comp : win;
-                v = *reinterpret_cast<const u32x4*>(base + off + (long long)ch * V16);
-            }
-            *reinterpret_cast<u32x4*>(Ks + (size_t)r * L::kStrideK + ch * V16) = v;
-            if (ch * V16 < DV) {
-                const T* e = reinterpret_cast<const T*>(&v);
+        if (row_off[tid] >= 0) tile_any[tid / kTile] = 1;  // benign race: all write 1
+        __syncthreads();
+
+    for (int t0 = c0; t0 < c1; t0 += kTile) {
+        const int tb = t0 - c0;
+        if (!tile_any[tb / kTile]) continue;  // uniform: nothing valid in this tile
+        // ---- gather: a thread moves chunk `ch` of the row pair (2rp, 2rp+1);
+        // K goes row-major, V transposed with the two rows packed in one write
+        // (consecutive lanes -> consecutive words: no bank conflicts)
+        constexpr int kUnits = (kTile / 2) * CPR;
+        constexpr int kIter = (kUnits + kAttnThreads - 1) / kAttnThreads;
+        u32x4 ga[kIter], gb[kIter];
 #pragma unroll
-                for (int x = 0; x < V16; ++x) Vt[(size_t)(ch * V16 + x) * L::kStrideV + r] = e[x];
+        for (int it = 0; it < kIter; ++it) {
+            const int u = tid + it * kAttnThreads;
+            const int rp = u % (kTile / 2), ch = u / (kTile / 2);
+            ga[it] = gb[it] = u32x4{0u, 0u, 0u, 0u};
+            if (u < kUnits) {
+                const long long oa = row_off[tb + 2 * rp], ob = row_off[tb + 2 * rp + 1];
+                if (oa >= 0)
+                    ga[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp] ? comp : win) + oa + (long long)ch * V16);
+                if (ob >= 0)
+                    gb[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp + 1] ? comp : win) + ob + (long long)ch * V16);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < kIter; ++it) {
+            const int u = tid + it * kAttnThreads;
+            const int rp = u % (kTile / 2), ch = u / (kTile / 2);
+            if (u < kUnits) {
+                *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp) * L::kStrideK + ch * V16) = ga[it];
+                *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp + 1) * L::kStrideK + ch * V16) = gb[it];
+                if (ch * V16 < DV) {
+#pragma unroll
+                    for (int x = 0; x < V16; ++x)
+                        Pair<T>::put(Vt + (size_t)(ch * V16 + x) * L::kStrideV + 2 * rp, ga[it], gb[it], x);
+                }
             }
         }
         __syncthreads();
-        if (!tile_any) {
-            __syncthreads();
-            continue;
-        }
 
         // ---- S^T tile: rows 16*mt + 4*quad + r, head `hl`
         f32x4 s[2];
@@ -245,7 +281,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = mt * 16 + quad * 4 + r;
-                const float v = row_off[row] >= 0 ? s[mt][r] * a.scale_log2 : -INFINITY;
+                const float v = row_off[tb + row] >= 0 ? s[mt][r] * a.scale_log2 : -INFINITY;
                 x[mt * 4 + r] = v;
                 tmax = fmaxf(tmax, v);
             }
@@ -305,6 +341,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         }
         __syncthreads();  // LDS tile is rewritten by the next iteration
     }
+    }
 
     // ---- epilogue.  acc[t][r] = O^T[16*t + 4*quad + r][head]
     if (!head_ok) return;
@@ -333,33 +370,74 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         a.lse[orow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
-// Merge the split partials of one (sequence, head): fixed split order.
+// Merge the split partials of one (sequence, head) in a fixed split order.
+// All (max, sum) pairs are loaded at once, the weights go through LDS, and
+// each thread then issues the loads of its 4 channels for every split before
+// combining them.
+constexpr int kMaxSplit = 128;
+
 template <typename T, int DV>
 __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part,
                                                          void* __restrict__ out,
                                                          float* __restrict__ lse, int H,
                                                          int n_split) {
-    const int b = blockIdx.y, h = blockIdx.x;
+    __shared__ float wsp[kMaxSplit], lsp[kMaxSplit];
+    __shared__ float stat[2];
+    const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
     const float* p0 = part + ((size_t)b * n_split * H + h) * (2 + DV);
     const size_t sstride = (size_t)H * (2 + DV);
-    float mx = -INFINITY;
-    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, p0[s * sstride]);
-    float L = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-        const float ms = p0[s * sstride];
-        if (ms != -INFINITY) L += p0[s * sstride + 1] * exp2f(ms - mx);
+    float ms = -INFINITY, ls = 0.f;
+    if (tid < n_split) {
+        ms = p0[tid * sstride];
+        ls = p0[tid * sstride + 1];
     }
+    wsp[tid] = ms;
+    __syncthreads();
+    if (tid == 0) {
+        float mx = -INFINITY;
+        for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, wsp[s]);
+        stat[0] = mx;
+    }
+    __syncthreads();
+    const float mx = stat[0];
+    const float wgt = (tid < n_split && ms != -INFINITY) ? exp2f(ms - mx) : 0.f;
+    __syncthreads();
+    wsp[tid] = wgt;
+    lsp[tid] = ls * wgt;
+    __syncthreads();
+    if (tid == 0) {
+        float L = 0.f;
+        for (int s = 0; s < n_split; ++s) L += lsp[s];
+        stat[1] = L;
+    }
+    __syncthreads();
+    const float L = stat[1];
     const float inv = L > 0.f ? 1.f / L : 0.f;
     T* o = reinterpret_cast<T*>(out) + ((size_t)b * H + h) * DV;
-    for (int d = threadIdx.x; d < DV; d += blockDim.x) {
-        float v = 0.f;
-        for (int s = 0; s < n_split; ++s) {
-            const float ms = p0[s * sstride];
-            if (ms != -INFINITY) v = fmaf(p0[s * sstride + 2 + d], exp2f(ms - mx), v);
+    for (int d = tid * 4; d < DV; d += 128 * 4) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < n_split; s0 += 8) {
+            f32x4 pv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int s = s0 + j;
+                pv[j] = s < n_split ? *reinterpret_cast<const f32x4*>(p0 + s * sstride + 2 + d)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int s = s0 + j;
+                if (s < n_split) {
+                    const float wj = wsp[s];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(pv[j][e], wj, acc[e]);
+                }
+            }
         }
-        Elem<T>::store(o, d, v * inv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Elem<T>::store(o, d + e, acc[e] * inv);
     }
-    if (lse && threadIdx.x == 0) lse[(size_t)b * H + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    if (lse && tid == 0) lse[(size_t)b * H + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int DQK, int DV, bool PREFILL>
@@ -407,6 +485,7 @@ DecodePlan plan_decode(int B, int H, int max_rows) {
     const int max_split = ceil_div(tiles, 2);
     if (n_split > max_split) n_split = max_split;
     if (n_split < 1) n_split = 1;
+    if (n_split > kMaxSplit) n_split = kMaxSplit;
     const int tiles_per = ceil_div(tiles, n_split);
     p.rows_per_split = tiles_per * kTile;
     p.n_split = ceil_div(max_rows, p.rows_per_split);

@@ -24,11 +24,13 @@
 //  - larger n: the scoring kernel also builds the 2048-bin histogram of the
 //    top 11 key bits per query (LDS histogram, integer atomics to global).
 //    A filter kernel then sends every candidate above the threshold bin to
-//    the "selected" list and every candidate inside it to a short list; the
-//    last filter workgroup of each query finishes the select on that short
-//    list in LDS (two more histogram passes, plus a pass over indices when
-//    a tie straddles rank k), sorts the result ascending and zeroes its
-//    part of the workspace for the next call.
+//    the "selected" list and every candidate inside it to a short list (one
+//    atomic reservation per workgroup and list).  A final kernel, one
+//    workgroup per query, finishes the select on the short list in LDS (two
+//    more histogram passes, plus passes over indices when a tie straddles
+//    rank k), sorts the result ascending and zeroes what the call wrote in
+//    the workspace.  The kernel boundaries order every hand-off, so no
+//    workgroup waits on or fences for another.
 #include "hsa_common.hpp"
 #include "hsa_internal.hpp"
 
@@ -41,7 +43,7 @@ constexpr int kNW = kThreads / kWave;
 constexpr int kBins = 2048;         // first digit: key bits 31..21
 constexpr int kFilterChunk = 4096;  // scores per filter workgroup
 constexpr int kCandCap = 4096;      // short-list entries the final select keeps in LDS
-constexpr int kScoreRowsMulti = 2048;
+constexpr int kScoreRowsMulti = 1024;
 
 // ---- workspace (multi-workgroup path), per query -------------------------
 //   hist[2048] u32 | ctr[16] u32 (0: short-list size, 1: selected size,
@@ -70,32 +72,71 @@ __device__ inline QWs ws_of(uint8_t* ws, int q, int S_max, int k) {
     return w;
 }
 
-// Counters that other workgroups of the same launch update with atomics.
-__device__ inline uint32_t counter_load(const uint32_t* p) {
-    return __atomic_load_n(p, __ATOMIC_RELAXED);
-}
-
 __device__ inline int clamp_n(const int32_t* n_cand, int q, int S_max) {
     int n = n_cand[q];
     return n < 0 ? 0 : (n > S_max ? S_max : n);
 }
 
-template <typename T> __device__ inline float widen(const T* p, size_t i);
-template <> __device__ inline float widen<float>(const float* p, size_t i) { return p[i]; }
-template <> __device__ inline float widen<bf16_t>(const bf16_t* p, size_t i) {
-    return __uint_as_float((uint32_t)p[i].bits << 16);
+// ---- scoring ---------------------------------------------------------------
+// Lanes of a wave are split into row groups of LPR lanes; lane `sub` of a row
+// group reads the sub-th 16-byte chunk of a key row.  A lane keeps U = 8 rows
+// per batch (one per load), forms its 8 partial dot products, and the row
+// group reduces them with a reduce-scatter butterfly: three halving steps
+// over the top three lane bits (8 -> 4 -> 2 -> 1 rows per lane) and plain
+// xor steps over the remaining bits.  Every row's sum has the same tree over
+// the LPR chunk partials (fp add is commutative), so equal rows give equal
+// scores wherever they sit.
+template <int LPR>
+__device__ __forceinline__ float reduce_scatter8(float (&v)[8], int sub) {
+    constexpr int LB = (LPR == 8) ? 3 : (LPR == 16 ? 4 : 5);  // log2(LPR)
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "rows are 128, 256 or 512 bytes");
+    // step over bit LB-1: 8 -> 4
+    {
+        const int m = 1 << (LB - 1);
+        const bool hi = (sub & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float send = hi ? v[i] : v[i + 4];
+            const float keep = hi ? v[i + 4] : v[i];
+            v[i] = keep + __shfl_xor(send, m, kWave);
+        }
+    }
+    {
+        const int m = 1 << (LB - 2);
+        const bool hi = (sub & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float send = hi ? v[i] : v[i + 2];
+            const float keep = hi ? v[i + 2] : v[i];
+            v[i] = keep + __shfl_xor(send, m, kWave);
+        }
+    }
+    float r;
+    {
+        const int m = 1 << (LB - 3);
+        const bool hi = (sub & m) != 0;
+        const float send = hi ? v[0] : v[1];
+        const float keep = hi ? v[1] : v[0];
+        r = keep + __shfl_xor(send, m, kWave);
+    }
+#pragma unroll
+    for (int b = LB - 4; b >= 0; --b) r += __shfl_xor(r, 1 << b, kWave);
+    return r;  // the row (sub >> (LB - 3)) of the batch
 }
 
-// ---- scoring ---------------------------------------------------------------
 template <typename T, int LPR, bool HIST>
 __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ n_cand, float* __restrict__ scores, uint8_t* __restrict__ ws,
     int B, int H_I, int S_max, int k, int rows_per_wg) {
     constexpr int V = Elem<T>::kPer16B;
-    constexpr int DI = LPR * V;          // indexer width
-    constexpr int RPL = kWave / LPR;     // rows covered by one wave-wide load
-    constexpr int UNROLL = 8;
+    constexpr int DI = LPR * V;            // indexer width
+    constexpr int RPL = kWave / LPR;       // rows covered by one wave-wide load
+    constexpr int U = 8;                   // loads per lane per batch
+    constexpr int RPB = RPL * U;           // rows per wave batch
+    constexpr int NG = kThreads / LPR;     // partial head sums per channel
+    constexpr int LB = (LPR == 8) ? 3 : (LPR == 16 ? 4 : 5);
+    __shared__ float qpart[NG][DI];
     __shared__ float qsum[DI];
     __shared__ uint32_t hist[HIST ? kBins : 1];
 
@@ -107,48 +148,92 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const int r1 = min(n, r0 + rows_per_wg);
     if (r0 >= r1) return;  // uniform over the workgroup
 
-    const int tid = threadIdx.x;
-    for (int e = tid; e < DI; e += kThreads) {
-        float s = 0.f;
-        for (int h = 0; h < H_I; ++h) s += widen<T>(q_idx, ((size_t)q * H_I + h) * DI + e);
-        qsum[e] = s;
-    }
-    if constexpr (HIST)
-        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-    __syncthreads();
-
-    const int lane = lane_id(), w = tid / kWave;
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int sub = lane % LPR, rs = lane / LPR;
-    float qv[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) qv[e] = qsum[sub * V + e];
     const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)sub * V;
-    float* srow = scores + (size_t)q * S_max;
+    const int nb = ceil_div(r1 - r0, RPB);  // wave batches of this workgroup
 
-    const int nit = ceil_div(r1 - r0, kNW * RPL);
-    for (int it0 = 0; it0 < nit; it0 += UNROLL) {
-        u32x4 buf[UNROLL];
+    auto load_batch = [&](u32x4 (&buf)[U], int bi) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int r = r0 + ((it0 + u) * kNW + w) * RPL + rs;
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + bi * RPB + u * RPL + rs;
             const int rc = r < r1 ? r : r1 - 1;  // stay inside this query's rows
             buf[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)rc * DI);
         }
+    };
+
+    // first batch in flight before the head fold
+    u32x4 cur[U];
+    int bi = w;
+    if (bi < nb) load_batch(cur, bi);
+
+    // fold the heads: thread t sums the chunks t, t+256, ... of q_idx[q] (all
+    // loads issued together), then the NG partials of each channel are added
+    // in a fixed order
+    {
+        const int ec = tid % LPR, grp = tid / LPR;
+        const int nchunks = H_I * LPR;
+        const T* qb = q_idx + (size_t)q * H_I * DI;
+        float part[V];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int r = r0 + ((it0 + u) * kNW + w) * RPL + rs;
-            float kv[V];
-            Elem<T>::unpack(buf[u], kv);
-            float d = 0.f;
+        for (int e = 0; e < V; ++e) part[e] = 0.f;
+        for (int c0 = tid; c0 < nchunks; c0 += 4 * kThreads) {
+            u32x4 t4[4];
 #pragma unroll
-            for (int e = 0; e < V; ++e) d = fmaf(qv[e], kv[e], d);
+            for (int j = 0; j < 4; ++j) {
+                const int c = c0 + j * kThreads;
+                t4[j] = c < nchunks ? *reinterpret_cast<const u32x4*>(qb + (size_t)c * V)
+                                    : u32x4{0u, 0u, 0u, 0u};
+            }
 #pragma unroll
-            for (int o = 1; o < LPR; o <<= 1) d += __shfl_xor(d, o, kWave);
-            if (sub == 0 && r < r1) {
-                srow[r] = d;
-                if constexpr (HIST) atomicAdd(&hist[score_key(d) >> 21], 1u);
+            for (int j = 0; j < 4; ++j) {
+                float f[V];
+                Elem<T>::unpack(t4[j], f);
+#pragma unroll
+                for (int e = 0; e < V; ++e) part[e] += f[e];
             }
         }
+#pragma unroll
+        for (int e = 0; e < V; ++e) qpart[grp][ec * V + e] = part[e];
+        if constexpr (HIST)
+            for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+        __syncthreads();
+        for (int e = tid; e < DI; e += kThreads) {
+            float acc = 0.f;
+            for (int g = 0; g < NG; ++g) acc += qpart[g][e];
+            qsum[e] = acc;
+        }
+        __syncthreads();
+    }
+    float qv[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) qv[e] = qsum[sub * V + e];
+    float* srow = scores + (size_t)q * S_max;
+    const bool writer = (sub & ((1 << (LB - 3)) - 1)) == 0;
+    const int my_u = sub >> (LB - 3);
+
+    for (; bi < nb; bi += kNW) {
+        u32x4 nxt[U];
+        const int bn = bi + kNW;
+        if (bn < nb) load_batch(nxt, bn);  // next batch in flight while this one is reduced
+        float d[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kv[V];
+            Elem<T>::unpack(cur[u], kv);
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc = fmaf(qv[e], kv[e], acc);
+            d[u] = acc;
+        }
+        const float sc = reduce_scatter8<LPR>(d, sub);
+        const int r = r0 + bi * RPB + my_u * RPL + rs;
+        if (writer && r < r1) {
+            srow[r] = sc;
+            if constexpr (HIST) atomicAdd(&hist[score_key(sc) >> 21], 1u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
     if constexpr (HIST) {
         __syncthreads();
@@ -293,42 +378,31 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
 }
 
 // ---- multi-workgroup path: filter + final select ---------------------------------
-__device__ inline void wave_append(bool pred, uint32_t* counter, uint32_t cap, uint32_t* dst0,
-                                   uint32_t v0, uint32_t* dst1, uint32_t v1) {
-    const uint64_t mask = __ballot(pred);
-    if (mask == 0) return;
-    const int lane = lane_id();
-    const int leader = __ffsll((long long)mask) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = __shfl(base, leader, kWave);
-    if (pred) {
-        const uint32_t pos = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-        if (pos < cap) {
-            dst0[pos] = v0;
-            if (dst1) dst1[pos] = v1;
-        }
-    }
-}
+constexpr int kPerThread = kFilterChunk / kThreads;  // scores per thread (16)
+static_assert(kPerThread <= 16, "per-thread counts are packed in 16 bits");
 
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ n_cand,
-                                                               int32_t* __restrict__ out,
                                                                uint8_t* __restrict__ ws, int S_max,
-                                                               int k, int G) {
+                                                               int k) {
     __shared__ uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
-    __shared__ uint32_t ck[kCandCap], ci[kCandCap];
-    __shared__ int32_t sel[kTopkMaxK];
-    __shared__ uint32_t nsel_lds;
-    __shared__ int is_last;
+    __shared__ uint32_t base_lds[2];
 
     const int q = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
     const int n = clamp_n(n_cand, q, S_max);
     const int take = min(k, n);
+    const int s0 = g * kFilterChunk;
 
-    // 1. threshold bin of the first digit from the completed histogram
+    // 1. this chunk's scores (all loads in flight together) and the threshold
+    //    bin of the first digit from the completed histogram
+    float v[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int s = s0 + i * kThreads + tid;
+        v[i] = s < n ? scores[(size_t)q * S_max + s] : 0.f;
+    }
     int t1 = -1;  // -1: every candidate is selected
     if (take < n) {
         for (int i = tid; i < kBins; i += kThreads) h[i] = W.hist[i];
@@ -337,35 +411,76 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         t1 = find_crossing<kBins>(h, take, tmp, &rem);
     }
 
-    // 2. route this chunk's candidates
-    const int s0 = g * kFilterChunk, s1 = min(n, s0 + kFilterChunk);
-    for (int base = s0; base < s1; base += kThreads) {
-        const int s = base + tid;
-        const bool in = s < s1;
-        const uint32_t key = in ? score_key(scores[(size_t)q * S_max + s]) : 0u;
-        const int bin = (int)(key >> 21);
-        wave_append(in && bin > t1, &W.ctr[1], (uint32_t)k, reinterpret_cast<uint32_t*>(W.sel),
-                    (uint32_t)s, nullptr, 0u);
-        wave_append(in && bin == t1, &W.ctr[0], (uint32_t)S_max, W.cand_key, key, W.cand_idx,
-                    (uint32_t)s);
+    // 2. route: above the threshold bin -> selected list, inside it -> short
+    //    list; one reservation per workgroup and list, offsets by prefix sum
+    uint32_t selm = 0, candm = 0, keys[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const int s = s0 + i * kThreads + tid;
+        keys[i] = score_key(v[i]);
+        const int bin = (int)(keys[i] >> 21);
+        if (s < n && bin > t1) selm |= 1u << i;
+        if (s < n && bin == t1) candm |= 1u << i;
+    }
+    const uint32_t packed = ((uint32_t)__popc(selm) << 16) | (uint32_t)__popc(candm);
+    uint32_t tot;
+    const uint32_t off = block_excl_scan<kThreads>(packed, tmp, &tot);
+    if (tid == 0) {
+        base_lds[0] = (tot >> 16) ? atomicAdd(&W.ctr[1], tot >> 16) : 0u;
+        base_lds[1] = (tot & 0xffffu) ? atomicAdd(&W.ctr[0], tot & 0xffffu) : 0u;
+    }
+    __syncthreads();
+    uint32_t ps = base_lds[0] + (off >> 16), pc = base_lds[1] + (off & 0xffffu);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        const uint32_t s = (uint32_t)(s0 + i * kThreads + tid);
+        if (selm & (1u << i)) {
+            if (ps < (uint32_t)k) W.sel[ps] = (int32_t)s;
+            ++ps;
+        }
+        if (candm & (1u << i)) {
+            if (pc < (uint32_t)S_max) { W.cand_key[pc] = keys[i]; W.cand_idx[pc] = s; }
+            ++pc;
+        }
     }
 
-    // 3. the last workgroup of this query finishes
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = (atomicAdd(&W.ctr[2], 1u) == (uint32_t)(G - 1));
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
+}
 
-    // counters read once and broadcast, so every branch below is uniform
+// Final select, one workgroup per query, after every filter workgroup of the
+// query has finished (kernel boundary): the short list is narrowed with two
+// LDS histogram passes (bits 20..10, 9..0 of the key) and, when a tie
+// straddles rank k, three passes over the complemented indices; the selected
+// indices are sorted ascending (bitonic, in LDS) and every word the call
+// wrote in the workspace is zeroed again.
+__global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __restrict__ n_cand,
+                                                              int32_t* __restrict__ out,
+                                                              uint8_t* __restrict__ ws, int S_max,
+                                                              int k) {
+    __shared__ uint32_t h[kBins];
+    __shared__ uint32_t tmp[kNW + 2];
+    __shared__ uint32_t ck[kCandCap], ci[kCandCap];
+    __shared__ int32_t sel[kTopkMaxK];
+    __shared__ uint32_t nsel_lds;
     __shared__ int cnt[2], cnt_raw[2];
+
+    const int q = blockIdx.x, tid = threadIdx.x;
+    QWs W = ws_of(ws, q, S_max, k);
+    const int n = clamp_n(n_cand, q, S_max);
+    const int take = min(k, n);
     if (tid == 0) {
-        const uint32_t a = counter_load(&W.ctr[1]), b = counter_load(&W.ctr[0]);
-        cnt[0] = min((int)min(a, (uint32_t)take), take);
+        const uint32_t a = W.ctr[1], b = W.ctr[0];
+        cnt[0] = (int)min(a, (uint32_t)take);
         cnt[1] = (int)min(b, (uint32_t)S_max);
         cnt_raw[0] = (int)min(a, (uint32_t)k);      // entries written to sel (capacity k)
         cnt_raw[1] = (int)min(b, (uint32_t)S_max);  // entries written to the short list
+    }
+    // the threshold bin again (the filter kernel did the same on the same histogram)
+    int t1 = -1;
+    if (take < n) {
+        for (int i = tid; i < kBins; i += kThreads) h[i] = W.hist[i];
+        __syncthreads();
+        int rem;
+        t1 = find_crossing<kBins>(h, take, tmp, &rem);
     }
     __syncthreads();
     const int nsel0 = cnt[0];
@@ -402,7 +517,6 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         // the need lowest indices among the T-valued: select on ~idx
         uint32_t imax = 0xffffffffu;  // take every T-valued candidate
         if ((int)eq_all > need) {
-            // ~idx of the need-th smallest index, found digit by digit
             // digits of ~idx, highest first, among the T-valued candidates
             int r = need;
             uint32_t pr = 0, pm = 0;
@@ -458,7 +572,6 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     // Leave every word this call wrote for this query zeroed again (histogram,
     // counters, short list, selected list), so the whole workspace is zero
     // whatever layout the next call uses.
-    __syncthreads();
     for (int i = tid; i < kBins; i += kThreads) W.hist[i] = 0;
     for (int i = tid; i < cnt_raw[1]; i += kThreads) { W.cand_key[i] = 0; W.cand_idx[i] = 0; }
     for (int i = tid; i < cnt_raw[0]; i += kThreads) W.sel[i] = 0;
@@ -529,7 +642,10 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     } else {
         const int G = ceil_div(S_max, kFilterChunk);
         hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0,
-                           st, scores, n_cand, topk_idx, w, S_max, k, G);
+                           st, scores, n_cand, w, S_max, k);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)Nq), dim3(kThreads), 0, st, n_cand,
+                           topk_idx, w, S_max, k);
     }
     return hipGetLastError();
 }

@@ -117,3 +117,29 @@ def test_full_size_decode_selection(oracle, name):
         dup = np.nonzero(first[inv.ravel()] != np.arange(S))[0]
         assert len(dup) > 0
         np.testing.assert_array_equal(sg[b, dup], sg[b, first[inv.ravel()][dup]])
+
+
+@pytest.mark.parametrize("dt,d_I,S_max", [(torch.bfloat16, 64, 5000), (torch.bfloat16, 256, 14000),
+                                          (torch.float32, 32, 3000), (torch.float32, 128, 13000),
+                                          (torch.bfloat16, 128, 777)])
+def test_scores_all_row_widths(oracle, dt, d_I, S_max):
+    """128-, 256- and 512-byte key rows (8, 16 and 32 lanes per row), both select paths."""
+    import hybrid_sparse_compressed_amd as hsa
+
+    g = torch.Generator().manual_seed(d_I + S_max)
+    B, Nq, H_I, k = 2, 5, 7, 96
+    q_idx = torch.randn(Nq, H_I, d_I, generator=g).to(dt)
+    k_idx = torch.randn(B, S_max, d_I, generator=g).to(dt)
+    k_idx[1, 5:9] = k_idx[1, 100]  # equal rows at different positions of a batch
+    q_seq = torch.tensor([0, 1, 1, 0, 1], dtype=torch.int32)
+    n_cand = torch.tensor([S_max, S_max - 1, 33, 0, S_max // 2], dtype=torch.int32)
+    note("index widths %s d_I=%d S=%d" % (dt, d_I, S_max))
+    s, idx = hsa.hsa_index_topk(q_idx.cuda(), k_idx.cuda(), n_cand, k, q_seq=q_seq)
+    torch.cuda.synchronize()
+    ref = oracle.index_scores(q_idx, k_idx, n_cand.numpy(), q_seq=q_seq.numpy())
+    _check_scores(s, ref, q_idx, k_idx, q_seq.numpy(), n_cand.numpy())
+    sg = s.cpu().numpy()
+    for i in (1, 4):  # queries of sequence 1 that see row 100
+        assert np.all(sg[i, 5:9] == sg[i, 100])
+    want = oracle.topk(ref.astype(np.float32), n_cand.numpy(), k)
+    assert _overlap(idx.cpu().numpy(), want) >= 0.999
