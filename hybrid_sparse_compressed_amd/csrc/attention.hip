@@ -82,7 +82,8 @@ struct AttnArgs {
     const int32_t* comp_len;
     void* out;
     float* lse;
-    float* part;          // decode partials: [B][n_split][H][2 + d_v]
+    float* part_ml;       // decode partials: (max, sum) [B][n_split][H][2]
+    float* part_o;        //                  outputs    [B][n_split][H][d_v]
     int H, W, S_max, k, m, T_len, n_q, q_start;
     int rows_per_split, n_split, max_rows;
     float scale_log2;     // scale * log2(e)
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     constexpr int CPR = DQK / V16;                 // 16-byte chunks per row
     constexpr int NKK = DQK / M::kK;               // MFMA steps of the QK product
     constexpr int NMT = DV / 16;                   // O^T row tiles
-    static_assert(DQK % M::kK == 0 && DV % 16 == 0 && DV <= DQK, "unsupported head dims");
+    static_assert(DQK % M::kK == 0 && DV % 16 == 0 && DV <= DQK && DV <= 512, "unsupported head dims");
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
     T* Ks = reinterpret_cast<T*>(lds_raw);
@@ -147,6 +148,42 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         n_comp = n_comp < 0 ? 0 : (n_comp > a.S_max ? a.S_max : n_comp);
     }
 
+    // Row list entry of virtual row vr (chunk end c1): element offset of the
+    // latent row in its source (-1: not a row of this query) and the source.
+    auto row_entry = [&](int vr, int c1, long long& off, int& src) {
+        off = -1;
+        src = 0;
+        if (vr >= c1) return;
+        if (vr < a.W) {
+            if constexpr (PREFILL) {
+                const int tok = qpos - a.W + 1 + vr;
+                if (tok >= 0) off = ((long long)b * a.T_len + tok) * DQK;
+            } else {
+                if (vr < n_swa) off = ((long long)b * a.W + vr) * DQK;
+            }
+        } else {
+            const int j = vr - a.W;
+            int ci = -1;
+            if (a.comp_idx) {
+                if (j < a.k) {
+                    const long long row = PREFILL ? (long long)qid : (long long)b;
+                    ci = a.comp_idx[row * a.k + j];
+                }
+            } else {
+                ci = j;
+            }
+            if (ci >= 0 && ci < n_comp) {
+                off = ((long long)b * a.S_max + ci) * DQK;
+                src = 1;
+            }
+        }
+    };
+    // the first chunk's index loads go out before the Q loads, so waiting for
+    // them does not wait for Q (the vector-memory counter retires in order)
+    long long first_off;
+    int first_src;
+    row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
+
     // Q fragments for this lane's head: k-slots of lane group `quad`
     typename M::frag qf[NKK];
     {
@@ -179,34 +216,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         const int c1 = min(vr1, c0 + kChunkRows);
         // ---- row list of this chunk: one thread per virtual row
         {
-            const int vr = c0 + tid;
-            long long off = -1;
-            int src = 0;
-            if (vr < c1) {
-                if (vr < a.W) {
-                    if constexpr (PREFILL) {
-                        const int tok = qpos - a.W + 1 + vr;
-                        if (tok >= 0) off = ((long long)b * a.T_len + tok) * DQK;
-                    } else {
-                        if (vr < n_swa) off = ((long long)b * a.W + vr) * DQK;
-                    }
-                } else {
-                    const int j = vr - a.W;
-                    int ci = -1;
-                    if (a.comp_idx) {
-                        if (j < a.k) {
-                            const long long row = PREFILL ? (long long)qid : (long long)b;
-                            ci = a.comp_idx[row * a.k + j];
-                        }
-                    } else {
-                        ci = j;
-                    }
-                    if (ci >= 0 && ci < n_comp) {
-                        off = ((long long)b * a.S_max + ci) * DQK;
-                        src = 1;
-                    }
-                }
-            }
+            long long off = first_off;
+            int src = first_src;
+            if (c0 != vr0) row_entry(c0 + tid, c1, off, src);
             row_off[tid] = off;
             row_src[tid] = src;
         }
@@ -287,15 +299,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        const float m_new = fmaxf(m_run, tmax);
+        // The reference max only moves when a logit exceeds it by more than
+        // 2^8 (p stays <= 256, no overflow); the rescale of the accumulator is
+        // skipped unless some lane of the wave moved a nonzero accumulator.
+        const bool move = tmax > m_run + 8.f;
+        const float m_new = move ? tmax : m_run;
+        const float alpha = move ? exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
         float p[8];
         float psum = 0.f;
-        float alpha = 1.f;
         if (m_new == -INFINITY) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = 0.f;
         } else {
-            alpha = exp2f(m_run - m_new);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 p[j] = exp2f(x[j] - m_new);
@@ -304,10 +319,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         }
         psum += __shfl_xor(psum, 16, kWave);
         psum += __shfl_xor(psum, 32, kWave);
+        if (__ballot(move && l_run > 0.f)) {
+#pragma unroll
+            for (int t = 0; t < NMT; ++t) acc[t] *= alpha;
+        }
         l_run = l_run * alpha + psum;
         m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < NMT; ++t) acc[t] *= alpha;
 
         // ---- O^T += V^T * P^T
         if constexpr (sizeof(T) == 2) {
@@ -347,15 +364,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     if (!head_ok) return;
     if constexpr (!PREFILL) {
         if (a.n_split > 1) {
-            float* pb = a.part + (((size_t)b * a.n_split + blockIdx.x) * a.H + head) * (2 + DV);
-            if (quad == 0) {
-                pb[0] = m_run;
-                pb[1] = l_run;
-            }
+            const size_t prow = ((size_t)b * a.n_split + blockIdx.x) * a.H + head;
+            if (quad == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = float2{m_run, l_run};
+            float* pb = a.part_o + prow * DV;
 #pragma unroll
             for (int t = 0; t < NMT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pb[2 + t * 16 + quad * 4 + r] = acc[t][r];
+                *reinterpret_cast<f32x4*>(pb + t * 16 + quad * 4) = acc[t];
             return;
         }
     }
@@ -377,19 +391,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 constexpr int kMaxSplit = 128;
 
 template <typename T, int DV>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_ml,
+                                                         const float* __restrict__ part_o,
                                                          void* __restrict__ out,
                                                          float* __restrict__ lse, int H,
                                                          int n_split) {
+    constexpr int kBatch = 32;  // split partials loaded per round
     __shared__ float wsp[kMaxSplit], lsp[kMaxSplit];
     __shared__ float stat[2];
     const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
-    const float* p0 = part + ((size_t)b * n_split * H + h) * (2 + DV);
-    const size_t sstride = (size_t)H * (2 + DV);
+    const float* p0 = part_o + ((size_t)b * n_split * H + h) * DV;
+    const size_t sstride = (size_t)H * DV;
+    const int d = tid * 4;           // this thread's 4 channels (DV <= 512)
+    const bool has_d = d < DV;
+    // first round of output partials in flight with the (max, sum) loads
+    f32x4 pv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+        pv[j] = (has_d && j < n_split) ? *reinterpret_cast<const f32x4*>(p0 + j * sstride + d)
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
     float ms = -INFINITY, ls = 0.f;
     if (tid < n_split) {
-        ms = p0[tid * sstride];
-        ls = p0[tid * sstride + 1];
+        const float2 v = *reinterpret_cast<const float2*>(part_ml + (((size_t)b * n_split + tid) * H + h) * 2);
+        ms = v.x;
+        ls = v.y;
     }
     wsp[tid] = ms;
     __syncthreads();
@@ -413,27 +438,28 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
     __syncthreads();
     const float L = stat[1];
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    T* o = reinterpret_cast<T*>(out) + ((size_t)b * H + h) * DV;
-    for (int d = tid * 4; d < DV; d += 128 * 4) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < n_split; s0 += 8) {
-            f32x4 pv[8];
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+        if (s0 > 0) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < kBatch; ++j) {
                 const int s = s0 + j;
-                pv[j] = s < n_split ? *reinterpret_cast<const f32x4*>(p0 + s * sstride + 2 + d)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int s = s0 + j;
-                if (s < n_split) {
-                    const float wj = wsp[s];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(pv[j][e], wj, acc[e]);
-                }
+                pv[j] = (has_d && s < n_split) ? *reinterpret_cast<const f32x4*>(p0 + s * sstride + d)
+                                               : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int s = s0 + j;
+            if (s < n_split) {
+                const float wj = wsp[s];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(pv[j][e], wj, acc[e]);
+            }
+        }
+    }
+    if (has_d) {
+        T* o = reinterpret_cast<T*>(out) + ((size_t)b * H + h) * DV;
 #pragma unroll
         for (int e = 0; e < 4; ++e) Elem<T>::store(o, d + e, acc[e] * inv);
     }
@@ -479,13 +505,12 @@ DecodePlan plan_decode(int B, int H, int max_rows) {
     p.max_rows = max_rows;
     const int hblocks = ceil_div(H, kHeadsPerWG);
     const int tiles = ceil_div(max_rows, kTile);
-    // aim for about two workgroups per compute unit, at least 2 tiles per split
-    int want = ceil_div(512, B * hblocks);
-    int n_split = want < 1 ? 1 : want;
-    const int max_split = ceil_div(tiles, 2);
-    if (n_split > max_split) n_split = max_split;
-    if (n_split < 1) n_split = 1;
+    // about one workgroup per compute unit; a workgroup's tiles run one after
+    // another, so small batches get one tile per split
+    int n_split = ceil_div(256, B * hblocks);
+    if (n_split > tiles) n_split = tiles;
     if (n_split > kMaxSplit) n_split = kMaxSplit;
+    if (n_split < 1) n_split = 1;
     const int tiles_per = ceil_div(tiles, n_split);
     p.rows_per_split = tiles_per * kTile;
     p.n_split = ceil_div(max_rows, p.rows_per_split);
@@ -493,10 +518,16 @@ DecodePlan plan_decode(int B, int H, int max_rows) {
     return p;
 }
 
+// decode partials: (max, sum) pairs [B][n_split][H][2], then the unnormalised
+// outputs [B][n_split][H][d_v] (16-byte aligned rows)
+static size_t ml_bytes(int B, int n_split, int H) {
+    return (((size_t)B * n_split * H * 2 * sizeof(float)) + 255) & ~(size_t)255;
+}
+
 size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows) {
     const DecodePlan p = plan_decode(B, H, max_rows);
     if (p.n_split <= 1) return 0;
-    return (size_t)B * p.n_split * H * (2 + (size_t)d_v) * sizeof(float);
+    return ml_bytes(B, p.n_split, H) + (size_t)B * p.n_split * H * d_v * sizeof(float);
 }
 
 hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
@@ -513,7 +544,7 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
     a.comp_len = comp_len;
     a.out = out;
     a.lse = lse;
-    a.part = static_cast<float*>(ws);
+    a.part_ml = static_cast<float*>(ws);
     a.H = H;
     a.W = W;
     a.S_max = S_max;
@@ -524,6 +555,8 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
     a.max_rows = max_rows;
     a.rows_per_split = p.rows_per_split;
     a.n_split = p.n_split;
+    a.part_o = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ml_bytes(B, p.n_split, H))
+                  : nullptr;
     a.scale_log2 = scale * kLog2e;
     dim3 grid((unsigned)p.n_split, (unsigned)B, (unsigned)ceil_div(H, kHeadsPerWG));
     hipError_t e = dispatch_attn<false>(dtype, d_qk, d_v, a, grid, st);
@@ -532,11 +565,11 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
     ProfScope prof(kProfMerge, st);
     if (dtype == kBF16) {
         if (d_v == 512)
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512>), mg, dim3(128), 0, st, a.part, out, lse, H, p.n_split);
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512>), mg, dim3(128), 0, st, a.part_ml, a.part_o, out, lse, H, p.n_split);
         else
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128>), mg, dim3(128), 0, st, a.part, out, lse, H, p.n_split);
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, out, lse, H, p.n_split);
     } else {
-        hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mg, dim3(128), 0, st, a.part, out, lse, H, p.n_split);
+        hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, out, lse, H, p.n_split);
     }
     return hipGetLastError();
 }

@@ -46,15 +46,17 @@ constexpr int kCandCap = 4096;      // short-list entries the final select keeps
 constexpr int kScoreRowsMulti = 1024;
 
 // ---- workspace (multi-workgroup path), per query -------------------------
-//   hist[2048] u32 | ctr[16] u32 (0: short-list size, 1: selected size,
-//   2: finished filter workgroups) | cand_key[S_max] | cand_idx[S_max] | sel[k]
+//   hist[2048] u32 (key bits 31..21 of every candidate) | hist2[2048] u32
+//   (key bits 20..10 of the short list) | ctr[16] u32 (0: short-list size,
+//   1: selected size) | cand_key[S_max] | cand_idx[S_max] | sel[k]
 __host__ __device__ inline size_t ws_per_query(int S_max, int k) {
-    size_t b = (size_t)kBins * 4 + 64 + (size_t)S_max * 8 + (size_t)k * 4;
+    size_t b = (size_t)kBins * 8 + 64 + (size_t)S_max * 8 + (size_t)k * 4;
     return (b + 255) & ~(size_t)255;
 }
 
 struct QWs {
     uint32_t* hist;
+    uint32_t* hist2;
     uint32_t* ctr;
     uint32_t* cand_key;
     uint32_t* cand_idx;
@@ -65,7 +67,8 @@ __device__ inline QWs ws_of(uint8_t* ws, int q, int S_max, int k) {
     uint8_t* base = ws + (size_t)q * ws_per_query(S_max, k);
     QWs w;
     w.hist = reinterpret_cast<uint32_t*>(base);
-    w.ctr = w.hist + kBins;
+    w.hist2 = w.hist + kBins;
+    w.ctr = w.hist2 + kBins;
     w.cand_key = w.ctr + 16;
     w.cand_idx = w.cand_key + S_max;
     w.sel = reinterpret_cast<int32_t*>(w.cand_idx + S_max);
@@ -153,12 +156,22 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)sub * V;
     const int nb = ceil_div(r1 - r0, RPB);  // wave batches of this workgroup
 
+    // Key rows are read once: nontemporal loads keep them from displacing
+    // reusable lines in the caches.  Full batches need no row clamp.
     auto load_batch = [&](u32x4 (&buf)[U], int bi) {
+        const int rb = r0 + bi * RPB;
+        if (rb + RPB <= r1) {
+            const T* p = kbase + (size_t)(rb + rs) * DI;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = r0 + bi * RPB + u * RPL + rs;
-            const int rc = r < r1 ? r : r1 - 1;  // stay inside this query's rows
-            buf[u] = *reinterpret_cast<const u32x4*>(kbase + (size_t)rc * DI);
+            for (int u = 0; u < U; ++u)
+                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (size_t)u * RPL * DI));
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = rb + u * RPL + rs;
+                const int rc = r < r1 ? r : r1 - 1;  // stay inside this query's rows
+                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)rc * DI));
+            }
         }
     };
 
@@ -229,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         const float sc = reduce_scatter8<LPR>(d, sub);
         const int r = r0 + bi * RPB + my_u * RPL + rs;
         if (writer && r < r1) {
-            srow[r] = sc;
+            __builtin_nontemporal_store(sc, srow + r);
             if constexpr (HIST) atomicAdd(&hist[score_key(sc) >> 21], 1u);
         }
 #pragma unroll
@@ -441,17 +454,25 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         if (candm & (1u << i)) {
             if (pc < (uint32_t)S_max) { W.cand_key[pc] = keys[i]; W.cand_idx[pc] = s; }
             ++pc;
+            atomicAdd(&W.hist2[(keys[i] >> 10) & (kBins - 1)], 1u);
         }
     }
 
 }
 
 // Final select, one workgroup per query, after every filter workgroup of the
-// query has finished (kernel boundary): the short list is narrowed with two
-// LDS histogram passes (bits 20..10, 9..0 of the key) and, when a tie
-// straddles rank k, three passes over the complemented indices; the selected
-// indices are sorted ascending (bitonic, in LDS) and every word the call
-// wrote in the workspace is zeroed again.
+// query has finished (kernel boundary).  The short list holds the candidates
+// of the threshold bin (all share its top 11 key bits); the second-digit
+// histogram the filter built gives key bits 20..10 of the k-th key, one LDS
+// histogram pass over bits 9..0 of the few candidates in that bucket gives
+// the k-th key T (skipped when the whole bucket is taken), and when more
+// candidates equal T than are still needed, three passes over the
+// complemented indices keep the lowest indices.  The output order is each
+// selected index's rank among the selected (broadcast LDS reads), and every
+// word the call wrote in the workspace is zeroed again.
+constexpr int kFinalLoads = kCandCap / kThreads;
+constexpr int kSelLoads = kTopkMaxK / kThreads;
+
 __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __restrict__ n_cand,
                                                               int32_t* __restrict__ out,
                                                               uint8_t* __restrict__ ws, int S_max,
@@ -459,122 +480,174 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
     __shared__ uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
     __shared__ uint32_t ck[kCandCap], ci[kCandCap];
-    __shared__ int32_t sel[kTopkMaxK];
+    __shared__ __align__(16) int32_t sel[kTopkMaxK];
     __shared__ uint32_t nsel_lds;
-    __shared__ int cnt[2], cnt_raw[2];
+    __shared__ int cnt[3];
 
     const int q = blockIdx.x, tid = threadIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
-    const int n = clamp_n(n_cand, q, S_max);
-    const int take = min(k, n);
-    if (tid == 0) {
-        const uint32_t a = W.ctr[1], b = W.ctr[0];
-        cnt[0] = (int)min(a, (uint32_t)take);
-        cnt[1] = (int)min(b, (uint32_t)S_max);
-        cnt_raw[0] = (int)min(a, (uint32_t)k);      // entries written to sel (capacity k)
-        cnt_raw[1] = (int)min(b, (uint32_t)S_max);  // entries written to the short list
-    }
-    // the threshold bin again (the filter kernel did the same on the same histogram)
-    int t1 = -1;
-    if (take < n) {
-        for (int i = tid; i < kBins; i += kThreads) h[i] = W.hist[i];
-        __syncthreads();
-        int rem;
-        t1 = find_crossing<kBins>(h, take, tmp, &rem);
-    }
+    if (tid == 0) cnt[0] = clamp_n(n_cand, q, S_max);
+    if (tid == 1) cnt[1] = (int)W.ctr[1];
+    if (tid == 2) cnt[2] = (int)W.ctr[0];
     __syncthreads();
-    const int nsel0 = cnt[0];
-    const int nc = cnt[1];
-    for (int i = tid; i < nsel0; i += kThreads) sel[i] = W.sel[i];
+    const int n = cnt[0];
+    const int take = min(k, n);
+    const int sel_raw = min(cnt[1], k), nsel0 = min(cnt[1], take);
+    const int nc = min(cnt[2], S_max);
+    const bool small = nc <= kCandCap;
+    int need = take - nsel0;
+    const bool refine = need > 0 && nc > 0;  // uniform
+
+    // every load in flight at once: selected list, short list, second-digit histogram
+    int32_t sv[kSelLoads];
+    uint32_t kv[kFinalLoads], iv[kFinalLoads], hv[kBins / kThreads];
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j) {
+        const int i = tid + j * kThreads;
+        sv[j] = i < nsel0 ? W.sel[i] : 0;
+    }
+    if (small) {
+#pragma unroll
+        for (int j = 0; j < kFinalLoads; ++j) {
+            const int i = tid + j * kThreads;
+            kv[j] = i < nc ? W.cand_key[i] : 0u;
+            iv[j] = i < nc ? W.cand_idx[i] : 0u;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kBins / kThreads; ++j) hv[j] = refine ? W.hist2[tid + j * kThreads] : 0u;
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < nsel0) sel[i] = sv[j];
+    }
+    if (small) {
+#pragma unroll
+        for (int j = 0; j < kFinalLoads; ++j) {
+            const int i = tid + j * kThreads;
+            if (i < nc) { ck[i] = kv[j]; ci[i] = iv[j]; }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kBins / kThreads; ++j) h[tid + j * kThreads] = hv[j];
     if (tid == 0) nsel_lds = (uint32_t)nsel0;
     __syncthreads();
-    int need = take - nsel0;
-    if (need > 0 && nc > 0) {
-        const uint32_t* key = W.cand_key;
-        const uint32_t* idx = W.cand_idx;
-        if (nc <= kCandCap) {
-            for (int i = tid; i < nc; i += kThreads) {
-                ck[i] = W.cand_key[i];
-                ci[i] = W.cand_idx[i];
-            }
-            __syncthreads();
-            key = ck;
-            idx = ci;
-        }
-        const uint32_t p1 = (uint32_t)t1 << 21;
+
+    if (refine) {
+        const uint32_t* key = small ? ck : W.cand_key;
+        const uint32_t* idx = small ? ci : W.cand_idx;
+        const uint32_t p1 = key[0] & 0xffe00000u;  // the threshold bin's 11 bits
         int rem;
-        const int d2 = radix_digit<kBins>(key, nc, 0xffe00000u, p1, 10, nullptr, 0u, need, h, tmp, &rem);
-        need = rem;
+        const int d2 = find_crossing<kBins>(h, need, tmp, &rem);
         const uint32_t p2 = p1 | ((uint32_t)d2 << 10);
-        const int d3 = radix_digit<1024>(key, nc, 0xfffffc00u, p2, 0, nullptr, 0u, need, h, tmp, &rem);
+        // the whole bucket is taken: no tie to break (read by all before h is reused)
+        const bool whole = (int)h[d2] == rem;
+        __syncthreads();
         need = rem;
-        const uint32_t T = p2 | (uint32_t)d3;
-        // how many candidates equal T?
-        uint32_t eq = 0;
-        for (int i = tid; i < nc; i += kThreads) eq += key[i] == T;
-        uint32_t eq_all;
-        block_excl_scan<kThreads>(eq, tmp, &eq_all);
-        // the need lowest indices among the T-valued: select on ~idx
-        uint32_t imax = 0xffffffffu;  // take every T-valued candidate
-        if ((int)eq_all > need) {
-            // digits of ~idx, highest first, among the T-valued candidates
-            int r = need;
-            uint32_t pr = 0, pm = 0;
-            const int shifts[3] = {21, 10, 0};
-            const int widths[3] = {11, 11, 10};
-            for (int pass = 0; pass < 3; ++pass) {
-                const int nb = 1 << widths[pass];
-                for (int i = tid; i < kBins; i += kThreads) h[i] = 0;
-                __syncthreads();
-                for (int i = tid; i < nc; i += kThreads) {
-                    if (key[i] != T) continue;
-                    const uint32_t ni = ~idx[i];
-                    if ((ni & pm) == pr) atomicAdd(&h[(ni >> shifts[pass]) & (nb - 1)], 1u);
+        uint32_t T = p2, imax = 0xffffffffu;
+        if (!whole) {
+            const int d3 = radix_digit<1024>(key, nc, 0xfffffc00u, p2, 0, nullptr, 0u, need, h, tmp, &rem);
+            need = rem;
+            T = p2 | (uint32_t)d3;
+            uint32_t eq = 0;
+            for (int i = tid; i < nc; i += kThreads) eq += key[i] == T;
+            uint32_t eq_all;
+            block_excl_scan<kThreads>(eq, tmp, &eq_all);
+            if ((int)eq_all > need) {
+                // the need lowest indices among the T-valued: digits of ~idx, highest first
+                int r = need;
+                uint32_t pr = 0, pm = 0;
+                const int shifts[3] = {21, 10, 0};
+                const int widths[3] = {11, 11, 10};
+                for (int pass = 0; pass < 3; ++pass) {
+                    const int nb = 1 << widths[pass];
+                    for (int i = tid; i < kBins; i += kThreads) h[i] = 0;
+                    __syncthreads();
+                    for (int i = tid; i < nc; i += kThreads) {
+                        if (key[i] != T) continue;
+                        const uint32_t ni = ~idx[i];
+                        if ((ni & pm) == pr) atomicAdd(&h[(ni >> shifts[pass]) & (nb - 1)], 1u);
+                    }
+                    __syncthreads();
+                    const int d = (nb == kBins) ? find_crossing<kBins>(h, r, tmp, &rem)
+                                                : find_crossing<1024>(h, r, tmp, &rem);
+                    r = rem;
+                    pr |= (uint32_t)d << shifts[pass];
+                    pm |= (uint32_t)(nb - 1) << shifts[pass];
                 }
-                __syncthreads();
-                const int d = (nb == kBins) ? find_crossing<kBins>(h, r, tmp, &rem)
-                                            : find_crossing<1024>(h, r, tmp, &rem);
-                r = rem;
-                pr |= (uint32_t)d << shifts[pass];
-                pm |= (uint32_t)(nb - 1) << shifts[pass];
+                imax = ~pr;  // indices <= imax among the T-valued are taken
             }
-            imax = ~pr;  // indices <= imax among the T-valued are taken
         }
+        // whole bucket: every key >= p2 is taken; otherwise keys > T, and T-valued up to imax
         for (int i = tid; i < nc; i += kThreads) {
             const uint32_t kk = key[i];
-            if (kk > T || (kk == T && idx[i] <= imax)) {
+            const bool take_it = whole ? (kk >= p2) : (kk > T || (kk == T && idx[i] <= imax));
+            if (take_it) {
                 const uint32_t pos = atomicAdd(&nsel_lds, 1u);
                 if (pos < (uint32_t)take) sel[pos] = (int32_t)idx[i];
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
-    // bitonic sort of sel[0..take) ascending (padded to a power of two)
-    int N = 1;
-    while (N < take) N <<= 1;
+    // Ascending order by a bucketed counting sort of the selected indices:
+    // bucket = index >> bshift (at most 2048 buckets over the candidate
+    // range), bucket starts by a prefix sum, and an index's place inside its
+    // bucket is the number of smaller indices in the same bucket (buckets
+    // hold a handful of entries).  Every step is parallel over the entries.
     const int filled = min((int)nsel_lds, take);
-    for (int i = filled + tid; i < N; i += kThreads) sel[i] = 0x7fffffff;
-    __syncthreads();
-    for (int size = 2; size <= N; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (N >> 1); i += kThreads) {
-                const int lo = 2 * stride * (i / stride) + (i % stride);
-                const int hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const int32_t a = sel[lo], c = sel[hi];
-                if ((a > c) == up) { sel[lo] = c; sel[hi] = a; }
+    int32_t* o = out + (size_t)q * k;
+    {
+        int bshift = 0;
+        while ((((uint32_t)S_max - 1u) >> bshift) >= (uint32_t)kBins) ++bshift;
+        uint32_t* bstart = h;                                   // [kBins]
+        uint32_t* bfill = ck;                                   // [kBins] fill counters
+        int32_t* bucketed = reinterpret_cast<int32_t*>(ci);     // [kTopkMaxK]
+        for (int i = tid; i < kBins; i += kThreads) { bstart[i] = 0; bfill[i] = 0; }
+        __syncthreads();
+        for (int i = tid; i < filled; i += kThreads) atomicAdd(&bstart[(uint32_t)sel[i] >> bshift], 1u);
+        __syncthreads();
+        {
+            // exclusive prefix over the bucket counts (8 buckets per thread)
+            constexpr int BPT = kBins / kThreads;
+            uint32_t c[BPT], sum = 0;
+#pragma unroll
+            for (int j = 0; j < BPT; ++j) { c[j] = bstart[tid * BPT + j]; sum += c[j]; }
+            uint32_t tot;
+            uint32_t base = block_excl_scan<kThreads>(sum, tmp, &tot);
+#pragma unroll
+            for (int j = 0; j < BPT; ++j) { bstart[tid * BPT + j] = base; base += c[j]; }
+        }
+        __syncthreads();
+        int32_t mine[kSelLoads];
+        uint32_t slot[kSelLoads];
+#pragma unroll
+        for (int j = 0; j < kSelLoads; ++j) {
+            const int i = tid + j * kThreads;
+            mine[j] = i < filled ? sel[i] : 0;
+            if (i < filled) {
+                const uint32_t bk = (uint32_t)mine[j] >> bshift;
+                slot[j] = bstart[bk] + atomicAdd(&bfill[bk], 1u);
+                bucketed[slot[j]] = mine[j];
             }
-            __syncthreads();
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSelLoads; ++j) {
+            const int i = tid + j * kThreads;
+            if (i < filled) {
+                const uint32_t bk = (uint32_t)mine[j] >> bshift;
+                const uint32_t b0 = bstart[bk], b1 = b0 + bfill[bk];
+                uint32_t rank = b0;
+                for (uint32_t e = b0; e < b1; ++e) rank += bucketed[e] < mine[j];
+                o[rank] = mine[j];
+            }
         }
     }
-    int32_t* o = out + (size_t)q * k;
-    for (int i = tid; i < k; i += kThreads) o[i] = (i < filled) ? sel[i] : -1;
-    // Leave every word this call wrote for this query zeroed again (histogram,
-    // counters, short list, selected list), so the whole workspace is zero
-    // whatever layout the next call uses.
-    for (int i = tid; i < kBins; i += kThreads) W.hist[i] = 0;
-    for (int i = tid; i < cnt_raw[1]; i += kThreads) { W.cand_key[i] = 0; W.cand_idx[i] = 0; }
-    for (int i = tid; i < cnt_raw[0]; i += kThreads) W.sel[i] = 0;
+    for (int i = filled + tid; i < k; i += kThreads) o[i] = -1;
+    // Leave every word this call wrote for this query zeroed again.
+    for (int i = tid; i < kBins; i += kThreads) { W.hist[i] = 0; W.hist2[i] = 0; }
+    for (int i = tid; i < nc; i += kThreads) { W.cand_key[i] = 0; W.cand_idx[i] = 0; }
+    for (int i = tid; i < sel_raw; i += kThreads) W.sel[i] = 0;
     if (tid < 16) W.ctr[tid] = 0;
 }
 
