@@ -43,7 +43,7 @@ constexpr int kNW = kThreads / kWave;
 constexpr int kBins = 2048;         // first digit: key bits 31..21
 constexpr int kFilterChunk = 4096;  // scores per filter workgroup
 constexpr int kCandCap = 4096;      // short-list entries the final select keeps in LDS
-constexpr int kScoreRowsMulti = 1024;
+constexpr int kScoreRowsMulti = 2048;
 
 // ---- workspace (multi-workgroup path), per query -------------------------
 //   hist[2048] u32 (key bits 31..21 of every candidate) | hist2[2048] u32
@@ -136,49 +136,56 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     constexpr int DI = LPR * V;            // indexer width
     constexpr int RPL = kWave / LPR;       // rows covered by one wave-wide load
     constexpr int U = 8;                   // loads per lane per batch
-    constexpr int RPB = RPL * U;           // rows per wave batch
+    constexpr int RPU = RPL * kNW;         // rows covered by one workgroup-wide load
+    constexpr int RPB = RPU * U;           // rows per workgroup batch
     constexpr int NG = kThreads / LPR;     // partial head sums per channel
     constexpr int LB = (LPR == 8) ? 3 : (LPR == 16 ? 4 : 5);
     __shared__ float qpart[NG][DI];
     __shared__ float qsum[DI];
     __shared__ uint32_t hist[HIST ? kBins : 1];
+    extern __shared__ __align__(16) float stage[];  // this workgroup's scores (rows_per_wg)
 
     const int q = blockIdx.y;
-    const int bseq = q_seq ? q_seq[q] : q;
-    int n = clamp_n(n_cand, q, S_max);
-    if (bseq < 0 || bseq >= B) n = 0;
-    const int r0 = blockIdx.x * rows_per_wg;
-    const int r1 = min(n, r0 + rows_per_wg);
-    if (r0 >= r1) return;  // uniform over the workgroup
-
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int sub = lane % LPR, rs = lane / LPR;
+    const int bseq_raw = q_seq ? q_seq[q] : q;
+    const int bseq = (bseq_raw < 0 || bseq_raw >= B) ? 0 : bseq_raw;
     const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)sub * V;
-    const int nb = ceil_div(r1 - r0, RPB);  // wave batches of this workgroup
+    const int r0 = blockIdx.x * rows_per_wg;
+    const int r1m = min(S_max, r0 + rows_per_wg);  // rows that are valid memory
 
     // Key rows are read once: nontemporal loads keep them from displacing
-    // reusable lines in the caches.  Full batches need no row clamp.
-    auto load_batch = [&](u32x4 (&buf)[U], int bi) {
+    // reusable lines.  Load u of batch bi: the 256 lanes read RPU consecutive
+    // rows (4 KB), wave w the w-th quarter.  Full batches need no clamp.
+    auto load_batch = [&](u32x4 (&buf)[U], int bi, int rlim) {
         const int rb = r0 + bi * RPB;
-        if (rb + RPB <= r1) {
-            const T* p = kbase + (size_t)(rb + rs) * DI;
+        if (rb + RPB <= rlim) {
+            const T* p = kbase + (size_t)(rb + w * RPL + rs) * DI;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (size_t)u * RPL * DI));
+                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (size_t)u * RPU * DI));
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int r = rb + u * RPL + rs;
-                const int rc = r < r1 ? r : r1 - 1;  // stay inside this query's rows
+                const int r = rb + u * RPU + w * RPL + rs;
+                const int rc = r < rlim ? r : rlim - 1;  // stay inside the valid rows
                 buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)rc * DI));
             }
         }
     };
 
-    // first batch in flight before the head fold
+    // first batch in flight before the candidate count and the head fold are known
     u32x4 cur[U];
-    int bi = w;
-    if (bi < nb) load_batch(cur, bi);
+    load_batch(cur, 0, r1m);
+
+    int n = clamp_n(n_cand, q, S_max);
+    if (bseq_raw < 0 || bseq_raw >= B) n = 0;
+    const int r1 = min(n, r0 + rows_per_wg);
+    if (r0 >= r1) {  // uniform over the workgroup: no candidate rows here
+        __builtin_amdgcn_s_waitcnt(0);  // retire the speculative loads first
+        return;
+    }
+    const int nb = ceil_div(r1 - r0, RPB);
 
     // fold the heads: thread t sums the chunks t, t+256, ... of q_idx[q] (all
     // loads issued together), then the NG partials of each channel are added
@@ -221,14 +228,12 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     float qv[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) qv[e] = qsum[sub * V + e];
-    float* srow = scores + (size_t)q * S_max;
     const bool writer = (sub & ((1 << (LB - 3)) - 1)) == 0;
     const int my_u = sub >> (LB - 3);
 
-    for (; bi < nb; bi += kNW) {
+    for (int bi = 0; bi < nb; ++bi) {
         u32x4 nxt[U];
-        const int bn = bi + kNW;
-        if (bn < nb) load_batch(nxt, bn);  // next batch in flight while this one is reduced
+        if (bi + 1 < nb) load_batch(nxt, bi + 1, r1);  // next batch in flight while this one is reduced
         float d[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -240,16 +245,27 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
             d[u] = acc;
         }
         const float sc = reduce_scatter8<LPR>(d, sub);
-        const int r = r0 + bi * RPB + my_u * RPL + rs;
+        const int r = r0 + bi * RPB + my_u * RPU + w * RPL + rs;
         if (writer && r < r1) {
-            __builtin_nontemporal_store(sc, srow + r);
+            stage[r - r0] = sc;
             if constexpr (HIST) atomicAdd(&hist[score_key(sc) >> 21], 1u);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
+    __syncthreads();
+    // the workgroup's scores leave in one coalesced burst
+    float* srow = scores + (size_t)q * S_max + r0;
+    const int nr = r1 - r0;
+    for (int i = tid * 4; i < nr; i += kThreads * 4) {
+        if (i + 4 <= nr && (((uintptr_t)(srow + i)) & 15u) == 0) {
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage + i),
+                                        reinterpret_cast<f32x4*>(srow + i));
+        } else {
+            for (int j = i; j < min(nr, i + 4); ++j) srow[j] = stage[j];
+        }
+    }
     if constexpr (HIST) {
-        __syncthreads();
         QWs W = ws_of(ws, q, S_max, k);
         for (int i = tid; i < kBins; i += kThreads) {
             const uint32_t c = hist[i];
@@ -657,13 +673,14 @@ hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32
                         int S_max, int k, bool hist, hipStream_t st) {
     const int rows = hist ? kScoreRowsMulti : min(S_max, 8192);
     dim3 grid((unsigned)ceil_div(S_max, rows), (unsigned)Nq);
+    const size_t lds = (size_t)rows * sizeof(float);  // staged scores
     ProfScope prof(kProfScore, st);
     if (hist)
-        hipLaunchKernelGGL((score_kernel<T, LPR, true>), grid, dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((score_kernel<T, LPR, true>), grid, dim3(kThreads), lds, st,
                            (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
                            S_max, k, rows);
     else
-        hipLaunchKernelGGL((score_kernel<T, LPR, false>), grid, dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((score_kernel<T, LPR, false>), grid, dim3(kThreads), lds, st,
                            (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
                            S_max, k, rows);
     return hipGetLastError();
