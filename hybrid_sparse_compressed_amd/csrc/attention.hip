@@ -57,6 +57,12 @@ template <> struct Mma<float> {
     }
 };
 
+// Position of tile row r inside a transposed V row: the 8 rows that lane
+// group q contracts in one bf16 MFMA step (4q..4q+3 and 16+4q..16+4q+3, the
+// rows its S^T registers hold) become contiguous, as do the 4 rows of one fp32
+// step (16*mt + 4q .. +3 at 8q + 4mt).
+__device__ __forceinline__ int vt_pos(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
+
 // Element x of a 16-byte chunk, and a store of the x-th elements of two rows
 // (consecutive in the transposed tile) as one 2-element write.
 template <typename T> struct Pair;
@@ -93,7 +99,7 @@ struct AttnArgs {
 template <typename T, int DQK, int DV> struct TileLds {
     static constexpr int kPadK = 16 / (int)sizeof(T);   // one 16-byte pad per K row
     static constexpr int kStrideK = DQK + kPadK;
-    static constexpr int kPadV = 4;  // transposed rows stay 8-byte (bf16) / 16-byte (fp32) aligned
+    static constexpr int kPadV = 8;  // transposed rows stay 16-byte aligned
     static constexpr int kStrideV = kTile + kPadV;
     static constexpr size_t kBytes = (size_t)kTile * kStrideK * sizeof(T) +
                                      (size_t)DV * kStrideV * sizeof(T);
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
                 if (ch * V16 < DV) {
 #pragma unroll
                     for (int x = 0; x < V16; ++x)
-                        Pair<T>::put(Vt + (size_t)(ch * V16 + x) * L::kStrideV + 2 * rp, ga[it], gb[it], x);
+                        Pair<T>::put(Vt + (size_t)(ch * V16 + x) * L::kStrideV + vt_pos(2 * rp), ga[it], gb[it], x);
                 }
             }
         }
@@ -337,9 +343,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int t = 0; t < NMT; ++t) {
                 const T* vrow = Vt + (size_t)(t * 16 + hl) * L::kStrideV;
-                uint2 lo = *reinterpret_cast<const uint2*>(vrow + quad * 4);
-                uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + quad * 4);
-                u32x4 vv = u32x4{lo.x, lo.y, hi.x, hi.y};
+                const u32x4 vv = *reinterpret_cast<const u32x4*>(vrow + quad * 8);
                 acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv), pf, acc[t]);
             }
         } else {
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
                 const float* vrow = reinterpret_cast<const float*>(Vt) + (size_t)(t * 16 + hl) * L::kStrideV;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    const f32x4 vv = *reinterpret_cast<const f32x4*>(vrow + mt * 16 + quad * 4);
+                    const f32x4 vv = *reinterpret_cast<const f32x4*>(vrow + quad * 8 + mt * 4);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[t] = M::mma(vv[r], p[mt * 4 + r], acc[t]);
                 }
@@ -397,6 +401,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
                                                          float* __restrict__ lse, int H,
                                                          int n_split) {
     constexpr int kBatch = 32;  // split partials loaded per round
+    auto load4 = [](const float* p) -> f32x4 { return *reinterpret_cast<const f32x4*>(p); };
     __shared__ float wsp[kMaxSplit], lsp[kMaxSplit];
     __shared__ float stat[2];
     const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
@@ -408,8 +413,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
     f32x4 pv[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
-        pv[j] = (has_d && j < n_split) ? *reinterpret_cast<const f32x4*>(p0 + j * sstride + d)
-                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+        pv[j] = (has_d && j < n_split) ? load4(p0 + j * sstride + d) : f32x4{0.f, 0.f, 0.f, 0.f};
     float ms = -INFINITY, ls = 0.f;
     if (tid < n_split) {
         const float2 v = *reinterpret_cast<const float2*>(part_ml + (((size_t)b * n_split + tid) * H + h) * 2);
@@ -444,8 +448,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 const int s = s0 + j;
-                pv[j] = (has_d && s < n_split) ? *reinterpret_cast<const f32x4*>(p0 + s * sstride + d)
-                                               : f32x4{0.f, 0.f, 0.f, 0.f};
+                pv[j] = (has_d && s < n_split) ? load4(p0 + s * sstride + d) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
