@@ -6,20 +6,22 @@
 // or C128 (dense).  One softmax runs over the union of the window rows and
 // the compressed rows; the value of a latent row is its first d_v channels.
 //
-// Layout of the work.  A workgroup (4 waves) owns up to 64 query heads, 16
-// per wave, and a range of "virtual rows": rows 0..W-1 are the window (ring
-// slots for decode, causal tokens for prefill), rows W.. are the compressed
-// candidates (the index list in sparse mode, 0..len-1 in dense mode).
-// Rows are processed in tiles of 32:
-//   1. gather: the 32 latent rows are copied into LDS with 16-byte loads,
+// Layout of the work.  A workgroup (4 waves) owns 16 query heads (one MFMA
+// column block) and a range of "virtual rows": rows 0..W-1 are the window
+// (ring slots for decode, causal tokens for prefill), rows W.. are the
+// compressed candidates (the index list in sparse mode, 0..len-1 in dense
+// mode).  Rows are processed in tiles of 64:
+//   1. gather: the 64 latent rows are copied into LDS with 16-byte loads,
 //      row-major for the QK product and transposed (first d_v channels) for
 //      the PV product; rows that are not valid are zero-filled and masked;
-//   2. S^T = K_tile * Q^T on MFMA 16x16 tiles (rows on M, heads on N), so a
-//      lane owns one head and 8 rows of the tile;
-//   3. online softmax per head in base 2 (running max and sum per lane);
-//   4. O^T += V^T * P^T on MFMA, P^T taken straight from the S^T registers
-//      (the row order inside the contraction is permuted identically in both
-//      operands, which leaves the sum unchanged), accumulating O^T in fp32.
+//   2. S^T = K_tile * Q^T on MFMA 16x16 tiles: wave w takes rows
+//      16w..16w+15 (rows on M, heads on N), so a lane owns one head and 4
+//      rows;
+//   3. online softmax per head in base 2: each wave reduces its 16 rows, the
+//      four (max, sum) pairs meet in LDS and every wave derives the same
+//      running statistics; P^T goes to LDS in bf16 (fp32 for fp32 inputs);
+//   4. O^T += V^T * P^T on MFMA over the 64 rows, wave w owning value
+//      channels [w*d_v/4, (w+1)*d_v/4), accumulating O^T in fp32.
 // Decode splits the rows of a sequence over several workgroups and merges
 // their (max, sum, O) partials in a second kernel, in a fixed order; prefill
 // gives each query position its own workgroup.
@@ -31,10 +33,10 @@ namespace hsa {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kHeadsPerWave = 16;
-constexpr int kHeadsPerWG = 64;
-constexpr int kTile = 32;
-constexpr int kChunkRows = 256;  // rows whose list is built at once (one per thread)
+constexpr int kNW = kAttnThreads / kWave;  // waves per workgroup
+constexpr int kHeadsPerWG = 16;
+constexpr int kTile = 16 * kNW;            // rows per tile: 16 per wave in the QK product
+constexpr int kChunkRows = 256;            // rows whose list is built at once (one per thread)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -56,12 +58,6 @@ template <> struct Mma<float> {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
 };
-
-// Position of tile row r inside a transposed V row: the 8 rows that lane
-// group q contracts in one bf16 MFMA step (4q..4q+3 and 16+4q..16+4q+3, the
-// rows its S^T registers hold) become contiguous, as do the 4 rows of one fp32
-// step (16*mt + 4q .. +3 at 8q + 4mt).
-__device__ __forceinline__ int vt_pos(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
 
 // Element x of a 16-byte chunk, and a store of the x-th elements of two rows
 // (consecutive in the transposed tile) as one 2-element write.
@@ -95,15 +91,24 @@ struct AttnArgs {
     float scale_log2;     // scale * log2(e)
 };
 
-// LDS footprint of one tile, in elements of T
+// LDS footprint of one tile, in elements of T: K row-major, V^T (one row per
+// value channel), P^T (one row per head).  Every row carries a 16-byte skew
+// so that the 16 rows one MFMA operand reads fall on distinct banks.
 template <typename T, int DQK, int DV> struct TileLds {
-    static constexpr int kPadK = 16 / (int)sizeof(T);   // one 16-byte pad per K row
-    static constexpr int kStrideK = DQK + kPadK;
-    static constexpr int kPadV = 8;  // transposed rows stay 16-byte aligned
-    static constexpr int kStrideV = kTile + kPadV;
-    static constexpr size_t kBytes = (size_t)kTile * kStrideK * sizeof(T) +
-                                     (size_t)DV * kStrideV * sizeof(T);
+    static constexpr int kSkew = 16 / (int)sizeof(T);
+    static constexpr int kStrideK = DQK + kSkew;
+    static constexpr int kStrideT = kTile + kSkew;   // V^T and P^T rows
+    static constexpr size_t kOffV = (size_t)kTile * kStrideK;
+    static constexpr size_t kOffP = kOffV + (size_t)DV * kStrideT;
+    static constexpr size_t kBytes = (kOffP + (size_t)kHeadsPerWG * kStrideT) * sizeof(T);
 };
+
+// Rows of the PV contraction.  bf16: step ks takes tile rows 32*ks..32*ks+31,
+// lane group q the 8 rows 32*ks + 8*q + j.  fp32: step ks takes 4 rows, lane
+// group q row 16*q + ks, so a lane's rows over the 16 steps are contiguous.
+// V^T and P^T are both stored in natural row order, which these maps read
+// with 16-byte loads.
+static_assert(kTile == 64, "the fp32 PV map assumes 16 steps of 4 rows");
 
 template <typename T, int DQK, int DV, bool PREFILL>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
@@ -112,20 +117,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     constexpr int V16 = Elem<T>::kPer16B;          // elements per 16-byte chunk
     constexpr int CPR = DQK / V16;                 // 16-byte chunks per row
     constexpr int NKK = DQK / M::kK;               // MFMA steps of the QK product
-    constexpr int NMT = DV / 16;                   // O^T row tiles
-    static_assert(DQK % M::kK == 0 && DV % 16 == 0 && DV <= DQK && DV <= 512, "unsupported head dims");
+    constexpr int DW = DV / kNW;                   // value channels per wave
+    constexpr int NMT = DW / 16;                   // O^T row tiles per wave
+    static_assert(DQK % M::kK == 0 && DV % (16 * kNW) == 0 && DV <= DQK && DV <= 512,
+                  "unsupported head dims");
+    static_assert(kChunkRows % kTile == 0 && kChunkRows == kAttnThreads, "row list layout");
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
     T* Ks = reinterpret_cast<T*>(lds_raw);
-    T* Vt = Ks + (size_t)kTile * L::kStrideK;
+    T* Vt = Ks + L::kOffV;
+    T* Pt = Ks + L::kOffP;
     __shared__ long long row_off[kChunkRows];  // element offset of the row in its source, -1 invalid
     __shared__ int row_src[kChunkRows];        // 0: window source, 1: compressed pool
     __shared__ int tile_any[kChunkRows / kTile];
+    __shared__ float red_m[kNW][kHeadsPerWG], red_s[kNW][kHeadsPerWG];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int hl = lane & 15, quad = lane >> 4;
     const int hb = blockIdx.z;
-    const int head = hb * kHeadsPerWG + wave * kHeadsPerWave + hl;
+    const int head = hb * kHeadsPerWG + hl;
     const bool head_ok = head < a.H;
 
     // sequence / query identity and row range
@@ -190,7 +200,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     int first_src;
     row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
 
-    // Q fragments for this lane's head: k-slots of lane group `quad`
+    // Q fragments for this lane's head: k-slots of lane group `quad` (every
+    // wave holds the same 16 heads)
     typename M::frag qf[NKK];
     {
         const T* qrow;
@@ -265,18 +276,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
                 if (ch * V16 < DV) {
 #pragma unroll
                     for (int x = 0; x < V16; ++x)
-                        Pair<T>::put(Vt + (size_t)(ch * V16 + x) * L::kStrideV + vt_pos(2 * rp), ga[it], gb[it], x);
+                        Pair<T>::put(Vt + (size_t)(ch * V16 + x) * L::kStrideT + 2 * rp, ga[it], gb[it], x);
                 }
             }
         }
         __syncthreads();
 
-        // ---- S^T tile: rows 16*mt + 4*quad + r, head `hl`
-        f32x4 s[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-            const T* krow = Ks + (size_t)(mt * 16 + hl) * L::kStrideK;
+        // ---- S^T for this wave's rows 16*wave + 4*quad + r, head `hl`; two
+        // accumulation chains (even / odd steps) halve the dependent latency
+        f32x4 s;
+        {
+            f32x4 c0v = f32x4{0.f, 0.f, 0.f, 0.f}, c1v = f32x4{0.f, 0.f, 0.f, 0.f};
+            const T* krow = Ks + (size_t)(wave * 16 + hl) * L::kStrideK;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 typename M::frag af;
@@ -286,77 +297,100 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
                 } else {
                     af = reinterpret_cast<const float*>(krow)[kk * M::kK + quad];
                 }
-                c = M::mma(af, qf[kk], c);
+                if (kk & 1)
+                    c1v = M::mma(af, qf[kk], c1v);
+                else
+                    c0v = M::mma(af, qf[kk], c0v);
             }
-            s[mt] = c;
+            s = c0v + c1v;
         }
 
-        // ---- online softmax (base 2); masked rows -> -inf
-        float x[8];
-        float tmax = -INFINITY;
+        // ---- online softmax (base 2); masked rows -> -inf.  Each wave
+        // reduces its 16 rows to (max, sum relative to that max) per head.
+        float x[4];
+        float wmax = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int r = 0; r < 4; ++r) {
+            const int row = wave * 16 + quad * 4 + r;
+            const float v = row_off[tb + row] >= 0 ? s[r] * a.scale_log2 : -INFINITY;
+            x[r] = v;
+            wmax = fmaxf(wmax, v);
+        }
+        wmax = fmaxf(wmax, __shfl_xor(wmax, 16, kWave));
+        wmax = fmaxf(wmax, __shfl_xor(wmax, 32, kWave));
+        float p[4];
+        float wsum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = mt * 16 + quad * 4 + r;
-                const float v = row_off[tb + row] >= 0 ? s[mt][r] * a.scale_log2 : -INFINITY;
-                x[mt * 4 + r] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        for (int r = 0; r < 4; ++r) {
+            p[r] = wmax == -INFINITY ? 0.f : exp2f(x[r] - wmax);
+            wsum += p[r];
+        }
+        wsum += __shfl_xor(wsum, 16, kWave);
+        wsum += __shfl_xor(wsum, 32, kWave);
+        if (quad == 0) {
+            red_m[wave][hl] = wmax;
+            red_s[wave][hl] = wsum;
+        }
+        __syncthreads();
         // The reference max only moves when a logit exceeds it by more than
         // 2^8 (p stays <= 256, no overflow); the rescale of the accumulator is
         // skipped unless some lane of the wave moved a nonzero accumulator.
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) tmax = fmaxf(tmax, red_m[w][hl]);
         const bool move = tmax > m_run + 8.f;
         const float m_new = move ? tmax : m_run;
         const float alpha = move ? exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
-        float p[8];
-        float psum = 0.f;
-        if (m_new == -INFINITY) {
+        float tsum = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = 0.f;
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                p[j] = exp2f(x[j] - m_new);
-                psum += p[j];
-            }
+        for (int w = 0; w < kNW; ++w) {
+            const float mw = red_m[w][hl];
+            if (mw != -INFINITY) tsum += red_s[w][hl] * exp2f(mw - m_new);
         }
-        psum += __shfl_xor(psum, 16, kWave);
-        psum += __shfl_xor(psum, 32, kWave);
+        const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
+        // P^T rows of this wave (natural row order)
+        if constexpr (sizeof(T) == 2) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(p[0] * sc) | ((uint32_t)f32_to_bf16(p[1] * sc) << 16);
+            pk.y = (uint32_t)f32_to_bf16(p[2] * sc) | ((uint32_t)f32_to_bf16(p[3] * sc) << 16);
+            *reinterpret_cast<uint2*>(Pt + (size_t)hl * L::kStrideT + wave * 16 + quad * 4) = pk;
+        } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Pt) + (size_t)hl * L::kStrideT + wave * 16 + quad * 4) =
+                f32x4{p[0] * sc, p[1] * sc, p[2] * sc, p[3] * sc};
+        }
         if (__ballot(move && l_run > 0.f)) {
 #pragma unroll
             for (int t = 0; t < NMT; ++t) acc[t] *= alpha;
         }
-        l_run = l_run * alpha + psum;
+        l_run = l_run * alpha + tsum;
         m_run = m_new;
+        __syncthreads();
 
-        // ---- O^T += V^T * P^T
+        // ---- O^T[wave's channels] += V^T * P^T
+        const T* vbase = Vt + (size_t)(wave * DW + hl) * L::kStrideT;
+        const T* pbase = Pt + (size_t)hl * L::kStrideT;
         if constexpr (sizeof(T) == 2) {
-            // k-slot j of lane group `quad` <-> tile row (j<4 ? 4*quad+j : 16+4*quad+j-4)
-            u32x4 pb;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                pb[w] = (uint32_t)f32_to_bf16(p[2 * w]) | ((uint32_t)f32_to_bf16(p[2 * w + 1]) << 16);
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+            for (int ks = 0; ks < kTile / 32; ++ks) {
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pbase + ks * 32 + quad * 8));
 #pragma unroll
-            for (int t = 0; t < NMT; ++t) {
-                const T* vrow = Vt + (size_t)(t * 16 + hl) * L::kStrideV;
-                const u32x4 vv = *reinterpret_cast<const u32x4*>(vrow + quad * 8);
-                acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv), pf, acc[t]);
+                for (int t = 0; t < NMT; ++t) {
+                    const u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + (size_t)t * 16 * L::kStrideT + ks * 32 + quad * 8);
+                    acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv), pf, acc[t]);
+                }
             }
         } else {
-            // one instruction per (row tile mt, register r): k-slot of group
-            // `quad` <-> tile row 16*mt + 4*quad + r
+            // lane group q contracts rows 16q..16q+15 (one per step): 4 vector reads per operand
+            const float* pf = reinterpret_cast<const float*>(pbase) + quad * 16;
 #pragma unroll
-            for (int t = 0; t < NMT; ++t) {
-                const float* vrow = reinterpret_cast<const float*>(Vt) + (size_t)(t * 16 + hl) * L::kStrideV;
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 pv = *reinterpret_cast<const f32x4*>(pf + 4 * j);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const f32x4 vv = *reinterpret_cast<const f32x4*>(vrow + quad * 8 + mt * 4);
+                for (int t = 0; t < NMT; ++t) {
+                    const f32x4 vv = *reinterpret_cast<const f32x4*>(
+                        reinterpret_cast<const float*>(vbase) + (size_t)t * 16 * L::kStrideT + quad * 16 + 4 * j);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[t] = M::mma(vv[r], p[mt * 4 + r], acc[t]);
+                    for (int e = 0; e < 4; ++e) acc[t] = M::mma(vv[e], pv[e], acc[t]);
                 }
             }
         }
@@ -364,27 +398,53 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     }
     }
 
-    // ---- epilogue.  acc[t][r] = O^T[16*t + 4*quad + r][head]
-    if (!head_ok) return;
+    // ---- epilogue.  acc[t][r] = O^T[wave*DW + 16*t + 4*quad + r][head]
     if constexpr (!PREFILL) {
         if (a.n_split > 1) {
-            const size_t prow = ((size_t)b * a.n_split + blockIdx.x) * a.H + head;
-            if (quad == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = float2{m_run, l_run};
-            float* pb = a.part_o + prow * DV;
+            // Split partials go out through LDS (the tile buffers are free: the
+            // tile loop ends on a barrier), so that each store instruction
+            // writes whole runs of one head's row.
+            constexpr int OS = DW + 4;                          // LDS row stride (floats)
+            constexpr int CPRW = DW / 4;                        // 16-byte chunks per row and wave
+            constexpr int NCH = kHeadsPerWG * CPRW / kWave;     // chunks per lane
+            static_assert((size_t)kNW * kHeadsPerWG * OS * sizeof(float) <= L::kBytes,
+                          "partial staging must fit in the tile buffers");
+            float* ob = reinterpret_cast<float*>(lds_raw) + (size_t)wave * kHeadsPerWG * OS;
+            const int h0 = hb * kHeadsPerWG;
+            const size_t prow0 = ((size_t)b * a.n_split + blockIdx.x) * a.H + h0;
+            if (wave == 0 && head_ok && quad == 0)
+                *reinterpret_cast<float2*>(a.part_ml + (prow0 + hl) * 2) = float2{m_run, l_run};
 #pragma unroll
             for (int t = 0; t < NMT; ++t)
-                *reinterpret_cast<f32x4*>(pb + t * 16 + quad * 4) = acc[t];
+                *reinterpret_cast<f32x4*>(ob + hl * OS + t * 16 + quad * 4) = acc[t];
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const int c = lane + j * kWave;
+                const int row = c / CPRW, col = (c % CPRW) * 4;
+                if (h0 + row < a.H)
+                    *reinterpret_cast<f32x4*>(a.part_o + (prow0 + row) * DV + wave * DW + col) =
+                        *reinterpret_cast<const f32x4*>(ob + row * OS + col);
+            }
             return;
         }
     }
+    if (!head_ok) return;
     const size_t orow = PREFILL ? ((size_t)qid * a.H + head) : ((size_t)b * a.H + head);
-    T* o = reinterpret_cast<T*>(a.out) + orow * DV;
+    T* o = reinterpret_cast<T*>(a.out) + orow * DV + wave * DW;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-    for (int t = 0; t < NMT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Elem<T>::store(o, t * 16 + quad * 4 + r, acc[t][r] * inv);
-    if (a.lse && quad == 0)
+    for (int t = 0; t < NMT; ++t) {
+        if constexpr (sizeof(T) == 2) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(acc[t][0] * inv) | ((uint32_t)f32_to_bf16(acc[t][1] * inv) << 16);
+            pk.y = (uint32_t)f32_to_bf16(acc[t][2] * inv) | ((uint32_t)f32_to_bf16(acc[t][3] * inv) << 16);
+            *reinterpret_cast<uint2*>(o + t * 16 + quad * 4) = pk;
+        } else {
+            *reinterpret_cast<f32x4*>(o + t * 16 + quad * 4) = acc[t] * inv;
+        }
+    }
+    if (a.lse && wave == 0 && quad == 0)
         a.lse[orow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
