@@ -4,10 +4,11 @@ Workload (c4_decode_1m): 4 sequences x 1,048,576 tokens, 262,144 C4 entries
 each, 64 heads over a 576-wide latent (value 512), window 128, indexer
 64 heads x 128, top-512; synthetic seeded inputs resident in HBM.
 
-One step = one decode layer-step: indexer scores over every C4 key + radix
-top-512 select (hsa_index_topk), fused SWA + selected-C4 attention with
-split-KV merge (hsa_attn_decode), and, on every 4th step, the compression of
-the 4 just-completed 4-token blocks (hsa_compress).  Two copies of the
+One step = one decode layer-step: indexer scores over every C4 key, exact
+radix top-512 select, and the SWA + selected-C4 attention with split-KV merge,
+all in one hsa_decode_sparse call (scoring, filter, attention that finishes
+the select, merge), and, on every 4th step, the compression of the 4
+just-completed 4-token blocks (hsa_compress).  Two copies of the
 indexer inputs alternate between steps so the 268 MB key stream is larger
 than the on-die cache across a pair of steps.
 
@@ -93,18 +94,16 @@ def main():
     idx = torch.empty((B, k), dtype=torch.int32, device=dev)
     out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    ws_topk = torch.zeros(max(256, hsa.lib.hsa_index_topk_workspace_size(B, S, k)),
-                          dtype=torch.uint8, device=dev)
-    ws_attn = torch.zeros(max(256, hsa.lib.hsa_attn_decode_workspace_size(B, H, d_v, W + k)),
-                          dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(256, hsa.lib.hsa_decode_sparse_workspace_size(B, H, d_v, W, S, k)),
+                     dtype=torch.uint8, device=dev)
 
     def step(i):
         qi, ki = sets[i & 1]
         if i % 4 == 3:
             hsa.hsa_compress(xb, gb, bb, 4, out=cb)
-        hsa.hsa_index_topk(qi, ki, w["n_cand"], k, scores=scores, topk_idx=idx, workspace=ws_topk)
-        hsa.hsa_attn_decode(w["q"], w["swa_kv"], w["swa_len"], w["comp_kv"], w["comp_len"],
-                            w["scale"], d_v, comp_idx=idx, out=out, lse=lse, workspace=ws_attn)
+        hsa.hsa_decode_sparse(qi, ki, w["n_cand"], k, w["q"], w["swa_kv"], w["swa_len"],
+                              w["comp_kv"], w["comp_len"], w["scale"], d_v, scores=scores,
+                              topk_idx=idx, out=out, lse=lse, workspace=ws)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

@@ -22,8 +22,8 @@ HSA_F32, HSA_BF16 = 0, 1
 EXPORTED = (
     "hsa_strerror", "hsa_version", "hsa_compress", "hsa_index_topk_workspace_size",
     "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
-    "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_profile_enable",
-    "hsa_profile_read",
+    "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
+    "hsa_decode_sparse", "hsa_profile_enable", "hsa_profile_read",
 )
 HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
 
@@ -58,6 +58,10 @@ def _load():
     lib.hsa_attn_decode.argtypes = [I, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                     F, P, SZ, P]
     lib.hsa_attn_decode.restype = I
+    lib.hsa_decode_sparse_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.hsa_decode_sparse_workspace_size.restype = SZ
+    lib.hsa_decode_sparse.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, P] + [I32] * 9 + [F, P, SZ, P]
+    lib.hsa_decode_sparse.restype = I
     lib.hsa_attn_prefill_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.hsa_attn_prefill_workspace_size.restype = SZ
     lib.hsa_attn_prefill.argtypes = [I, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
@@ -216,6 +220,44 @@ def hsa_attn_decode(q, swa_kv, swa_len, comp_kv, comp_len, scale, d_v, comp_idx=
         _ptr(comp_len), _ptr(out), _ptr(lse), B, H, d_qk, d_v, W, S_max, k, float(scale),
         _ptr(workspace), wsz, _stream(st)))
     return out, lse
+
+
+def hsa_decode_sparse(q_idx, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp_len, scale, d_v,
+                      scores=None, topk_idx=None, out=None, lse=None, workspace=None, stream=None):
+    """The C4 decode layer-step in one call (query b reads sequence b): indexer
+    scores, exact top-k, and the SWA + selected-row attention.
+
+    q_idx: [B, H_I, d_I]; k_idx: [B, S_max, d_I]; q: [B, H, d_qk]; swa_kv: [B, W, d_qk];
+    comp_kv: [B, S_max, d_qk].  Returns (scores, topk_idx, out, lse)."""
+    B, H_I, d_I = q_idx.shape
+    _, S_max, _ = k_idx.shape
+    _, H, d_qk = q.shape
+    W = swa_kv.shape[1]
+    if comp_kv.shape[1] != S_max or k_idx.dtype != q_idx.dtype or q.dtype != q_idx.dtype:
+        raise ValueError("hsa_decode_sparse: shape or dtype mismatch")
+    dev = q.device
+    n_cand, swa_len, comp_len = _i32(n_cand, dev), _i32(swa_len, dev), _i32(comp_len, dev)
+    if scores is None:
+        scores = torch.empty((B, S_max), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream() if stream is None else stream
+    need = lib.hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k)
+    if workspace is None:
+        # the select part sits at the front and must be zero-filled, so a
+        # cached buffer serves one layout only
+        workspace = Workspace.get("decode_sparse:%d:%d:%d:%d:%d" % (B, H, d_v, W, S_max * 4096 + k),
+                                  need, dev, st)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hsa_decode_sparse", lib.hsa_decode_sparse(
+        _dt(q), _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
+        _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
+        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)))
+    return scores, topk_idx, out, lse
 
 
 def hsa_attn_prefill(q, kv, comp_kv, q_start, W, m, scale, d_v, comp_idx=None, out=None,

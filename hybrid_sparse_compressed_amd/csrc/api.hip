@@ -62,6 +62,7 @@ int hsa_index_topk(int dtype, const void* q_idx, const void* k_idx, int32_t B,
         if (flags != 0) return HSA_ERR_INVALID_ARG;
         if (!n_cand || !scores || !topk_idx) return HSA_ERR_INVALID_ARG;
         if (Nq < 1 || S_max < 1 || k < 1 || k > hsa::kTopkMaxK) return HSA_ERR_INVALID_ARG;
+        if (S_max > hsa::kTopkMaxSegments * 4096) return HSA_ERR_UNSUPPORTED;
         if (q_idx) {
             if (!dtype_ok(dtype) || !k_idx || B < 1 || H_I < 1 || d_I < 1) return HSA_ERR_INVALID_ARG;
             if (!aligned16(q_idx) || !aligned16(k_idx)) return HSA_ERR_INVALID_ARG;
@@ -107,6 +108,61 @@ int hsa_attn_decode(int dtype, const void* q, const void* swa_kv, const int32_t*
                                               comp_len, out, lse, B, H, d_qk, d_v, W, S_max,
                                               comp_idx ? k : 0, scale, workspace,
                                               as_stream(stream)));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t hsa_decode_sparse_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t W,
+                                        int32_t S_max, int32_t k) {
+    if (B < 1 || H < 1 || d_v < 1 || W < 1 || S_max < 1 || k < 1) return 0;
+    return round256(hsa::topk_workspace_bytes(B, S_max, k)) + hsa::decode_workspace_bytes(B, H, d_v, W + k);
+}
+
+int hsa_decode_sparse(int dtype, const void* q_idx, const void* k_idx, const int32_t* n_cand,
+                      float* scores, int32_t* topk_idx, const void* q, const void* swa_kv,
+                      const int32_t* swa_len, const void* comp_kv, const int32_t* comp_len,
+                      void* out, float* lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
+                      int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        // indexer + select arguments (as hsa_index_topk with Nq = B, no q_seq)
+        if (!dtype_ok(dtype) || !q_idx || !k_idx || !n_cand || !scores || !topk_idx)
+            return HSA_ERR_INVALID_ARG;
+        if (B < 1 || H_I < 1 || d_I < 1 || S_max < 1 || k < 1 || k > hsa::kTopkMaxK)
+            return HSA_ERR_INVALID_ARG;
+        if (S_max > hsa::kTopkMaxSegments * 4096) return HSA_ERR_UNSUPPORTED;
+        if (!aligned16(q_idx) || !aligned16(k_idx)) return HSA_ERR_INVALID_ARG;
+        const int row_bytes = d_I * esize(dtype);
+        if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512) return HSA_ERR_UNSUPPORTED;
+        // attention arguments (as hsa_attn_decode, sparse mode)
+        if (!q || !swa_kv || !swa_len || !comp_kv || !comp_len || !out) return HSA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(swa_kv) || !aligned16(out) || !aligned16(comp_kv))
+            return HSA_ERR_INVALID_ARG;
+        if (H < 1 || H > 1024 || d_qk < 1 || d_v < 1 || d_v > d_qk || W < 1) return HSA_ERR_INVALID_ARG;
+        if (!(scale == scale)) return HSA_ERR_INVALID_ARG;
+        if (!hsa::attn_shape_supported(dtype, d_qk, d_v)) return HSA_ERR_UNSUPPORTED;
+        const size_t need = hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k);
+        if (!workspace || workspace_bytes < need) return HSA_ERR_WORKSPACE;
+        hipStream_t st = as_stream(stream);
+        uint8_t* ws_sel = static_cast<uint8_t*>(workspace);
+        uint8_t* ws_attn = ws_sel + round256(hsa::topk_workspace_bytes(B, S_max, k));
+        if (S_max > hsa::kRowSelectCap && hsa::fused_decode_supported(B, H, W, k)) {
+            hipError_t e = hsa::launch_index_filter(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
+                                                    d_I, S_max, k, ws_sel, st);
+            if (e != hipSuccess) return finish(e);
+            return finish(hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len,
+                                                        n_cand, ws_sel, topk_idx, out, lse, B, H,
+                                                        d_qk, d_v, W, S_max, k, scale, ws_attn, st));
+        }
+        hipError_t e = hsa::launch_index_topk(dtype, q_idx, k_idx, B, nullptr, n_cand, scores,
+                                              topk_idx, B, H_I, d_I, S_max, k, ws_sel, st);
+        if (e != hipSuccess) return finish(e);
+        return finish(hsa::launch_attn_decode(dtype, q, swa_kv, swa_len, comp_kv, topk_idx,
+                                              comp_len, out, lse, B, H, d_qk, d_v, W, S_max, k,
+                                              scale, ws_attn, st));
     } catch (...) {
         return HSA_ERR_HIP;
     }

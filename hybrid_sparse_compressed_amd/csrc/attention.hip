@@ -25,8 +25,17 @@
 // Decode splits the rows of a sequence over several workgroups and merges
 // their (max, sum, O) partials in a second kernel, in a fixed order; prefill
 // gives each query position its own workgroup.
+//
+// Fused sparse decode (the whole C4 layer-step after the filter kernel): a
+// workgroup with compressed rows first finishes its sequence's top-k select
+// itself (select.hpp, in the LDS its tiles use later) and takes its rows from
+// the selected list followed by the chosen short-list entries, both in index
+// order, so no separate select kernel, index round trip or sort sits on the
+// attention's critical path.  One extra workgroup per sequence writes the
+// ascending top-k indices and clears the first-digit histogram.
 #include "hsa_common.hpp"
 #include "hsa_internal.hpp"
+#include "select.hpp"
 
 namespace hsa {
 
@@ -77,6 +86,9 @@ template <> struct Pair<float> {
 
 struct AttnArgs {
     const void* q;
+    uint8_t* sel_ws;      // fused decode: top-k workspace (filter output)
+    const int32_t* n_cand;
+    int32_t* topk_out;    // fused decode: [B, k] ascending top-k indices
     const void* win;      // decode: swa ring [B, W, d_qk]; prefill: token kv [n_seq, T, d_qk]
     const int32_t* swa_len;
     const void* comp;     // [n_seq, S_max, d_qk]
@@ -110,8 +122,31 @@ template <typename T, int DQK, int DV> struct TileLds {
 // with 16-byte loads.
 static_assert(kTile == 64, "the fp32 PV map assumes 16 steps of 4 rows");
 
-template <typename T, int DQK, int DV, bool PREFILL>
+constexpr int kModeDecode = 0, kModePrefill = 1, kModeFused = 2;
+
+// LDS the select prologue of the fused mode carves out of the tile buffers
+constexpr size_t kSelLdsBytes = (size_t)sel::kBins * 4 + (sel::kSelNW + 2) * 4 + 3 * (size_t)sel::kMaxSeg * 4 +
+                                2 * (size_t)sel::kCandCap * 4 + 2 * (size_t)kTopkMaxK * 4 + 16;
+__device__ inline sel::SelLds sel_lds_at(unsigned char* base) {
+    sel::SelLds L;
+    uint32_t* p = reinterpret_cast<uint32_t*>(base);
+    L.h = p; p += sel::kBins;
+    L.segc = p; p += sel::kMaxSeg;
+    L.sbase = p; p += sel::kMaxSeg;
+    L.lbase = p; p += sel::kMaxSeg;
+    L.ck = p; p += sel::kCandCap;
+    L.ci = p; p += sel::kCandCap;
+    L.sel = reinterpret_cast<int32_t*>(p); p += kTopkMaxK;
+    L.chs = reinterpret_cast<int32_t*>(p); p += kTopkMaxK;
+    L.misc = p; p += 4;
+    L.tmp = p;
+    return L;
+}
+
+template <typename T, int DQK, int DV, int MODE>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
+    constexpr bool PREFILL = MODE == kModePrefill;
+    constexpr bool FUSED = MODE == kModeFused;
     typedef TileLds<T, DQK, DV> L;
     typedef Mma<T> M;
     constexpr int V16 = Elem<T>::kPer16B;          // elements per 16-byte chunk
@@ -131,6 +166,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     __shared__ int row_src[kChunkRows];        // 0: window source, 1: compressed pool
     __shared__ int tile_any[kChunkRows / kTile];
     __shared__ float red_m[kNW][kHeadsPerWG], red_s[kNW][kHeadsPerWG];
+    __shared__ int32_t fidx[FUSED ? kChunkRows : 1];  // fused: this workgroup's selected indices
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int hl = lane & 15, quad = lane >> 4;
@@ -164,6 +200,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         n_comp = n_comp < 0 ? 0 : (n_comp > a.S_max ? a.S_max : n_comp);
     }
 
+    // Fused: finish the sequence's select and keep this workgroup's list
+    // positions [f_j0, f_j0 + f_jn) in fidx (the host keeps a split within
+    // one row chunk).
+    int f_j0 = 0, f_jn = 0;
+    if constexpr (FUSED) {
+        const sel::QWs Wq = sel::ws_of(a.sel_ws, b, a.S_max, a.k);
+        const sel::SelLds SL = sel_lds_at(lds_raw);
+        const int n = sel::clamp_n(a.n_cand, b, a.S_max);
+        if ((int)blockIdx.x == a.n_split) {  // the sequence's ascending top-k output
+            if (hb != 0) return;
+            const sel::SelResult R = sel::select_query(Wq, n, a.S_max, a.k, a.k, SL);
+            sel::select_write_sorted(SL, R, a.topk_out + (size_t)b * a.k, a.k);
+            // the first-digit histogram's readers (the filter) are done: clear it for
+            // the next call's scoring (the score kernel clears the second digit's)
+            for (int i = tid; i < sel::kBins; i += kAttnThreads) Wq.hist[i] = 0;
+            return;
+        }
+    }
+
     // Row list entry of virtual row vr (chunk end c1): element offset of the
     // latent row in its source (-1: not a row of this query) and the source.
     auto row_entry = [&](int vr, int c1, long long& off, int& src) {
@@ -180,7 +235,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         } else {
             const int j = vr - a.W;
             int ci = -1;
-            if (a.comp_idx) {
+            if constexpr (FUSED) {
+                const int t = j - f_j0;
+                ci = (t >= 0 && t < f_jn) ? fidx[t] : -1;
+            } else if (a.comp_idx) {
                 if (j < a.k) {
                     const long long row = PREFILL ? (long long)qid : (long long)b;
                     ci = a.comp_idx[row * a.k + j];
@@ -198,7 +256,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     // them does not wait for Q (the vector-memory counter retires in order)
     long long first_off;
     int first_src;
-    row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
+    if constexpr (!FUSED) row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
 
     // Q fragments for this lane's head: k-slots of lane group `quad` (every
     // wave holds the same 16 heads)
@@ -220,6 +278,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             }
         }
     }
+
+
+    if constexpr (FUSED) {
+        const sel::QWs Wq = sel::ws_of(a.sel_ws, b, a.S_max, a.k);
+        const sel::SelLds SL = sel_lds_at(lds_raw);
+        const int n = sel::clamp_n(a.n_cand, b, a.S_max);
+        if (vr1 > a.W) {  // uniform: this workgroup has compressed rows
+            f_j0 = max(0, vr0 - a.W);
+            const int j1 = min(a.k, vr1 - a.W);
+            const sel::SelResult R = sel::select_query(Wq, n, a.S_max, a.k, j1, SL);
+            f_jn = j1 - f_j0;
+            for (int t = tid; t < f_jn; t += kAttnThreads) {
+                const int j = f_j0 + t;
+                fidx[t] = j < R.nsel ? SL.sel[j] : (j - R.nsel < R.nch ? SL.chs[j - R.nsel] : -1);
+            }
+            __syncthreads();  // fidx published; the select LDS goes back to the tiles
+        }
+    }
+    if constexpr (FUSED) row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[NMT];
@@ -529,31 +606,32 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
     if (lse && tid == 0) lse[(size_t)b * H + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
 }
 
-template <typename T, int DQK, int DV, bool PREFILL>
+template <typename T, int DQK, int DV, int MODE>
 hipError_t launch_attn_kernel(const AttnArgs& a, dim3 grid, hipStream_t st) {
-    const size_t lds = TileLds<T, DQK, DV>::kBytes;
+    size_t lds = TileLds<T, DQK, DV>::kBytes;
+    if (MODE == kModeFused && lds < kSelLdsBytes) lds = kSelLdsBytes;
     static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&attn_kernel<T, DQK, DV, PREFILL>),
+            reinterpret_cast<const void*>(&attn_kernel<T, DQK, DV, MODE>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     ProfScope prof(kProfAttn, st);
-    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, PREFILL>), grid, dim3(kAttnThreads), lds, st, a);
+    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, MODE>), grid, dim3(kAttnThreads), lds, st, a);
     return hipGetLastError();
 }
 
-template <bool PREFILL>
+template <int MODE>
 hipError_t dispatch_attn(int dtype, int d_qk, int d_v, const AttnArgs& a, dim3 grid,
                          hipStream_t st) {
     (void)d_v;
     if (dtype == kBF16) {
-        if (d_qk == 576) return launch_attn_kernel<bf16_t, 576, 512, PREFILL>(a, grid, st);
-        return launch_attn_kernel<bf16_t, 128, 128, PREFILL>(a, grid, st);
+        if (d_qk == 576) return launch_attn_kernel<bf16_t, 576, 512, MODE>(a, grid, st);
+        return launch_attn_kernel<bf16_t, 128, 128, MODE>(a, grid, st);
     }
-    return launch_attn_kernel<float, 128, 128, PREFILL>(a, grid, st);
+    return launch_attn_kernel<float, 128, 128, MODE>(a, grid, st);
 }
 
 }  // namespace
@@ -593,6 +671,21 @@ size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows) {
     return ml_bytes(B, p.n_split, H) + (size_t)B * p.n_split * H * d_v * sizeof(float);
 }
 
+static hipError_t launch_merge(int dtype, int d_v, const AttnArgs& a, int B, int H, int n_split,
+                               int S_max, int k, hipStream_t st) {
+    dim3 mg((unsigned)H, (unsigned)B);
+    ProfScope prof(kProfMerge, st);
+    if (dtype == kBF16) {
+        if (d_v == 512)
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split);
+        else
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split);
+    } else {
+        hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
                               const int32_t* swa_len, const void* comp_kv,
                               const int32_t* comp_idx, const int32_t* comp_len, void* out,
@@ -622,19 +715,53 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
                   : nullptr;
     a.scale_log2 = scale * kLog2e;
     dim3 grid((unsigned)p.n_split, (unsigned)B, (unsigned)ceil_div(H, kHeadsPerWG));
-    hipError_t e = dispatch_attn<false>(dtype, d_qk, d_v, a, grid, st);
+    hipError_t e = dispatch_attn<kModeDecode>(dtype, d_qk, d_v, a, grid, st);
     if (e != hipSuccess || p.n_split <= 1) return e;
-    dim3 mg((unsigned)H, (unsigned)B);
-    ProfScope prof(kProfMerge, st);
-    if (dtype == kBF16) {
-        if (d_v == 512)
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512>), mg, dim3(128), 0, st, a.part_ml, a.part_o, out, lse, H, p.n_split);
-        else
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, out, lse, H, p.n_split);
-    } else {
-        hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, out, lse, H, p.n_split);
-    }
-    return hipGetLastError();
+    return launch_merge(dtype, d_v, a, B, H, p.n_split, S_max, k, st);
+}
+
+bool fused_decode_supported(int B, int H, int W, int k) {
+    const DecodePlan p = plan_decode(B, H, W + k);
+    return p.n_split >= 2 && p.rows_per_split <= kChunkRows;
+}
+
+hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv,
+                                    const int32_t* swa_len, const void* comp_kv,
+                                    const int32_t* comp_len, const int32_t* n_cand, void* sel_ws,
+                                    int32_t* topk_out, void* out, float* lse, int B, int H,
+                                    int d_qk, int d_v, int W, int S_max, int k, float scale,
+                                    void* ws, hipStream_t st) {
+    AttnArgs a = {};
+    a.q = q;
+    a.win = swa_kv;
+    a.swa_len = swa_len;
+    a.comp = comp_kv;
+    a.comp_idx = nullptr;
+    a.comp_len = comp_len;
+    a.sel_ws = static_cast<uint8_t*>(sel_ws);
+    a.n_cand = n_cand;
+    a.topk_out = topk_out;
+    a.out = out;
+    a.lse = lse;
+    a.part_ml = static_cast<float*>(ws);
+    a.H = H;
+    a.W = W;
+    a.S_max = S_max;
+    a.k = k;
+    a.m = 1;
+    const int max_rows = W + k;
+    const DecodePlan p = plan_decode(B, H, max_rows);
+    if (p.n_split < 2 || p.rows_per_split > kChunkRows) return hipErrorNotSupported;
+    a.max_rows = max_rows;
+    a.rows_per_split = p.rows_per_split;
+    a.n_split = p.n_split;
+    a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ml_bytes(B, p.n_split, H));
+    a.scale_log2 = scale * kLog2e;
+    // one more workgroup column per sequence writes the ascending top-k
+    dim3 grid((unsigned)p.n_split + 1u, (unsigned)B, (unsigned)ceil_div(H, kHeadsPerWG));
+    hipError_t e = dispatch_attn<kModeFused>(dtype, d_qk, d_v, a, grid, st);
+    if (e != hipSuccess) return e;
+    return launch_merge(dtype, d_v, a, B, H, p.n_split, S_max, k, st);
 }
 
 hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const void* comp_kv,
@@ -661,7 +788,7 @@ hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const v
     a.n_split = 1;
     a.scale_log2 = scale * kLog2e;
     dim3 grid((unsigned)n_q, (unsigned)n_seq, (unsigned)ceil_div(H, kHeadsPerWG));
-    return dispatch_attn<true>(dtype, d_qk, d_v, a, grid, st);
+    return dispatch_attn<kModePrefill>(dtype, d_qk, d_v, a, grid, st);
 }
 
 }  // namespace hsa

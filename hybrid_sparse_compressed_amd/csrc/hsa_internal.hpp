@@ -41,11 +41,17 @@ hipError_t launch_compress(int dtype, const void* x, const void* g, const void* 
 // (histogram pass fused into scoring, then a filter + final select).
 constexpr int kRowSelectCap = 12288;
 constexpr int kTopkMaxK = 2048;
+constexpr int kTopkMaxSegments = 1024;  // multi-workgroup select: S_max <= 1024 * 4096
 size_t topk_workspace_bytes(int Nq, int S_max, int k);
 hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, int B,
                              const int32_t* q_seq, const int32_t* n_cand, float* scores,
                              int32_t* topk_idx, int Nq, int H_I, int d_I, int S_max, int k,
                              void* ws, hipStream_t st);
+// Scoring (with the first-digit histogram) and the filter kernel only, for
+// S_max > kRowSelectCap: the select is finished by the fused decode attention.
+hipError_t launch_index_filter(int dtype, const void* q_idx, const void* k_idx, int B,
+                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
+                               int S_max, int k, void* ws, hipStream_t st);
 
 // ---- attention ----
 struct DecodePlan {
@@ -61,6 +67,16 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
                               const int32_t* comp_idx, const int32_t* comp_len, void* out,
                               float* lse, int B, int H, int d_qk, int d_v, int W, int S_max,
                               int k, float scale, void* ws, hipStream_t st);
+// Fused sparse decode after launch_index_filter (one query per sequence):
+// finishes the select inside the attention kernel, writes topk_out ascending,
+// and zeroes the select workspace in the merge kernel.
+bool fused_decode_supported(int B, int H, int W, int k);
+hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv,
+                                    const int32_t* swa_len, const void* comp_kv,
+                                    const int32_t* comp_len, const int32_t* n_cand, void* sel_ws,
+                                    int32_t* topk_out, void* out, float* lse, int B, int H,
+                                    int d_qk, int d_v, int W, int S_max, int k, float scale,
+                                    void* ws, hipStream_t st);
 hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const void* comp_kv,
                                const int32_t* comp_idx, void* out, float* lse, int n_seq,
                                int n_q, int q_start, int T_len, int H, int d_qk, int d_v, int W,

@@ -23,61 +23,40 @@
 //    selection in ascending index order with two workgroup prefix sums.
 //  - larger n: the scoring kernel also builds the 2048-bin histogram of the
 //    top 11 key bits per query (LDS histogram, integer atomics to global).
-//    A filter kernel then sends every candidate above the threshold bin to
-//    the "selected" list and every candidate inside it to a short list (one
-//    atomic reservation per workgroup and list).  A final kernel, one
-//    workgroup per query, finishes the select on the short list in LDS (two
-//    more histogram passes, plus passes over indices when a tie straddles
-//    rank k), sorts the result ascending and zeroes what the call wrote in
-//    the workspace.  The kernel boundaries order every hand-off, so no
-//    workgroup waits on or fences for another.
+//    A filter kernel then sends, per segment of 4096 candidates, every
+//    candidate above the threshold bin to the segment's "selected" run and
+//    every candidate inside it to its short-list run, both in index order
+//    at fixed places of the segment (no reservation atomics).  A final
+//    kernel, one workgroup per query, gathers the runs, finishes the select
+//    on the short list in LDS (two more histogram passes, plus passes over
+//    indices when a tie straddles rank k), merges the two ascending lists
+//    into the output and zeroes what the call wrote in the workspace.  The
+//    kernel boundaries order every hand-off, so no workgroup waits on or
+//    fences for another.
 #include "hsa_common.hpp"
 #include "hsa_internal.hpp"
+#include "select.hpp"
 
 namespace hsa {
 
 namespace {
 
-constexpr int kThreads = 256;
+using namespace sel;
+
+constexpr int kThreads = kSelThreads;
 constexpr int kNW = kThreads / kWave;
-constexpr int kBins = 2048;         // first digit: key bits 31..21
-constexpr int kFilterChunk = 4096;  // scores per filter workgroup
-constexpr int kCandCap = 4096;      // short-list entries the final select keeps in LDS
 constexpr int kScoreRowsMulti = 2048;
 
-// ---- workspace (multi-workgroup path), per query -------------------------
-//   hist[2048] u32 (key bits 31..21 of every candidate) | hist2[2048] u32
-//   (key bits 20..10 of the short list) | ctr[16] u32 (0: short-list size,
-//   1: selected size) | cand_key[S_max] | cand_idx[S_max] | sel[k]
-__host__ __device__ inline size_t ws_per_query(int S_max, int k) {
-    size_t b = (size_t)kBins * 8 + 64 + (size_t)S_max * 8 + (size_t)k * 4;
-    return (b + 255) & ~(size_t)255;
-}
-
-struct QWs {
-    uint32_t* hist;
-    uint32_t* hist2;
-    uint32_t* ctr;
-    uint32_t* cand_key;
-    uint32_t* cand_idx;
-    int32_t* sel;
-};
-
-__device__ inline QWs ws_of(uint8_t* ws, int q, int S_max, int k) {
-    uint8_t* base = ws + (size_t)q * ws_per_query(S_max, k);
-    QWs w;
-    w.hist = reinterpret_cast<uint32_t*>(base);
-    w.hist2 = w.hist + kBins;
-    w.ctr = w.hist2 + kBins;
-    w.cand_key = w.ctr + 16;
-    w.cand_idx = w.cand_key + S_max;
-    w.sel = reinterpret_cast<int32_t*>(w.cand_idx + S_max);
-    return w;
-}
-
-__device__ inline int clamp_n(const int32_t* n_cand, int q, int S_max) {
-    int n = n_cand[q];
-    return n < 0 ? 0 : (n > S_max ? S_max : n);
+// The second-digit histogram of a query is built by the filter kernel of the
+// same call; the workgroups of the kernel before it (scoring, or the
+// select-only histogram) clear it, each its slice, so no later kernel has to.
+__device__ inline void clear_hist2_slice(uint8_t* ws, int q, int S_max, int k) {
+    const int per = ceil_div(kBins, (int)gridDim.x);
+    uint32_t* h2 = ws_of(ws, q, S_max, k).hist2;
+    for (int j = (int)threadIdx.x; j < per; j += (int)blockDim.x) {
+        const int i = (int)blockIdx.x * per + j;
+        if (i < kBins) h2[i] = 0;
+    }
 }
 
 // ---- scoring ---------------------------------------------------------------
@@ -148,6 +127,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const int q = blockIdx.y;
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int sub = lane % LPR, rs = lane / LPR;
+    if constexpr (HIST) clear_hist2_slice(ws, q, S_max, k);
     const int bseq_raw = q_seq ? q_seq[q] : q;
     const int bseq = (bseq_raw < 0 || bseq_raw >= B) ? 0 : bseq_raw;
     const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)sub * V;
@@ -281,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const float* __restrict_
                                                         int chunk) {
     __shared__ uint32_t hist[kBins];
     const int q = blockIdx.y, tid = threadIdx.x;
+    clear_hist2_slice(ws, q, S_max, k);
     const int n = clamp_n(n_cand, q, S_max);
     const int s0 = blockIdx.x * chunk, s1 = min(n, s0 + chunk);
     if (s0 >= s1) return;
@@ -294,61 +275,6 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const float* __restrict_
         const uint32_t c = hist[i];
         if (c) atomicAdd(&W.hist[i], c);
     }
-}
-
-// ---- LDS radix machinery -------------------------------------------------------
-// Given bin counts h[0..NB), find the bin d such that (members in bins above d)
-// < need <= (members in bins above d) + h[d].  Returns d; *rem = need minus the
-// members above d.  Every thread calls it (it has barriers).
-template <int NB>
-__device__ int find_crossing(const uint32_t* h, int need, uint32_t* tmp, int* rem) {
-    static_assert(NB % kThreads == 0, "bins must be a multiple of the workgroup size");
-    constexpr int BPT = NB / kThreads;
-    __shared__ int res[2];
-    const int tid = threadIdx.x;
-    const int grp = kThreads - 1 - tid;  // thread 0 owns the top bins
-    if (tid == 0) { res[0] = 0; res[1] = 1; }
-    uint32_t s = 0;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) s += h[grp * BPT + j];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan<kThreads>(s, tmp, &tot);
-    if (above < (uint32_t)need && (uint32_t)need <= above + s) {
-        uint32_t cum = above;
-        for (int j = BPT - 1; j >= 0; --j) {
-            const uint32_t c = h[grp * BPT + j];
-            if (cum + c >= (uint32_t)need) {
-                res[0] = grp * BPT + j;
-                res[1] = need - (int)cum;
-                break;
-            }
-            cum += c;
-        }
-    }
-    __syncthreads();
-    const int d = res[0];
-    *rem = res[1];
-    __syncthreads();
-    return d;
-}
-
-// Histogram of digit (key >> shift) & (NB-1) over the members i < n
-// (member: (key & pmask) == pref, and, if eq_key != nullptr, eq_key[i] == eq_val),
-// then find_crossing.
-template <int NB>
-__device__ int radix_digit(const uint32_t* keys, int n, uint32_t pmask, uint32_t pref, int shift,
-                           const uint32_t* eq_key, uint32_t eq_val, int need, uint32_t* h,
-                           uint32_t* tmp, int* rem) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < NB; i += kThreads) h[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-        const uint32_t kk = keys[i];
-        if ((kk & pmask) == pref && (eq_key == nullptr || eq_key[i] == eq_val))
-            atomicAdd(&h[(kk >> shift) & (NB - 1)], 1u);
-    }
-    __syncthreads();
-    return find_crossing<NB>(h, need, tmp, rem);
 }
 
 // ---- one workgroup per query, all keys in LDS ---------------------------------
@@ -407,30 +333,45 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
 }
 
 // ---- multi-workgroup path: filter + final select ---------------------------------
-constexpr int kPerThread = kFilterChunk / kThreads;  // scores per thread (16)
-static_assert(kPerThread <= 16, "per-thread counts are packed in 16 bits");
+constexpr int kPerThread = kFilterChunk / kThreads;  // consecutive scores per thread (16)
+static_assert(kPerThread == 16, "per-thread masks and counts are 16 bits wide");
 
+// One workgroup per segment of 4096 candidates: thread t classifies the 16
+// consecutive candidates 16t..16t+15 of the segment against the threshold
+// bin, so one block prefix sum over (selected, short) counts places every
+// entry in index order.  Segment g's short list goes to cand_[4096 g ...),
+// its selected indices right after it, and its two counts to seg[g].
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ n_cand,
                                                                uint8_t* __restrict__ ws, int S_max,
                                                                int k) {
     __shared__ uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
-    __shared__ uint32_t base_lds[2];
 
     const int q = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
     const int n = clamp_n(n_cand, q, S_max);
     const int take = min(k, n);
     const int s0 = g * kFilterChunk;
+    if (s0 >= n) {  // uniform: nothing here; the count is written every call
+        if (tid == 0) W.seg[g] = 0;
+        return;
+    }
+    const int sb = s0 + tid * kPerThread;
 
-    // 1. this chunk's scores (all loads in flight together) and the threshold
-    //    bin of the first digit from the completed histogram
+    // 1. this thread's scores (all loads in flight together) and the
+    //    threshold bin of the first digit from the completed histogram
     float v[kPerThread];
+    const float* src = scores + (size_t)q * S_max + sb;
+    if (sb + kPerThread <= n && (((uintptr_t)src) & 15u) == 0) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        const int s = s0 + i * kThreads + tid;
-        v[i] = s < n ? scores[(size_t)q * S_max + s] : 0.f;
+        for (int j = 0; j < kPerThread / 4; ++j) {
+            const f32x4 t4 = reinterpret_cast<const f32x4*>(src)[j];
+            v[4 * j] = t4[0]; v[4 * j + 1] = t4[1]; v[4 * j + 2] = t4[2]; v[4 * j + 3] = t4[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) v[i] = sb + i < n ? src[i] : 0.f;
     }
     int t1 = -1;  // -1: every candidate is selected
     if (take < n) {
@@ -440,231 +381,58 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         t1 = find_crossing<kBins>(h, take, tmp, &rem);
     }
 
-    // 2. route: above the threshold bin -> selected list, inside it -> short
-    //    list; one reservation per workgroup and list, offsets by prefix sum
+    // 2. route: above the threshold bin -> selected, inside it -> short list
     uint32_t selm = 0, candm = 0, keys[kPerThread];
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-        const int s = s0 + i * kThreads + tid;
         keys[i] = score_key(v[i]);
         const int bin = (int)(keys[i] >> 21);
-        if (s < n && bin > t1) selm |= 1u << i;
-        if (s < n && bin == t1) candm |= 1u << i;
+        const bool ok = sb + i < n;
+        if (ok && bin > t1) selm |= 1u << i;
+        if (ok && bin == t1) candm |= 1u << i;
     }
     const uint32_t packed = ((uint32_t)__popc(selm) << 16) | (uint32_t)__popc(candm);
     uint32_t tot;
     const uint32_t off = block_excl_scan<kThreads>(packed, tmp, &tot);
-    if (tid == 0) {
-        base_lds[0] = (tot >> 16) ? atomicAdd(&W.ctr[1], tot >> 16) : 0u;
-        base_lds[1] = (tot & 0xffffu) ? atomicAdd(&W.ctr[0], tot & 0xffffu) : 0u;
-    }
-    __syncthreads();
-    uint32_t ps = base_lds[0] + (off >> 16), pc = base_lds[1] + (off & 0xffffu);
+    const uint32_t n_short = tot & 0xffffu;
+    uint32_t pc = (uint32_t)s0 + (off & 0xffffu);
+    uint32_t ps = (uint32_t)s0 + n_short + (off >> 16);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-        const uint32_t s = (uint32_t)(s0 + i * kThreads + tid);
-        if (selm & (1u << i)) {
-            if (ps < (uint32_t)k) W.sel[ps] = (int32_t)s;
-            ++ps;
-        }
+        const uint32_t sidx = (uint32_t)(sb + i);
         if (candm & (1u << i)) {
-            if (pc < (uint32_t)S_max) { W.cand_key[pc] = keys[i]; W.cand_idx[pc] = s; }
+            W.cand_key[pc] = keys[i];
+            W.cand_idx[pc] = sidx;
             ++pc;
             atomicAdd(&W.hist2[(keys[i] >> 10) & (kBins - 1)], 1u);
         }
+        if (selm & (1u << i)) W.cand_idx[ps++] = sidx;
     }
-
+    if (tid == 0) W.seg[g] = tot;
 }
 
 // Final select, one workgroup per query, after every filter workgroup of the
-// query has finished (kernel boundary).  The short list holds the candidates
-// of the threshold bin (all share its top 11 key bits); the second-digit
-// histogram the filter built gives key bits 20..10 of the k-th key, one LDS
-// histogram pass over bits 9..0 of the few candidates in that bucket gives
-// the k-th key T (skipped when the whole bucket is taken), and when more
-// candidates equal T than are still needed, three passes over the
-// complemented indices keep the lowest indices.  The output order is each
-// selected index's rank among the selected (broadcast LDS reads), and every
-// word the call wrote in the workspace is zeroed again.
-constexpr int kFinalLoads = kCandCap / kThreads;
-constexpr int kSelLoads = kTopkMaxK / kThreads;
-
+// query has finished (kernel boundary): the steps of select.hpp, the merge of
+// the two ascending lists into the output, and the zeroing of the query's
+// workspace.
 __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __restrict__ n_cand,
                                                               int32_t* __restrict__ out,
                                                               uint8_t* __restrict__ ws, int S_max,
                                                               int k) {
     __shared__ uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
+    __shared__ uint32_t segc[kMaxSeg], sbase[kMaxSeg], lbase[kMaxSeg];
     __shared__ uint32_t ck[kCandCap], ci[kCandCap];
-    __shared__ __align__(16) int32_t sel[kTopkMaxK];
-    __shared__ uint32_t nsel_lds;
-    __shared__ int cnt[3];
+    __shared__ int32_t selv[kTopkMaxK], chs[kTopkMaxK];
+    __shared__ uint32_t misc[4];
 
-    const int q = blockIdx.x, tid = threadIdx.x;
+    const int q = blockIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
-    if (tid == 0) cnt[0] = clamp_n(n_cand, q, S_max);
-    if (tid == 1) cnt[1] = (int)W.ctr[1];
-    if (tid == 2) cnt[2] = (int)W.ctr[0];
+    const SelLds L = {h, tmp, segc, sbase, lbase, ck, ci, selv, chs, misc};
+    const SelResult R = select_query(W, clamp_n(n_cand, q, S_max), S_max, k, k, L);
+    select_write_sorted(L, R, out + (size_t)q * k, k);
     __syncthreads();
-    const int n = cnt[0];
-    const int take = min(k, n);
-    const int sel_raw = min(cnt[1], k), nsel0 = min(cnt[1], take);
-    const int nc = min(cnt[2], S_max);
-    const bool small = nc <= kCandCap;
-    int need = take - nsel0;
-    const bool refine = need > 0 && nc > 0;  // uniform
-
-    // every load in flight at once: selected list, short list, second-digit histogram
-    int32_t sv[kSelLoads];
-    uint32_t kv[kFinalLoads], iv[kFinalLoads], hv[kBins / kThreads];
-#pragma unroll
-    for (int j = 0; j < kSelLoads; ++j) {
-        const int i = tid + j * kThreads;
-        sv[j] = i < nsel0 ? W.sel[i] : 0;
-    }
-    if (small) {
-#pragma unroll
-        for (int j = 0; j < kFinalLoads; ++j) {
-            const int i = tid + j * kThreads;
-            kv[j] = i < nc ? W.cand_key[i] : 0u;
-            iv[j] = i < nc ? W.cand_idx[i] : 0u;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kBins / kThreads; ++j) hv[j] = refine ? W.hist2[tid + j * kThreads] : 0u;
-#pragma unroll
-    for (int j = 0; j < kSelLoads; ++j) {
-        const int i = tid + j * kThreads;
-        if (i < nsel0) sel[i] = sv[j];
-    }
-    if (small) {
-#pragma unroll
-        for (int j = 0; j < kFinalLoads; ++j) {
-            const int i = tid + j * kThreads;
-            if (i < nc) { ck[i] = kv[j]; ci[i] = iv[j]; }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kBins / kThreads; ++j) h[tid + j * kThreads] = hv[j];
-    if (tid == 0) nsel_lds = (uint32_t)nsel0;
-    __syncthreads();
-
-    if (refine) {
-        const uint32_t* key = small ? ck : W.cand_key;
-        const uint32_t* idx = small ? ci : W.cand_idx;
-        const uint32_t p1 = key[0] & 0xffe00000u;  // the threshold bin's 11 bits
-        int rem;
-        const int d2 = find_crossing<kBins>(h, need, tmp, &rem);
-        const uint32_t p2 = p1 | ((uint32_t)d2 << 10);
-        // the whole bucket is taken: no tie to break (read by all before h is reused)
-        const bool whole = (int)h[d2] == rem;
-        __syncthreads();
-        need = rem;
-        uint32_t T = p2, imax = 0xffffffffu;
-        if (!whole) {
-            const int d3 = radix_digit<1024>(key, nc, 0xfffffc00u, p2, 0, nullptr, 0u, need, h, tmp, &rem);
-            need = rem;
-            T = p2 | (uint32_t)d3;
-            uint32_t eq = 0;
-            for (int i = tid; i < nc; i += kThreads) eq += key[i] == T;
-            uint32_t eq_all;
-            block_excl_scan<kThreads>(eq, tmp, &eq_all);
-            if ((int)eq_all > need) {
-                // the need lowest indices among the T-valued: digits of ~idx, highest first
-                int r = need;
-                uint32_t pr = 0, pm = 0;
-                const int shifts[3] = {21, 10, 0};
-                const int widths[3] = {11, 11, 10};
-                for (int pass = 0; pass < 3; ++pass) {
-                    const int nb = 1 << widths[pass];
-                    for (int i = tid; i < kBins; i += kThreads) h[i] = 0;
-                    __syncthreads();
-                    for (int i = tid; i < nc; i += kThreads) {
-                        if (key[i] != T) continue;
-                        const uint32_t ni = ~idx[i];
-                        if ((ni & pm) == pr) atomicAdd(&h[(ni >> shifts[pass]) & (nb - 1)], 1u);
-                    }
-                    __syncthreads();
-                    const int d = (nb == kBins) ? find_crossing<kBins>(h, r, tmp, &rem)
-                                                : find_crossing<1024>(h, r, tmp, &rem);
-                    r = rem;
-                    pr |= (uint32_t)d << shifts[pass];
-                    pm |= (uint32_t)(nb - 1) << shifts[pass];
-                }
-                imax = ~pr;  // indices <= imax among the T-valued are taken
-            }
-        }
-        // whole bucket: every key >= p2 is taken; otherwise keys > T, and T-valued up to imax
-        for (int i = tid; i < nc; i += kThreads) {
-            const uint32_t kk = key[i];
-            const bool take_it = whole ? (kk >= p2) : (kk > T || (kk == T && idx[i] <= imax));
-            if (take_it) {
-                const uint32_t pos = atomicAdd(&nsel_lds, 1u);
-                if (pos < (uint32_t)take) sel[pos] = (int32_t)idx[i];
-            }
-        }
-        __syncthreads();
-    }
-    // Ascending order by a bucketed counting sort of the selected indices:
-    // bucket = index >> bshift (at most 2048 buckets over the candidate
-    // range), bucket starts by a prefix sum, and an index's place inside its
-    // bucket is the number of smaller indices in the same bucket (buckets
-    // hold a handful of entries).  Every step is parallel over the entries.
-    const int filled = min((int)nsel_lds, take);
-    int32_t* o = out + (size_t)q * k;
-    {
-        int bshift = 0;
-        while ((((uint32_t)S_max - 1u) >> bshift) >= (uint32_t)kBins) ++bshift;
-        uint32_t* bstart = h;                                   // [kBins]
-        uint32_t* bfill = ck;                                   // [kBins] fill counters
-        int32_t* bucketed = reinterpret_cast<int32_t*>(ci);     // [kTopkMaxK]
-        for (int i = tid; i < kBins; i += kThreads) { bstart[i] = 0; bfill[i] = 0; }
-        __syncthreads();
-        for (int i = tid; i < filled; i += kThreads) atomicAdd(&bstart[(uint32_t)sel[i] >> bshift], 1u);
-        __syncthreads();
-        {
-            // exclusive prefix over the bucket counts (8 buckets per thread)
-            constexpr int BPT = kBins / kThreads;
-            uint32_t c[BPT], sum = 0;
-#pragma unroll
-            for (int j = 0; j < BPT; ++j) { c[j] = bstart[tid * BPT + j]; sum += c[j]; }
-            uint32_t tot;
-            uint32_t base = block_excl_scan<kThreads>(sum, tmp, &tot);
-#pragma unroll
-            for (int j = 0; j < BPT; ++j) { bstart[tid * BPT + j] = base; base += c[j]; }
-        }
-        __syncthreads();
-        int32_t mine[kSelLoads];
-        uint32_t slot[kSelLoads];
-#pragma unroll
-        for (int j = 0; j < kSelLoads; ++j) {
-            const int i = tid + j * kThreads;
-            mine[j] = i < filled ? sel[i] : 0;
-            if (i < filled) {
-                const uint32_t bk = (uint32_t)mine[j] >> bshift;
-                slot[j] = bstart[bk] + atomicAdd(&bfill[bk], 1u);
-                bucketed[slot[j]] = mine[j];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kSelLoads; ++j) {
-            const int i = tid + j * kThreads;
-            if (i < filled) {
-                const uint32_t bk = (uint32_t)mine[j] >> bshift;
-                const uint32_t b0 = bstart[bk], b1 = b0 + bfill[bk];
-                uint32_t rank = b0;
-                for (uint32_t e = b0; e < b1; ++e) rank += bucketed[e] < mine[j];
-                o[rank] = mine[j];
-            }
-        }
-    }
-    for (int i = filled + tid; i < k; i += kThreads) o[i] = -1;
-    // Leave every word this call wrote for this query zeroed again.
-    for (int i = tid; i < kBins; i += kThreads) { W.hist[i] = 0; W.hist2[i] = 0; }
-    for (int i = tid; i < nc; i += kThreads) { W.cand_key[i] = 0; W.cand_idx[i] = 0; }
-    for (int i = tid; i < sel_raw; i += kThreads) W.sel[i] = 0;
-    if (tid < 16) W.ctr[tid] = 0;
+    select_zero<kThreads>(W, S_max, segc, tmp);
 }
 
 template <typename T, int LPR>
@@ -703,6 +471,21 @@ hipError_t launch_score_t(int d_I, const void* q_idx, const void* k_idx, int B,
 size_t topk_workspace_bytes(int Nq, int S_max, int k) {
     if (S_max <= kRowSelectCap) return 0;
     return (size_t)Nq * ws_per_query(S_max, k);
+}
+
+hipError_t launch_index_filter(int dtype, const void* q_idx, const void* k_idx, int B,
+                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
+                               int S_max, int k, void* ws, hipStream_t st) {
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    hipError_t e = dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
+                                                         Nq, H_I, S_max, k, true, st)
+                                 : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores,
+                                                          w, Nq, H_I, S_max, k, true, st);
+    if (e != hipSuccess) return e;
+    ProfScope prof(kProfSelect, st);
+    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)n_segments(S_max), (unsigned)Nq), dim3(kThreads),
+                       0, st, scores, n_cand, w, S_max, k);
+    return hipGetLastError();
 }
 
 hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, int B,

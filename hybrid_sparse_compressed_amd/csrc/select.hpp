@@ -1,0 +1,373 @@
+// select.hpp -- workspace layout and device steps of the multi-workgroup
+// exact top-k, shared by the final select kernel (index_topk.hip) and the
+// fused sparse-decode attention kernel (attention.hip).
+//
+// [KD "Arquitectura del Sistema"] and [NK "推理侧优化", Lightning topk
+// bullet]: the C4 top-k is a radix select.  Order: score descending, equal
+// scores by lower index; keys are the order-preserving u32 images of the
+// fp32 scores (score_key).  The scoring kernel builds the histogram of the
+// top 11 key bits, the filter kernel writes per segment of 4096 candidates
+// the candidates above the threshold bin ("selected") and inside it ("short
+// list"), both in index order, and the steps here finish the select for one
+// query inside one workgroup of 256 threads.
+#pragma once
+
+#include "hsa_common.hpp"
+#include "hsa_internal.hpp"
+
+namespace hsa {
+namespace sel {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelNW = kSelThreads / kWave;
+constexpr int kBins = 2048;         // first digit: key bits 31..21
+constexpr int kFilterChunk = 4096;  // candidates per filter segment
+constexpr int kCandCap = 4096;      // short-list entries kept in LDS
+constexpr int kMaxSeg = kTopkMaxSegments;
+
+// ---- workspace (multi-workgroup path), per query -------------------------
+//   hist[2048] u32 (key bits 31..21 of every candidate) | hist2[2048] u32
+//   (key bits 20..10 of the short list) | ctr[16] u32 (reserved) |
+//   seg[nseg] u32 (per filter segment: short-list count | selected count << 16)
+//   | cand_key[S_max] | cand_idx[S_max] (segment g owns [4096 g, 4096 g + 4096):
+//   its short-list (key, index) pairs first, then its selected indices) |
+//   flat_key[S_max] | flat_idx[S_max] (the whole short list in one run, used
+//   only when it does not fit in LDS)
+__host__ __device__ inline int n_segments(int S_max) { return (S_max + kFilterChunk - 1) / kFilterChunk; }
+__host__ __device__ inline size_t ws_per_query(int S_max, int k) {
+    (void)k;
+    size_t b = (size_t)kBins * 8 + 64 + (size_t)n_segments(S_max) * 4 + (size_t)S_max * 16;
+    return (b + 255) & ~(size_t)255;
+}
+
+struct QWs {
+    uint32_t* hist;
+    uint32_t* hist2;
+    uint32_t* ctr;
+    uint32_t* seg;
+    uint32_t* cand_key;
+    uint32_t* cand_idx;
+    uint32_t* flat_key;
+    uint32_t* flat_idx;
+};
+
+__device__ inline QWs ws_of(uint8_t* ws, int q, int S_max, int k) {
+    uint8_t* base = ws + (size_t)q * ws_per_query(S_max, k);
+    QWs w;
+    w.hist = reinterpret_cast<uint32_t*>(base);
+    w.hist2 = w.hist + kBins;
+    w.ctr = w.hist2 + kBins;
+    w.seg = w.ctr + 16;
+    w.cand_key = w.seg + n_segments(S_max);
+    w.cand_idx = w.cand_key + S_max;
+    w.flat_key = w.cand_idx + S_max;
+    w.flat_idx = w.flat_key + S_max;
+    return w;
+}
+
+__device__ inline int clamp_n(const int32_t* n_cand, int q, int S_max) {
+    int n = n_cand[q];
+    return n < 0 ? 0 : (n > S_max ? S_max : n);
+}
+
+// ---- LDS radix machinery -------------------------------------------------------
+// Given bin counts h[0..NB), find the bin d such that (members in bins above d)
+// < need <= (members in bins above d) + h[d].  Returns d; *rem = need minus the
+// members above d.  Every thread calls it (it has barriers).
+template <int NB>
+__device__ int find_crossing(const uint32_t* h, int need, uint32_t* tmp, int* rem) {
+    static_assert(NB % kSelThreads == 0, "bins must be a multiple of the workgroup size");
+    constexpr int BPT = NB / kSelThreads;
+    __shared__ int res[2];
+    const int tid = threadIdx.x;
+    const int grp = kSelThreads - 1 - tid;  // thread 0 owns the top bins
+    if (tid == 0) { res[0] = 0; res[1] = 1; }
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) s += h[grp * BPT + j];
+    uint32_t tot;
+    const uint32_t above = block_excl_scan<kSelThreads>(s, tmp, &tot);
+    if (above < (uint32_t)need && (uint32_t)need <= above + s) {
+        uint32_t cum = above;
+        for (int j = BPT - 1; j >= 0; --j) {
+            const uint32_t c = h[grp * BPT + j];
+            if (cum + c >= (uint32_t)need) {
+                res[0] = grp * BPT + j;
+                res[1] = need - (int)cum;
+                break;
+            }
+            cum += c;
+        }
+    }
+    __syncthreads();
+    const int d = res[0];
+    *rem = res[1];
+    __syncthreads();
+    return d;
+}
+
+// Histogram of digit (key >> shift) & (NB-1) over the members i < n
+// (member: (key & pmask) == pref, and, if eq_key != nullptr, eq_key[i] == eq_val),
+// then find_crossing.
+template <int NB>
+__device__ int radix_digit(const uint32_t* keys, int n, uint32_t pmask, uint32_t pref, int shift,
+                           const uint32_t* eq_key, uint32_t eq_val, int need, uint32_t* h,
+                           uint32_t* tmp, int* rem) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < NB; i += kSelThreads) h[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+        const uint32_t kk = keys[i];
+        if ((kk & pmask) == pref && (eq_key == nullptr || eq_key[i] == eq_val))
+            atomicAdd(&h[(kk >> shift) & (NB - 1)], 1u);
+    }
+    __syncthreads();
+    return find_crossing<NB>(h, need, tmp, rem);
+}
+
+// lower bound of v in the ascending LDS list a[0..n)
+__device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n, int32_t v) {
+    uint32_t lo = 0, hi = n;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (a[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// ---- one query's select inside one workgroup ---------------------------------
+// LDS working set (any LDS the caller owns; nothing else may use it meanwhile).
+struct SelLds {
+    uint32_t* h;      // [kBins]
+    uint32_t* tmp;    // [kSelNW + 2]
+    uint32_t* segc;   // [kMaxSeg] per segment: short count | selected count << 16
+    uint32_t* sbase;  // [kMaxSeg] first short-list position of the segment
+    uint32_t* lbase;  // [kMaxSeg] first selected-list position of the segment
+    uint32_t* ck;     // [kCandCap] short-list keys   (when it fits)
+    uint32_t* ci;     // [kCandCap] short-list indices
+    int32_t* sel;     // [kTopkMaxK] selected indices, ascending
+    int32_t* chs;     // [kTopkMaxK] chosen short-list indices, ascending
+    uint32_t* misc;   // [4]
+};
+
+struct SelResult {
+    int nseg;    // filter segments
+    int take;    // min(k, n)
+    int nc;      // short-list length
+    int nsel;    // selected-list length (<= take)
+    int nch;     // chosen short-list entries (nsel + nch = take)
+    int T_s;     // threads per segment in the gather / zero mapping
+};
+
+// Gathers the selected list (ascending, all of it) and, when positions past
+// it are needed (j_need > its length), the short list, then finds the k-th key from the second-digit histogram (plus one 10-bit pass
+// over its bucket unless the bucket is taken whole, plus three passes over
+// complemented indices when a tie straddles rank k) and compacts the chosen
+// short-list entries in order.  The result lists are L.sel[0..nsel) and
+// L.chs[0..nch), both ascending; the first take = nsel + nch entries of the
+// query's top-k are their union.  Short lists longer than kCandCap go through
+// W.flat_key / W.flat_idx (every caller that reaches that path writes the
+// same values).  Every thread calls it.
+__device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, int j_need,
+                                        const SelLds& L) {
+    const int tid = threadIdx.x;
+    SelResult R;
+    R.nseg = n_segments(S_max);
+    R.take = min(k, n);
+
+    // 1. segment counts and the second-digit histogram (loads in flight together)
+    constexpr int SPT = kMaxSeg / kSelThreads;  // segments per thread (contiguous)
+    uint32_t c[SPT], hv[kBins / kSelThreads];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int gg = tid * SPT + j;
+        c[j] = gg < R.nseg ? W.seg[gg] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kBins / kSelThreads; ++j) hv[j] = W.hist2[tid + j * kSelThreads];
+    uint32_t s_short = 0, s_sel = 0;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) { s_short += c[j] & 0xffffu; s_sel += c[j] >> 16; }
+    uint32_t nc_all, nsel_all;
+    uint32_t b_short = block_excl_scan<kSelThreads>(s_short, L.tmp, &nc_all);
+    uint32_t b_sel = block_excl_scan<kSelThreads>(s_sel, L.tmp, &nsel_all);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int gg = tid * SPT + j;
+        if (gg < R.nseg) { L.segc[gg] = c[j]; L.sbase[gg] = b_short; L.lbase[gg] = b_sel; }
+        b_short += c[j] & 0xffffu;
+        b_sel += c[j] >> 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kBins / kSelThreads; ++j) L.h[tid + j * kSelThreads] = hv[j];
+    __syncthreads();
+    R.nc = (int)nc_all;
+    R.nsel = min((int)nsel_all, R.take);
+    const bool small = R.nc <= kCandCap;
+    int need = R.take - R.nsel;
+    const bool refine = need > 0 && R.nc > 0 && j_need > R.nsel;  // uniform
+
+    // 2. gather the runs: T_s threads per segment, 8 entries per thread in flight
+    int T_s = 1;
+    while (T_s * 2 * R.nseg <= kSelThreads) T_s *= 2;
+    R.T_s = T_s;
+    {
+        const int par = kSelThreads / T_s, r = tid % T_s;
+        for (int gg = tid / T_s; gg < R.nseg; gg += par) {
+            const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
+            const uint32_t base = (uint32_t)gg * kFilterChunk;
+            for (uint32_t j0 = (uint32_t)r; j0 < cnt; j0 += 8u * (uint32_t)T_s) {
+                uint32_t kk[8], ii[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t j = j0 + (uint32_t)(u * T_s);
+                    ii[u] = j < cnt ? W.cand_idx[base + j] : 0u;
+                    kk[u] = (refine && j < cs) ? W.cand_key[base + j] : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t j = j0 + (uint32_t)(u * T_s);
+                    if (j < cs) {
+                        if (refine) {
+                            const uint32_t d = L.sbase[gg] + j;
+                            if (small) { L.ck[d] = kk[u]; L.ci[d] = ii[u]; }
+                            else { W.flat_key[d] = kk[u]; W.flat_idx[d] = ii[u]; }
+                        }
+                    } else if (j < cnt) {
+                        const uint32_t d = L.lbase[gg] + (j - cs);
+                        if (d < (uint32_t)kTopkMaxK) L.sel[d] = (int32_t)ii[u];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    R.nch = 0;
+    if (!refine) return R;
+
+    // 3. the k-th key and how many of its ties are taken
+    const uint32_t* key = small ? L.ck : W.flat_key;
+    const uint32_t* idx = small ? L.ci : W.flat_idx;
+    const int nc = R.nc;
+    uint32_t* h = L.h;
+    bool whole;
+    uint32_t p2, T, imax = 0xffffffffu;
+    {
+        const uint32_t p1 = key[0] & 0xffe00000u;  // the threshold bin's 11 bits
+        int rem;
+        const int d2 = find_crossing<kBins>(h, need, L.tmp, &rem);
+        p2 = p1 | ((uint32_t)d2 << 10);
+        // the whole bucket is taken: no tie to break (read by all before h is reused)
+        whole = (int)h[d2] == rem;
+        __syncthreads();
+        need = rem;
+        T = p2;
+        if (!whole) {
+            const int d3 = radix_digit<1024>(key, nc, 0xfffffc00u, p2, 0, nullptr, 0u, need, h, L.tmp, &rem);
+            need = rem;
+            T = p2 | (uint32_t)d3;
+            uint32_t eq = 0;
+            for (int i = tid; i < nc; i += kSelThreads) eq += key[i] == T;
+            uint32_t eq_all;
+            block_excl_scan<kSelThreads>(eq, L.tmp, &eq_all);
+            if ((int)eq_all > need) {
+                // the need lowest indices among the T-valued: digits of ~idx, highest first
+                int rr = need;
+                uint32_t pr = 0, pm = 0;
+                const int shifts[3] = {21, 10, 0};
+                const int widths[3] = {11, 11, 10};
+                for (int pass = 0; pass < 3; ++pass) {
+                    const int nb = 1 << widths[pass];
+                    for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0;
+                    __syncthreads();
+                    for (int i = tid; i < nc; i += kSelThreads) {
+                        if (key[i] != T) continue;
+                        const uint32_t ni = ~idx[i];
+                        if ((ni & pm) == pr) atomicAdd(&h[(ni >> shifts[pass]) & (nb - 1)], 1u);
+                    }
+                    __syncthreads();
+                    const int d = (nb == kBins) ? find_crossing<kBins>(h, rr, L.tmp, &rem)
+                                                : find_crossing<1024>(h, rr, L.tmp, &rem);
+                    rr = rem;
+                    pr |= (uint32_t)d << shifts[pass];
+                    pm |= (uint32_t)(nb - 1) << shifts[pass];
+                }
+                imax = ~pr;  // indices <= imax among the T-valued are taken
+            }
+        }
+    }
+
+    // 4. chosen short-list entries, compacted in order (contiguous ranges per thread)
+    {
+        const int E = ceil_div(nc, kSelThreads);
+        const int i0 = min(nc, tid * E), i1 = min(nc, i0 + E);
+        auto chosen = [&](int i) {
+            const uint32_t kk = key[i];
+            return whole ? (kk >= p2) : (kk > T || (kk == T && idx[i] <= imax));
+        };
+        uint32_t cnt = 0;
+        for (int i = i0; i < i1; ++i) cnt += chosen(i);
+        uint32_t all;
+        uint32_t pos = block_excl_scan<kSelThreads>(cnt, L.tmp, &all);
+        for (int i = i0; i < i1; ++i)
+            if (chosen(i)) {
+                if (pos < (uint32_t)kTopkMaxK) L.chs[pos] = (int32_t)idx[i];
+                ++pos;
+            }
+        if (tid == 0) L.misc[0] = all;
+        __syncthreads();
+        R.nch = min((int)L.misc[0], R.take - R.nsel);
+    }
+    return R;
+}
+
+// The query's top-k in ascending index order: the merge of the two ascending
+// lists (output position = own rank + rank in the other list), -1 padded.
+__device__ inline void select_write_sorted(const SelLds& L, const SelResult& R, int32_t* o, int k) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < R.nsel; i += kSelThreads) {
+        const int32_t v = L.sel[i];
+        o[i + (int)lower_bound_lds(L.chs, (uint32_t)R.nch, v)] = v;
+    }
+    for (int j = tid; j < R.nch; j += kSelThreads) {
+        const int32_t v = L.chs[j];
+        o[j + (int)lower_bound_lds(L.sel, (uint32_t)R.nsel, v)] = v;
+    }
+    for (int i = R.nsel + R.nch + tid; i < k; i += kSelThreads) o[i] = -1;
+}
+
+// Zero every workspace word a call wrote for one query (one workgroup of NT
+// threads, after every reader of the query's workspace has finished).
+// segc: LDS [kMaxSeg], tmp: LDS [NT / 64 + 2].
+template <int NT>
+__device__ inline void select_zero(const QWs& W, int S_max, uint32_t* segc, uint32_t* tmp) {
+    const int tid = threadIdx.x;
+    const int nseg = n_segments(S_max);
+    uint32_t mine = 0;
+    for (int gg = tid; gg < nseg; gg += NT) {
+        const uint32_t v = W.seg[gg];
+        segc[gg] = v;
+        mine += v & 0xffffu;
+    }
+    for (int i = tid; i < kBins; i += NT) { W.hist[i] = 0; W.hist2[i] = 0; }
+    if (tid < 16) W.ctr[tid] = 0;
+    uint32_t nc;  // short-list length (decides whether the flat copy was written)
+    block_excl_scan<NT>(mine, tmp, &nc);  // its barriers publish segc
+    int T_s = 1;
+    while (T_s * 2 * nseg <= NT) T_s *= 2;
+    const int par = NT / T_s, r = tid % T_s;
+    for (int gg = tid / T_s; gg < nseg; gg += par) {
+        const uint32_t cs = segc[gg] & 0xffffu, cnt = cs + (segc[gg] >> 16);
+        const uint32_t base = (uint32_t)gg * kFilterChunk;
+        for (uint32_t j = (uint32_t)r; j < cnt; j += (uint32_t)T_s) {
+            W.cand_idx[base + j] = 0;
+            if (j < cs) W.cand_key[base + j] = 0;
+        }
+    }
+    if (nc > (uint32_t)kCandCap)
+        for (uint32_t i = (uint32_t)tid; i < nc; i += NT) { W.flat_key[i] = 0; W.flat_idx[i] = 0; }
+    for (int gg = tid; gg < nseg; gg += NT) W.seg[gg] = 0;  // every count was read above
+}
+
+}  // namespace sel
+}  // namespace hsa

@@ -111,8 +111,9 @@ int hsa_compress(int dtype, const void *x, const void *gate, const void *bias, v
  *   scores   : [Nq, S_max] fp32, output (score mode) or input (select-only)
  *   topk_idx : [Nq, k] int32 output
  *   Sizes    : Nq >= 1, B >= 1, H_I >= 1, d_I*sizeof(dtype) in {128, 256, 512},
- *              S_max >= 1, 1 <= k <= 2048.  flags must be 0 (reserved for a
- *              weighted/activated head combination).
+ *              1 <= S_max <= 4,194,304 (HSA_ERR_UNSUPPORTED above), 1 <= k <= 2048.
+ *              flags must be 0 (reserved for a weighted/activated head
+ *              combination).
  *   workspace: device memory of hsa_index_topk_workspace_size(Nq, S_max, k)
  *              bytes.  It must be zero-filled before its first use; every
  *              call that completes leaves it zero-filled again.
@@ -162,6 +163,42 @@ int hsa_attn_decode(int dtype, const void *q, const void *swa_kv, const int32_t 
                     void *out, float *lse, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                     int32_t W, int32_t S_max, int32_t k, float scale, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * hsa_decode_sparse -- the C4 decode layer-step in one call: indexer scores,
+ * exact top-k select and the SWA + selected-row attention, for one query per
+ * sequence (query b reads sequence b).
+ *
+ * [KD "Flujo de Inferencia", step "Indexer (TopK)"] then [LH "Tich hop Kernel
+ * va Giai ma suy doan"]: the indexer picks the top-k C4 entries and one
+ * attention call covers the window and those entries.
+ *
+ * Results equal hsa_index_topk(dtype, q_idx, k_idx, B, NULL, n_cand, scores,
+ * topk_idx, B, H_I, d_I, S_max, k, 0, ...) followed by hsa_attn_decode(dtype,
+ * q, swa_kv, swa_len, comp_kv, topk_idx, comp_len, out, lse, B, H, d_qk, d_v,
+ * W, S_max, k, scale, ...): scores and topk_idx identically; out and lse up
+ * to rounding, since the attention may sum the selected rows in another
+ * order (for S_max > 12,288 the select is finished inside the attention
+ * kernel and the rows are taken as the selected-above-threshold list followed
+ * by the chosen threshold-bin entries, each in index order).
+ *
+ *   Arguments: as in hsa_index_topk (q_idx must not be NULL) and
+ *              hsa_attn_decode (sparse mode), same layouts and limits.
+ *   workspace: hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k)
+ *              bytes, zero-filled before its first use.  Every call that
+ *              completes leaves it ready for the next call with the same
+ *              (B, H, d_v, W, S_max, k) (its histograms zero; other words it
+ *              holds are rewritten before they are read), so a buffer reused
+ *              with other sizes must be zero-filled again first.
+ */
+size_t hsa_decode_sparse_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t W,
+                                        int32_t S_max, int32_t k);
+int hsa_decode_sparse(int dtype, const void *q_idx, const void *k_idx, const int32_t *n_cand,
+                      float *scores, int32_t *topk_idx, const void *q, const void *swa_kv,
+                      const int32_t *swa_len, const void *comp_kv, const int32_t *comp_len,
+                      void *out, float *lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
+                      int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
+                      float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * hsa_attn_prefill -- a chunk of n_q consecutive query positions per
