@@ -125,7 +125,7 @@ static_assert(kTile == 64, "the fp32 PV map assumes 16 steps of 4 rows");
 constexpr int kModeDecode = 0, kModePrefill = 1, kModeFused = 2;
 
 // LDS the select prologue of the fused mode carves out of the tile buffers
-constexpr size_t kSelLdsBytes = (size_t)sel::kBins * 4 + (sel::kSelNW + 2) * 4 + 3 * (size_t)sel::kMaxSeg * 4 +
+constexpr size_t kSelLdsBytes = (size_t)sel::kBins * 4 + (2 * sel::kSelNW + 2) * 4 + 3 * (size_t)sel::kMaxSeg * 4 +
                                 2 * (size_t)sel::kCandCap * 4 + 2 * (size_t)kTopkMaxK * 4 + 16;
 __device__ inline sel::SelLds sel_lds_at(unsigned char* base) {
     sel::SelLds L;

@@ -101,6 +101,33 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
     return base + inc - v;
 }
 
+// Two exclusive prefix sums over a workgroup of NT threads in one pass (one
+// barrier pair).  `tmp` must hold 2 * (NT/64) words of LDS.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t* tmp,
+                                                 uint32_t* base_a, uint32_t* base_b,
+                                                 uint32_t* total_a, uint32_t* total_b) {
+    constexpr int NW = NT / kWave;
+    const int w = (int)threadIdx.x / kWave;
+    const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    if (lane_id() == kWave - 1) { tmp[w] = ia; tmp[NW + w] = ib; }
+    __syncthreads();
+    uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t xa = tmp[i], xb = tmp[NW + i];
+        pa += (i < w) ? xa : 0u;
+        pb += (i < w) ? xb : 0u;
+        ta += xa;
+        tb += xb;
+    }
+    __syncthreads();
+    *base_a = pa + ia - a;
+    *base_b = pb + ib - b;
+    *total_a = ta;
+    *total_b = tb;
+}
+
 // ---- radix-select key -------------------------------------------------------
 // Order-preserving map fp32 -> u32: a > b (IEEE) iff key(a) > key(b); -0 and
 // +0 share one key; every NaN maps to 0, below -inf (0x007fffff).

@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
                                                               uint8_t* __restrict__ ws, int S_max,
                                                               int k) {
     __shared__ uint32_t h[kBins];
-    __shared__ uint32_t tmp[kNW + 2];
+    __shared__ uint32_t tmp[2 * kNW + 2];
     __shared__ uint32_t segc[kMaxSeg], sbase[kMaxSeg], lbase[kMaxSeg];
     __shared__ uint32_t ck[kCandCap], ci[kCandCap];
     __shared__ int32_t selv[kTopkMaxK], chs[kTopkMaxK];

@@ -139,7 +139,7 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
 // LDS working set (any LDS the caller owns; nothing else may use it meanwhile).
 struct SelLds {
     uint32_t* h;      // [kBins]
-    uint32_t* tmp;    // [kSelNW + 2]
+    uint32_t* tmp;    // [2 * kSelNW + 2]
     uint32_t* segc;   // [kMaxSeg] per segment: short count | selected count << 16
     uint32_t* sbase;  // [kMaxSeg] first short-list position of the segment
     uint32_t* lbase;  // [kMaxSeg] first selected-list position of the segment
@@ -175,9 +175,18 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
     R.nseg = n_segments(S_max);
     R.take = min(k, n);
 
-    // 1. segment counts and the second-digit histogram (loads in flight together)
-    constexpr int SPT = kMaxSeg / kSelThreads;  // segments per thread (contiguous)
-    uint32_t c[SPT], hv[kBins / kSelThreads];
+    // 1. segment counts, the second-digit histogram and the first entries of
+    //    every segment's runs, all loads in flight together: T_s threads per
+    //    segment, thread r of a segment takes entries r, r + T_s, ... and the
+    //    first kSpec of them are read before their count is known (they lie
+    //    inside the segment's slots, so reading them is always in bounds)
+    constexpr int SPT = kMaxSeg / kSelThreads;  // segments per thread in the scan (contiguous)
+    constexpr int kSpec = 8;
+    int T_s = 1;
+    while (T_s * 2 * R.nseg <= kSelThreads) T_s *= 2;
+    R.T_s = T_s;
+    const int par = kSelThreads / T_s, r = tid % T_s, g0 = tid / T_s;
+    uint32_t c[SPT], hv[kBins / kSelThreads], kk[kSpec], ii[kSpec];
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
         const int gg = tid * SPT + j;
@@ -185,12 +194,22 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
     }
 #pragma unroll
     for (int j = 0; j < kBins / kSelThreads; ++j) hv[j] = W.hist2[tid + j * kSelThreads];
+    if (g0 < R.nseg) {
+        const uint32_t base = (uint32_t)g0 * kFilterChunk;
+        const uint32_t room = (uint32_t)min(kFilterChunk, S_max - g0 * kFilterChunk);  // slots of the segment
+#pragma unroll
+        for (int u = 0; u < kSpec; ++u) {
+            const uint32_t j = (uint32_t)(r + u * T_s);
+            ii[u] = j < room ? W.cand_idx[base + j] : 0u;
+            kk[u] = j < room ? W.cand_key[base + j] : 0u;
+        }
+    }
     uint32_t s_short = 0, s_sel = 0;
 #pragma unroll
     for (int j = 0; j < SPT; ++j) { s_short += c[j] & 0xffffu; s_sel += c[j] >> 16; }
     uint32_t nc_all, nsel_all;
-    uint32_t b_short = block_excl_scan<kSelThreads>(s_short, L.tmp, &nc_all);
-    uint32_t b_sel = block_excl_scan<kSelThreads>(s_sel, L.tmp, &nsel_all);
+    uint32_t b_short, b_sel;
+    block_excl_scan2<kSelThreads>(s_short, s_sel, L.tmp, &b_short, &b_sel, &nc_all, &nsel_all);
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
         const int gg = tid * SPT + j;
@@ -207,38 +226,38 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
     int need = R.take - R.nsel;
     const bool refine = need > 0 && R.nc > 0 && j_need > R.nsel;  // uniform
 
-    // 2. gather the runs: T_s threads per segment, 8 entries per thread in flight
-    int T_s = 1;
-    while (T_s * 2 * R.nseg <= kSelThreads) T_s *= 2;
-    R.T_s = T_s;
-    {
-        const int par = kSelThreads / T_s, r = tid % T_s;
-        for (int gg = tid / T_s; gg < R.nseg; gg += par) {
-            const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
-            const uint32_t base = (uint32_t)gg * kFilterChunk;
-            for (uint32_t j0 = (uint32_t)r; j0 < cnt; j0 += 8u * (uint32_t)T_s) {
-                uint32_t kk[8], ii[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t j = j0 + (uint32_t)(u * T_s);
-                    ii[u] = j < cnt ? W.cand_idx[base + j] : 0u;
-                    kk[u] = (refine && j < cs) ? W.cand_key[base + j] : 0u;
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t j = j0 + (uint32_t)(u * T_s);
-                    if (j < cs) {
-                        if (refine) {
-                            const uint32_t d = L.sbase[gg] + j;
-                            if (small) { L.ck[d] = kk[u]; L.ci[d] = ii[u]; }
-                            else { W.flat_key[d] = kk[u]; W.flat_idx[d] = ii[u]; }
-                        }
-                    } else if (j < cnt) {
-                        const uint32_t d = L.lbase[gg] + (j - cs);
-                        if (d < (uint32_t)kTopkMaxK) L.sel[d] = (int32_t)ii[u];
-                    }
-                }
+    // 2. place the runs: the speculative entries first, then whatever lies past them
+    auto place = [&](int gg, uint32_t j, uint32_t kv, uint32_t iv) {
+        const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
+        if (j < cs) {
+            if (refine) {
+                const uint32_t d = L.sbase[gg] + j;
+                if (small) { L.ck[d] = kv; L.ci[d] = iv; }
+                else { W.flat_key[d] = kv; W.flat_idx[d] = iv; }
             }
+        } else if (j < cnt) {
+            const uint32_t d = L.lbase[gg] + (j - cs);
+            if (d < (uint32_t)kTopkMaxK) L.sel[d] = (int32_t)iv;
+        }
+    };
+    if (g0 < R.nseg) {
+#pragma unroll
+        for (int u = 0; u < kSpec; ++u) place(g0, (uint32_t)(r + u * T_s), kk[u], ii[u]);
+    }
+    for (int gg = g0; gg < R.nseg; gg += par) {
+        const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
+        const uint32_t base = (uint32_t)gg * kFilterChunk;
+        const uint32_t jstart = (uint32_t)r + (gg == g0 ? (uint32_t)(kSpec * T_s) : 0u);
+        for (uint32_t j0 = jstart; j0 < cnt; j0 += 8u * (uint32_t)T_s) {
+            uint32_t k8[8], i8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t j = j0 + (uint32_t)(u * T_s);
+                i8[u] = j < cnt ? W.cand_idx[base + j] : 0u;
+                k8[u] = (refine && j < cs) ? W.cand_key[base + j] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) place(gg, j0 + (uint32_t)(u * T_s), k8[u], i8[u]);
         }
     }
     __syncthreads();
