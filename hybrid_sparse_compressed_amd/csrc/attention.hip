@@ -126,7 +126,8 @@ constexpr int kModeDecode = 0, kModePrefill = 1, kModeFused = 2;
 
 // LDS the select prologue of the fused mode carves out of the tile buffers
 constexpr size_t kSelLdsBytes = (size_t)sel::kBins * 4 + (2 * sel::kSelNW + 2) * 4 + 3 * (size_t)sel::kMaxSeg * 4 +
-                                2 * (size_t)sel::kCandCap * 4 + 2 * (size_t)kTopkMaxK * 4 + 16;
+                                2 * (size_t)sel::kCandCap * 4 + 2 * (size_t)kTopkMaxK * 4 + 16 +
+                                3 * (size_t)sel::kSelThreads * 4 + (size_t)sel::kCandCap;
 __device__ inline sel::SelLds sel_lds_at(unsigned char* base) {
     sel::SelLds L;
     uint32_t* p = reinterpret_cast<uint32_t*>(base);
@@ -139,7 +140,9 @@ __device__ inline sel::SelLds sel_lds_at(unsigned char* base) {
     L.sel = reinterpret_cast<int32_t*>(p); p += kTopkMaxK;
     L.chs = reinterpret_cast<int32_t*>(p); p += kTopkMaxK;
     L.misc = p; p += 4;
-    L.tmp = p;
+    L.mem = p; p += 3 * sel::kSelThreads;
+    L.tmp = p; p += 2 * sel::kSelNW + 2;
+    L.flag = reinterpret_cast<uint8_t*>(p);
     return L;
 }
 

@@ -425,10 +425,12 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
     __shared__ uint32_t ck[kCandCap], ci[kCandCap];
     __shared__ int32_t selv[kTopkMaxK], chs[kTopkMaxK];
     __shared__ uint32_t misc[4];
+    __shared__ uint32_t mem[3 * kThreads];
+    __shared__ uint8_t flag[kCandCap];
 
     const int q = blockIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
-    const SelLds L = {h, tmp, segc, sbase, lbase, ck, ci, selv, chs, misc};
+    const SelLds L = {h, tmp, segc, sbase, lbase, ck, ci, selv, chs, misc, mem, flag};
     const SelResult R = select_query(W, clamp_n(n_cand, q, S_max), S_max, k, k, L);
     select_write_sorted(L, R, out + (size_t)q * k, k);
     __syncthreads();

@@ -148,6 +148,8 @@ struct SelLds {
     int32_t* sel;     // [kTopkMaxK] selected indices, ascending
     int32_t* chs;     // [kTopkMaxK] chosen short-list indices, ascending
     uint32_t* misc;   // [4]
+    uint32_t* mem;    // [3 * kSelThreads] crossing-bucket members: position, key, index
+    uint8_t* flag;    // [kCandCap] chosen flags of crossing-bucket members
 };
 
 struct SelResult {
@@ -160,10 +162,14 @@ struct SelResult {
 };
 
 // Gathers the selected list (ascending, all of it) and, when positions past
-// it are needed (j_need > its length), the short list, then finds the k-th key from the second-digit histogram (plus one 10-bit pass
-// over its bucket unless the bucket is taken whole, plus three passes over
-// complemented indices when a tie straddles rank k) and compacts the chosen
-// short-list entries in order.  The result lists are L.sel[0..nsel) and
+// it are needed (j_need > its length), the short list, then resolves the
+// short list from the second-digit histogram: buckets above the crossing
+// bucket are taken, and the crossing bucket is taken whole, or its members
+// (at most kSelThreads of them, short list in LDS) are ranked directly under
+// (key desc, index asc), or else one 10-bit pass gives the k-th key and three
+// passes over complemented indices settle a tie that straddles rank k.  The
+// chosen short-list entries are then compacted in order.  The result lists
+// are L.sel[0..nsel) and
 // L.chs[0..nch), both ascending; the first take = nsel + nch entries of the
 // query's top-k are their union.  Short lists longer than kCandCap go through
 // W.flat_key / W.flat_idx (every caller that reaches that path writes the
@@ -264,24 +270,52 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
     R.nch = 0;
     if (!refine) return R;
 
-    // 3. the k-th key and how many of its ties are taken
+    // 3. the crossing bucket of the second digit and how much of it is taken
     const uint32_t* key = small ? L.ck : W.flat_key;
     const uint32_t* idx = small ? L.ci : W.flat_idx;
     const int nc = R.nc;
     uint32_t* h = L.h;
-    bool whole;
+    bool whole, direct = false;
     uint32_t p2, T, imax = 0xffffffffu;
     {
         const uint32_t p1 = key[0] & 0xffe00000u;  // the threshold bin's 11 bits
         int rem;
         const int d2 = find_crossing<kBins>(h, need, L.tmp, &rem);
         p2 = p1 | ((uint32_t)d2 << 10);
-        // the whole bucket is taken: no tie to break (read by all before h is reused)
-        whole = (int)h[d2] == rem;
+        // read by all before h is reused
+        const uint32_t members = h[d2];
+        whole = (int)members == rem;
+        if (tid == 0) L.misc[1] = 0;
         __syncthreads();
         need = rem;
         T = p2;
-        if (!whole) {
+        if (!whole && small && members <= (uint32_t)kSelThreads) {
+            // rank the bucket's members directly: (key desc, index asc)
+            direct = true;
+            uint32_t* mpos = L.mem;
+            uint32_t* mkey = L.mem + kSelThreads;
+            uint32_t* midx = L.mem + 2 * kSelThreads;
+            for (int i = tid; i < nc; i += kSelThreads) {
+                const uint32_t kk = key[i];
+                if ((kk & 0xfffffc00u) == p2) {
+                    const uint32_t slot = atomicAdd(&L.misc[1], 1u);
+                    mpos[slot] = (uint32_t)i;
+                    mkey[slot] = kk;
+                    midx[slot] = idx[i];
+                }
+            }
+            __syncthreads();
+            if (tid < (int)members) {
+                const uint32_t mk = mkey[tid], mi = midx[tid];
+                uint32_t rank = 0;
+                for (uint32_t j = 0; j < members; ++j) {
+                    const uint32_t kj = mkey[j];
+                    rank += (kj > mk) || (kj == mk && midx[j] < mi);
+                }
+                L.flag[mpos[tid]] = rank < (uint32_t)need ? 1 : 0;
+            }
+            __syncthreads();
+        } else if (!whole) {
             const int d3 = radix_digit<1024>(key, nc, 0xfffffc00u, p2, 0, nullptr, 0u, need, h, L.tmp, &rem);
             need = rem;
             T = p2 | (uint32_t)d3;
@@ -322,7 +356,9 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
         const int i0 = min(nc, tid * E), i1 = min(nc, i0 + E);
         auto chosen = [&](int i) {
             const uint32_t kk = key[i];
-            return whole ? (kk >= p2) : (kk > T || (kk == T && idx[i] <= imax));
+            if (whole) return kk >= p2;
+            if (direct) return kk >= p2 + 1024u || ((kk & 0xfffffc00u) == p2 && L.flag[i] != 0);
+            return kk > T || (kk == T && idx[i] <= imax);
         };
         uint32_t cnt = 0;
         for (int i = i0; i < i1; ++i) cnt += chosen(i);
