@@ -83,7 +83,11 @@ int hsa_profile_enable(unsigned family_mask) {
     if (family_mask != 0 && s.ev.empty()) {
         s.ev.resize(2 * hsa::kPool);
         for (auto& e : s.ev)
-            if (hipEventCreate(&e) != hipSuccess) return HSA_ERR_HIP;
+            // timing only: no system-scope fence (cache write-back and
+            // invalidate) when the event is recorded, so the pair brackets
+            // the kernel and not the fence
+            if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess)
+                return HSA_ERR_HIP;
         for (int i = hsa::kPool - 1; i >= 0; --i) s.free_slots.push_back(i);
     }
     hsa::g_mask.store(family_mask, std::memory_order_relaxed);
