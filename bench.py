@@ -12,6 +12,11 @@ just-completed 4-token blocks (hsa_compress).  Two copies of the
 indexer inputs alternate between steps so the 268 MB key stream is larger
 than the on-die cache across a pair of steps.
 
+After the metric, "rows" measures every other row of the path at its own
+full-size workload (compressor, prefill indexer + top-k and prefill attention
+at prefill_32k, dense C128 decode, fused sparse decode at c4_decode_64k), each
+against its own roofline; --no-rows skips them.
+
 Prints ONE JSON line (rank 0).  --gpus N > 1 is not supported: the path is
 measured on one GPU.
 """
@@ -38,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time over which the oracle layer-step is repeated")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-row measurements at the other workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warm-up, run three plain device copies of this many MiB, so that "
                          "a hardware byte counter can be scaled by a transfer of known size")
@@ -198,9 +205,101 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_rows:
+        res["rows"] = other_rows(hsa, workloads)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def _median_us(torch, fn, reps):
+    """Median wall time of fn() on the current stream, in microseconds (one warm-up call)."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1000.0)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def _row(workload, us, bound, alg, unit, peak, **extra):
+    if unit == "GB/s":
+        achieved = alg / (us * 1e-6) / 1e9
+    else:  # TFLOP/s
+        achieved = alg / (us * 1e-6) / 1e12
+    r = {"workload": workload, "us": round(us, 2), "bound": bound, "alg": alg,
+         "achieved": round(achieved, 1), "unit": unit, "peak": peak,
+         "frac": round(achieved / peak, 4)}
+    r.update(extra)
+    return r
+
+
+def other_rows(hsa, workloads):
+    """Each row of the path at its own full-size workload (whole calls, median of a few):
+    the compressor and the prefill chain at prefill_32k (compress -> indexer + top-k over
+    16,384 queries -> prefill attention over their own top-512), the dense C128 decode at
+    c128_dense_decode, and the fused sparse decode at c4_decode_64k."""
+    import torch
+
+    rows = {}
+    w = workloads.prefill("cuda")
+    n_seq, T, D = 8, 32768, 576
+    c4 = torch.empty((n_seq, T // 4, D), dtype=torch.bfloat16, device="cuda")
+    c128 = torch.empty((n_seq, T // 128, D), dtype=torch.bfloat16, device="cuda")
+    # each call reads x and its gate once and writes the entries once
+    for m, g, b, out, key in ((4, w["gate4"], w["bias4"], c4, "a1_compress_c4"),
+                              (128, w["gate128"], w["bias128"], c128, "a1_compress_c128")):
+        us = _median_us(torch, lambda: hsa.hsa_compress(w["x"], g, b, m, out=out), 7)
+        alg = 2 * n_seq * T * D * 2 + m * D * 2 + n_seq * (T // m) * D * 2
+        rows[key] = _row("prefill_32k", us, "hbm", alg, "GB/s", HBM_PEAK_GBPS)
+    Nq, S, k = 16384, T // 4, 512
+    scores = torch.empty((Nq, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((Nq, k), dtype=torch.int32, device="cuda")
+    us = _median_us(torch, lambda: hsa.hsa_index_topk(w["q_idx"], w["k_idx"], w["n_cand"], k,
+                                                      q_seq=w["q_seq"], scores=scores,
+                                                      topk_idx=idx), 5)
+    # q_I read once, K_I once, the indices written once (the fp32 score round trip,
+    # 2 x 536.9 MB, is the implementation's and not counted)
+    alg = Nq * 64 * 128 * 2 + n_seq * S * 128 * 2 + Nq * k * 4
+    n_cand = w["n_cand"].double().sum().item()
+    rows["a2_a3_index_topk"] = _row("prefill_32k", us, "hbm", alg, "GB/s", HBM_PEAK_GBPS,
+                                    queries=Nq, per_head_tflop=round(n_cand * 64 * 128 * 2 / 1e12, 3))
+    out = torch.empty((n_seq, 2048, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((n_seq, 2048, 64), dtype=torch.float32, device="cuda")
+    us = _median_us(torch, lambda: hsa.hsa_attn_prefill(w["q"], w["x"], c4, w["q_start"], 128, 4,
+                                                        w["scale"], 512, comp_idx=idx, out=out,
+                                                        lse=lse), 3)
+    flop = Nq * 64 * (128 + k) * (576 + 512) * 2
+    rows["a5_prefill_attention"] = _row("prefill_32k", us, "mfma", flop, "TFLOP/s", 2500.0)
+    del w, c4, c128, scores, idx, out, lse
+    torch.cuda.empty_cache()
+
+    d = workloads.c128_dense_decode("cuda")
+    lens = d["lengths"]
+    alg = sum((128 + L // 128) * 1152 + 139264 for L in lens)
+    us = _median_us(torch, lambda: hsa.hsa_attn_decode(d["q"], d["swa_kv"], d["swa_len"],
+                                                       d["comp_kv"], d["comp_len"], d["scale"],
+                                                       512), 21)
+    rows["a4_dense_decode_c128"] = _row("c128_dense_decode", us, "hbm", alg, "GB/s",
+                                        HBM_PEAK_GBPS)
+    del d
+    e = workloads.c4_decode("c4_decode_64k", "cuda")
+    us = _median_us(torch, lambda: hsa.hsa_decode_sparse(e["q_idx"], e["k_idx"], e["n_cand"], 512,
+                                                         e["q"], e["swa_kv"], e["swa_len"],
+                                                         e["comp_kv"], e["comp_len"], e["scale"],
+                                                         512), 21)
+    rows["a2_a3_a4_decode_c4_64k"] = _row("c4_decode_64k", us, "hbm", 5089280, "GB/s",
+                                          HBM_PEAK_GBPS)
+    del e
+    torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(w, min_seconds):

@@ -22,9 +22,12 @@
 //      running statistics; P^T goes to LDS in bf16 (fp32 for fp32 inputs);
 //   4. O^T += V^T * P^T on MFMA over the 64 rows, wave w owning value
 //      channels [w*d_v/4, (w+1)*d_v/4), accumulating O^T in fp32.
-// Decode splits the rows of a sequence over several workgroups and merges
-// their (max, sum, O) partials in a second kernel, in a fixed order; prefill
-// gives each query position its own workgroup.
+// The rows of the next tile are loaded into registers while the current
+// tile is computed.  Decode splits the rows of a sequence over several
+// workgroups and merges their (max, sum, O) partials in a second kernel, in a
+// fixed order; prefill gives each (query position, head block) its own
+// workgroup, the head blocks of a query dispatched back to back on one XCD so
+// that they gather the same rows through one L2.
 //
 // Fused sparse decode (the whole C4 layer-step after the filter kernel): a
 // workgroup with compressed rows first finishes its sequence's top-k select
@@ -100,6 +103,7 @@ struct AttnArgs {
     float* part_o;        //                  outputs    [B][n_split][H][d_v]
     int H, W, S_max, k, m, T_len, n_q, q_start;
     int rows_per_split, n_split, max_rows;
+    int hblocks, n_queries;  // prefill: head blocks per query, queries in the grid
     float scale_log2;     // scale * log2(e)
 };
 
@@ -173,16 +177,27 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int hl = lane & 15, quad = lane >> 4;
-    const int hb = blockIdx.z;
+    int hb = blockIdx.z;
+    int pq = 0;  // prefill: query (sequence-major)
+    if constexpr (PREFILL) {
+        // Workgroup L runs on XCD L % 8.  Among one XCD's workgroups the head
+        // blocks of a query come one after another, and consecutive queries
+        // of that XCD are 8 positions apart: rows shared by them (the head
+        // blocks' whole lists, neighbouring windows) meet in one L2.
+        const int L = (int)blockIdx.x, s8 = L / 8;
+        hb = s8 % a.hblocks;
+        pq = (s8 / a.hblocks) * 8 + L % 8;
+        if (pq >= a.n_queries) return;
+    }
     const int head = hb * kHeadsPerWG + hl;
     const bool head_ok = head < a.H;
 
     // sequence / query identity and row range
     int b, qpos = 0, qid = 0, vr0, vr1;
     if constexpr (PREFILL) {
-        const int i = blockIdx.x;
-        b = blockIdx.y;
-        qid = b * a.n_q + i;
+        const int i = pq % a.n_q;
+        b = pq / a.n_q;
+        qid = pq;
         qpos = a.q_start + i;
         vr0 = 0;
         vr1 = a.max_rows;
@@ -309,6 +324,27 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     const T* win = reinterpret_cast<const T*>(a.win);
     const T* comp = reinterpret_cast<const T*>(a.comp);
 
+    // gather registers: a thread moves chunk `ch` of the row pair (2rp, 2rp+1)
+    // of a tile; the next tile's rows are loaded while this one is computed
+    constexpr int kUnits = (kTile / 2) * CPR;
+    constexpr int kIter = (kUnits + kAttnThreads - 1) / kAttnThreads;
+    u32x4 ga[kIter], gb[kIter];
+    auto issue = [&](int tb) {
+#pragma unroll
+        for (int it = 0; it < kIter; ++it) {
+            const int u = tid + it * kAttnThreads;
+            const int rp = u % (kTile / 2), ch = u / (kTile / 2);
+            ga[it] = gb[it] = u32x4{0u, 0u, 0u, 0u};
+            if (u < kUnits) {
+                const long long oa = row_off[tb + 2 * rp], ob = row_off[tb + 2 * rp + 1];
+                if (oa >= 0)
+                    ga[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp] ? comp : win) + oa + (long long)ch * V16);
+                if (ob >= 0)
+                    gb[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp + 1] ? comp : win) + ob + (long long)ch * V16);
+            }
+        }
+    };
+
     for (int c0 = vr0; c0 < vr1; c0 += kChunkRows) {
         const int c1 = min(vr1, c0 + kChunkRows);
         // ---- row list of this chunk: one thread per virtual row
@@ -324,28 +360,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         if (row_off[tid] >= 0) tile_any[tid / kTile] = 1;  // benign race: all write 1
         __syncthreads();
 
+    int pre = -1;  // tile (offset in the chunk) whose rows are in flight in ga/gb
     for (int t0 = c0; t0 < c1; t0 += kTile) {
         const int tb = t0 - c0;
         if (!tile_any[tb / kTile]) continue;  // uniform: nothing valid in this tile
-        // ---- gather: a thread moves chunk `ch` of the row pair (2rp, 2rp+1);
-        // K goes row-major, V transposed with the two rows packed in one write
-        // (consecutive lanes -> consecutive words: no bank conflicts)
-        constexpr int kUnits = (kTile / 2) * CPR;
-        constexpr int kIter = (kUnits + kAttnThreads - 1) / kAttnThreads;
-        u32x4 ga[kIter], gb[kIter];
-#pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-            const int u = tid + it * kAttnThreads;
-            const int rp = u % (kTile / 2), ch = u / (kTile / 2);
-            ga[it] = gb[it] = u32x4{0u, 0u, 0u, 0u};
-            if (u < kUnits) {
-                const long long oa = row_off[tb + 2 * rp], ob = row_off[tb + 2 * rp + 1];
-                if (oa >= 0)
-                    ga[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp] ? comp : win) + oa + (long long)ch * V16);
-                if (ob >= 0)
-                    gb[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp + 1] ? comp : win) + ob + (long long)ch * V16);
-            }
-        }
+        // ---- gather: K goes row-major, V transposed with the two rows packed
+        // in one write (consecutive lanes -> consecutive words: no bank conflicts)
+        if (pre != tb) issue(tb);
 #pragma unroll
         for (int it = 0; it < kIter; ++it) {
             const int u = tid + it * kAttnThreads;
@@ -361,6 +382,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             }
         }
         __syncthreads();
+        // the next tile of this chunk with valid rows goes out now
+        pre = -1;
+        for (int nb = tb + kTile; nb < c1 - c0; nb += kTile) {
+            if (tile_any[nb / kTile]) {
+                issue(nb);
+                pre = nb;
+                break;
+            }
+        }
 
         // ---- S^T for this wave's rows 16*wave + 4*quad + r, head `hl`; two
         // accumulation chains (even / odd steps) halve the dependent latency
@@ -790,7 +820,11 @@ hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const v
     a.rows_per_split = a.max_rows;
     a.n_split = 1;
     a.scale_log2 = scale * kLog2e;
-    dim3 grid((unsigned)n_q, (unsigned)n_seq, (unsigned)ceil_div(H, kHeadsPerWG));
+    a.hblocks = ceil_div(H, kHeadsPerWG);
+    a.n_queries = n_seq * n_q;
+    const long long nwg = (long long)ceil_div(a.n_queries, 8) * 8 * a.hblocks;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)nwg, 1u, 1u);
     return dispatch_attn<kModePrefill>(dtype, d_qk, d_v, a, grid, st);
 }
 
