@@ -27,7 +27,9 @@
 // workgroups and merges their (max, sum, O) partials in a second kernel, in a
 // fixed order; prefill gives each (query position, head block) its own
 // workgroup, the head blocks of a query dispatched back to back on one XCD so
-// that they gather the same rows through one L2.
+// that they gather the same rows through one L2.  For the 64-head bf16
+// latent-576 shape, prefill64_kernel instead gives a query's 64 heads one
+// 8-wave workgroup that gathers each tile once.
 //
 // Fused sparse decode (the whole C4 layer-step after the filter kernel): a
 // workgroup with compressed rows first finishes its sequence's top-k select
@@ -558,6 +560,275 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         a.lse[orow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
+// ---- prefill with all heads of a query in one workgroup --------------------
+//
+// bf16, latent 576 / value 512, 64 heads.  A workgroup (8 waves) owns one
+// query position and every head, so each 64-row tile is gathered into LDS
+// once for all 64 heads.  Wave w takes head block w % 4 (16 heads, one MFMA
+// column block) and half w / 4 of the work: tile rows 32*half..+31 in the QK
+// product and value channels 256*half..+255 in the PV product.  The two waves
+// of a head block meet in LDS for the per-head (max, sum) of the tile; the
+// rest is the tile pipeline of attn_kernel (same operand layouts).  Rows are
+// listed 512 at a time as device addresses (0: not a row of this query), and
+// the next tile's rows are loaded into registers while a tile is computed.
+constexpr int kP64Threads = 512;
+constexpr int kP64Waves = kP64Threads / kWave;
+constexpr int kP64Heads = 64;
+constexpr int kP64Rows = 64;                    // rows per tile
+constexpr int kP64Chunk = kP64Threads;          // rows listed at once (one per thread)
+
+template <int DQK, int DV> struct P64Lds {
+    static constexpr int kSkew = 8;             // 16 bytes of bf16
+    static constexpr int kStrideK = DQK + kSkew;
+    static constexpr int kStrideT = kP64Rows + kSkew;
+    static constexpr size_t kOffV = (size_t)kP64Rows * kStrideK;
+    static constexpr size_t kOffP = kOffV + (size_t)DV * kStrideT;
+    static constexpr size_t kBytes = (kOffP + (size_t)kP64Heads * kStrideT) * sizeof(bf16_t);
+};
+
+// the two bf16 halves x of chunks a and b as one word (a low, b high)
+__device__ __forceinline__ uint32_t pair_word(const u32x4& a, const u32x4& b, int x) {
+    return (x & 1) ? __builtin_amdgcn_perm(b[x >> 1], a[x >> 1], 0x07060302u)
+                   : __builtin_amdgcn_perm(b[x >> 1], a[x >> 1], 0x05040100u);
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
+    typedef bf16_t T;
+    typedef P64Lds<DQK, DV> L;
+    typedef Mma<T> M;
+    constexpr int V16 = 8;                          // bf16 per 16-byte chunk
+    constexpr int CPR = DQK / V16;                  // chunks per row
+    constexpr int NKK = DQK / M::kK;                // MFMA steps of the QK product
+    constexpr int DW = DV / 2;                      // value channels per wave
+    constexpr int NMT = DW / 16;                    // O^T row tiles per wave
+    static_assert(DQK % M::kK == 0 && DV % 32 == 0 && DV <= DQK, "unsupported head dims");
+    static_assert(kP64Waves == 8 && kP64Heads == 4 * 16, "wave split");
+
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    T* Ks = reinterpret_cast<T*>(lds_raw);
+    T* Vt = Ks + L::kOffV;
+    T* Pt = Ks + L::kOffP;
+    __shared__ const T* row_ptr[kP64Chunk];        // row address, nullptr: no row
+    __shared__ int tile_any[kP64Chunk / kP64Rows];
+    __shared__ float red_m[2][kP64Heads], red_s[2][kP64Heads];
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int hb = wave & 3, half = wave >> 2;
+    const int hl = lane & 15, quad = lane >> 4;
+    const int head = hb * 16 + hl;
+    const bool head_ok = head < a.H;
+
+    // queries go to XCDs in contiguous ranges (workgroup L runs on XCD L % 8),
+    // so the windows of neighbouring positions meet in one L2
+    const int nq8 = ceil_div(a.n_queries, 8);
+    const int pq = ((int)blockIdx.x % 8) * nq8 + (int)blockIdx.x / 8;
+    if (pq >= a.n_queries) return;
+    const int b = pq / a.n_q;
+    const int qpos = a.q_start + pq % a.n_q;
+    int n_comp = (qpos + 1) / a.m;
+    n_comp = n_comp < a.S_max ? n_comp : a.S_max;
+    const int vr1 = a.max_rows;
+
+    const T* win = reinterpret_cast<const T*>(a.win);
+    const T* comp = reinterpret_cast<const T*>(a.comp);
+    auto row_at = [&](int vr) -> const T* {
+        if (vr >= vr1) return nullptr;
+        if (vr < a.W) {
+            const int tok = qpos - a.W + 1 + vr;
+            return tok >= 0 ? win + ((size_t)b * a.T_len + tok) * DQK : nullptr;
+        }
+        const int j = vr - a.W;
+        int ci;
+        if (a.comp_idx)
+            ci = j < a.k ? a.comp_idx[(size_t)pq * a.k + j] : -1;
+        else
+            ci = j;
+        return (ci >= 0 && ci < n_comp) ? comp + ((size_t)b * a.S_max + ci) * DQK : nullptr;
+    };
+    const T* first_row = row_at(tid);  // index loads before the Q loads
+
+    typename M::frag qf[NKK];
+    {
+        const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)pq * a.H + (head_ok ? head : 0)) * DQK;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qrow + kk * M::kK + quad * 8)
+                              : u32x4{0u, 0u, 0u, 0u};
+            qf[kk] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[NMT];
+#pragma unroll
+    for (int t = 0; t < NMT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // gather: thread moves chunk ch of the row pair (2rp, 2rp+1) of a tile
+    constexpr int kUnits = (kP64Rows / 2) * CPR;
+    constexpr int kIter = (kUnits + kP64Threads - 1) / kP64Threads;
+    u32x4 ga[kIter], gb[kIter];
+    auto issue = [&](int tb) {
+#pragma unroll
+        for (int it = 0; it < kIter; ++it) {
+            const int u = tid + it * kP64Threads;
+            const int rp = u % (kP64Rows / 2), ch = u / (kP64Rows / 2);
+            ga[it] = gb[it] = u32x4{0u, 0u, 0u, 0u};
+            if (u < kUnits) {
+                const T* pa = row_ptr[tb + 2 * rp];
+                const T* pb = row_ptr[tb + 2 * rp + 1];
+                if (pa) ga[it] = *reinterpret_cast<const u32x4*>(pa + ch * V16);
+                if (pb) gb[it] = *reinterpret_cast<const u32x4*>(pb + ch * V16);
+            }
+        }
+    };
+
+    for (int c0 = 0; c0 < vr1; c0 += kP64Chunk) {
+        const int c1 = min(vr1, c0 + kP64Chunk);
+        {
+            const T* p = c0 == 0 ? first_row : row_at(c0 + tid);
+            row_ptr[tid] = p;
+        }
+        if (tid < kP64Chunk / kP64Rows) tile_any[tid] = 0;
+        __syncthreads();
+        if (row_ptr[tid] != nullptr) tile_any[tid / kP64Rows] = 1;  // benign race: all write 1
+        __syncthreads();
+
+        int pre = -1;
+        for (int t0 = c0; t0 < c1; t0 += kP64Rows) {
+            const int tb = t0 - c0;
+            if (!tile_any[tb / kP64Rows]) continue;  // uniform
+            if (pre != tb) issue(tb);
+#pragma unroll
+            for (int it = 0; it < kIter; ++it) {
+                const int u = tid + it * kP64Threads;
+                const int rp = u % (kP64Rows / 2), ch = u / (kP64Rows / 2);
+                if (u < kUnits) {
+                    *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp) * L::kStrideK + ch * V16) = ga[it];
+                    *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp + 1) * L::kStrideK + ch * V16) = gb[it];
+                    if (ch * V16 < DV) {
+#pragma unroll
+                        for (int x = 0; x < V16; ++x)
+                            *reinterpret_cast<uint32_t*>(Vt + (size_t)(ch * V16 + x) * L::kStrideT + 2 * rp) =
+                                pair_word(ga[it], gb[it], x);
+                    }
+                }
+            }
+            __syncthreads();
+            pre = -1;
+            for (int nb = tb + kP64Rows; nb < c1 - c0; nb += kP64Rows) {
+                if (tile_any[nb / kP64Rows]) {
+                    issue(nb);
+                    pre = nb;
+                    break;
+                }
+            }
+
+            // ---- S^T for rows 32*half + 16*rb + 4*quad + r, head hl
+            f32x4 s[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                f32x4 e0 = f32x4{0.f, 0.f, 0.f, 0.f}, e1 = f32x4{0.f, 0.f, 0.f, 0.f};
+                const T* krow = Ks + (size_t)(32 * half + 16 * rb + hl) * L::kStrideK;
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(krow + kk * M::kK + quad * 8);
+                    if (kk & 1)
+                        e1 = M::mma(__builtin_bit_cast(bf16x8, v), qf[kk], e1);
+                    else
+                        e0 = M::mma(__builtin_bit_cast(bf16x8, v), qf[kk], e0);
+                }
+                s[rb] = e0 + e1;
+            }
+
+            // ---- online softmax (base 2) over this wave's 32 rows, then the
+            // two halves of the head block meet in LDS
+            float x[8];
+            float wmax = -INFINITY;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 32 * half + 16 * rb + 4 * quad + r;
+                    const float v = row_ptr[tb + row] != nullptr ? s[rb][r] * a.scale_log2 : -INFINITY;
+                    x[4 * rb + r] = v;
+                    wmax = fmaxf(wmax, v);
+                }
+            }
+            wmax = fmaxf(wmax, __shfl_xor(wmax, 16, kWave));
+            wmax = fmaxf(wmax, __shfl_xor(wmax, 32, kWave));
+            float p[8];
+            float wsum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                p[r] = wmax == -INFINITY ? 0.f : exp2f(x[r] - wmax);
+                wsum += p[r];
+            }
+            wsum += __shfl_xor(wsum, 16, kWave);
+            wsum += __shfl_xor(wsum, 32, kWave);
+            if (quad == 0) {
+                red_m[half][head] = wmax;
+                red_s[half][head] = wsum;
+            }
+            __syncthreads();
+            const float tmax = fmaxf(red_m[0][head], red_m[1][head]);
+            const bool move = tmax > m_run + 8.f;   // lazy rescale, p stays <= 2^8
+            const float m_new = move ? tmax : m_run;
+            const float alpha = move ? exp2f(m_run - m_new) : 1.f;
+            float tsum = 0.f;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const float mw = red_m[h2][head];
+                if (mw != -INFINITY) tsum += red_s[h2][head] * exp2f(mw - m_new);
+            }
+            const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(p[4 * rb] * sc) | ((uint32_t)f32_to_bf16(p[4 * rb + 1] * sc) << 16);
+                pk.y = (uint32_t)f32_to_bf16(p[4 * rb + 2] * sc) | ((uint32_t)f32_to_bf16(p[4 * rb + 3] * sc) << 16);
+                *reinterpret_cast<uint2*>(Pt + (size_t)head * L::kStrideT + 32 * half + 16 * rb + 4 * quad) = pk;
+            }
+            if (__ballot(move && l_run > 0.f)) {
+#pragma unroll
+                for (int t = 0; t < NMT; ++t) acc[t] *= alpha;
+            }
+            l_run = l_run * alpha + tsum;
+            m_run = m_new;
+            __syncthreads();
+
+            // ---- O^T[channels 256*half + 16t.., head] += V^T * P^T
+            const T* vbase = Vt + (size_t)(half * DW + hl) * L::kStrideT;
+            const T* pbase = Pt + (size_t)head * L::kStrideT;
+#pragma unroll
+            for (int ks = 0; ks < kP64Rows / 32; ++ks) {
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pbase + ks * 32 + quad * 8));
+#pragma unroll
+                for (int t = 0; t < NMT; ++t) {
+                    const u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + (size_t)t * 16 * L::kStrideT + ks * 32 + quad * 8);
+                    acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv), pf, acc[t]);
+                }
+            }
+            __syncthreads();  // the tile buffers are rewritten next
+        }
+    }
+
+    // ---- epilogue.  acc[t][r] = O^T[256*half + 16t + 4quad + r][head]
+    if (!head_ok) return;
+    const size_t orow = (size_t)pq * a.H + head;
+    T* o = reinterpret_cast<T*>(a.out) + orow * DV + half * DW;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int t = 0; t < NMT; ++t) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(acc[t][0] * inv) | ((uint32_t)f32_to_bf16(acc[t][1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(acc[t][2] * inv) | ((uint32_t)f32_to_bf16(acc[t][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(o + t * 16 + quad * 4) = pk;
+    }
+    if (a.lse && half == 0 && quad == 0)
+        a.lse[orow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
 // Merge the split partials of one (sequence, head) in a fixed split order.
 // All (max, sum) pairs are loaded at once, the weights go through LDS, and
 // each thread then issues the loads of its 4 channels for every split before
@@ -820,8 +1091,25 @@ hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const v
     a.rows_per_split = a.max_rows;
     a.n_split = 1;
     a.scale_log2 = scale * kLog2e;
+    if ((long long)n_seq * n_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     a.hblocks = ceil_div(H, kHeadsPerWG);
     a.n_queries = n_seq * n_q;
+    if (dtype == kBF16 && d_qk == 576 && d_v == 512 && H == kP64Heads) {
+        constexpr size_t lds = P64Lds<576, 512>::kBytes;
+        static bool attr_set = false;  // raise the dynamic-LDS limit once
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill64_kernel<576, 512>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        const long long nwg = (long long)ceil_div(a.n_queries, 8) * 8;
+        if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        ProfScope prof(kProfAttn, st);
+        hipLaunchKernelGGL((prefill64_kernel<576, 512>), dim3((unsigned)nwg), dim3(kP64Threads), lds,
+                           st, a);
+        return hipGetLastError();
+    }
     const long long nwg = (long long)ceil_div(a.n_queries, 8) * 8 * a.hblocks;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)nwg, 1u, 1u);

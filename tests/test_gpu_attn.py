@@ -154,6 +154,22 @@ def test_prefill_small(oracle, dt, d_qk, d_v, H, sparse):
     compare(lse, rl, TOL_FP32 if dt == torch.float32 else (1e-3, 1e-4), "prefill lse")
 
 
+def test_prefill_dense_many_chunks(oracle):
+    """Dense prefill with over a thousand visible compressed rows per query: the row
+    list of a query is built in several chunks."""
+    g = torch.Generator().manual_seed(123)
+    n_seq, T, n_q, W, m, H = 1, 4400, 6, 128, 4, 64
+    q_start = T - n_q
+    q = _rand((n_seq, n_q, H, 576), torch.bfloat16, g)
+    kv = _rand((n_seq, T, 576), torch.bfloat16, g)
+    comp = _rand((n_seq, T // m, 576), torch.bfloat16, g)
+    note("prefill dense many chunks")
+    o, lse = _prefill(q, kv, comp, q_start, W, m, 0.04, 512, None)
+    ro, rl = oracle.attn_prefill(q, kv, comp, q_start, W, m, 0.04, 512)
+    compare(o.reshape(n_seq * n_q, H, 512), ro, TOL_BF16, "prefill dense chunks out")
+    compare(lse, rl, (1e-3, 1e-4), "prefill dense chunks lse")
+
+
 def test_prefill_window_start(oracle):
     """Queries at positions 0..39: windows shorter than W, few visible blocks."""
     g = torch.Generator().manual_seed(99)
