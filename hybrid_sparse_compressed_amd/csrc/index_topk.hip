@@ -277,6 +277,175 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const float* __restrict_
     }
 }
 
+// ---- many queries per sequence: scores as a matrix product on MFMA ----------
+//
+// With many queries routed to the same sequence (prefill: every query
+// position of a chunk), the scores of a sequence are one matrix product
+// qsum[q,:] . k_idx[b,s,:].  A workgroup takes 32 consecutive queries: it
+// folds their heads in fp32 (h = 0, 1, ... in order) and splits each folded
+// value exactly into three bf16 terms (hi + mid + lo, residual below 2^-26
+// of the value), so that the bf16 MFMA products carry the folded query at
+// better than fp32 precision.  Keys are staged in LDS 128 rows at a time and
+// every wave produces 16 queries x 64 keys with v_mfma_f32_16x16x32_bf16
+// (the three terms accumulated lo, mid, hi per step).  Queries of one
+// workgroup that belong to different sequences are served by one pass per
+// distinct sequence.  Equal key rows of a sequence give bitwise-equal scores.
+constexpr int kGemmQ = 32;       // queries per workgroup
+constexpr int kGemmK = 128;      // key rows per LDS block
+constexpr int kGemmMinQueries = 64;  // fewer queries: the streaming kernel
+
+__device__ __forceinline__ uint16_t bf16_bits_rn(float f) { return f32_to_bf16(f); }
+__device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_gemm_kernel(
+    const bf16_t* __restrict__ q_idx, const bf16_t* __restrict__ k_idx,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ n_cand,
+    float* __restrict__ scores, int B, int Nq, int H_I, int S_max) {
+    constexpr int NKS = D / 32;      // MFMA steps over the key width
+    constexpr int CPR = D / 8;       // 16-byte chunks per key row
+    constexpr int SK = D + 8;        // LDS row stride (elements): rows land on distinct banks
+    static_assert(D % 32 == 0 && kThreads == 256, "layout");
+    __shared__ __align__(16) uint16_t kb[kGemmK][SK];
+    __shared__ __align__(16) uint16_t qs[3][kGemmQ][SK];
+    __shared__ int s_seq[kGemmQ], s_n[kGemmQ];
+    __shared__ int s_list[kGemmQ], s_lmax[kGemmQ], s_nl;
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int hl = lane & 15, quad = lane >> 4;
+    const int q0 = blockIdx.x * kGemmQ;
+    if (tid < kGemmQ) {
+        const int q = q0 + tid;
+        int b = -1, n = 0;
+        if (q < Nq) {
+            b = q_seq ? q_seq[q] : q;
+            if (b < 0 || b >= B) b = -1;
+            else n = clamp_n(n_cand, q, S_max);
+        }
+        s_seq[tid] = b;
+        s_n[tid] = n;
+    }
+    // fold + exact three-term split: thread pair (query, 16-byte chunk)
+    for (int p = tid; p < kGemmQ * CPR; p += kThreads) {
+        const int qq = p / CPR, c = p % CPR, q = q0 + qq;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        if (q < Nq) {
+            const bf16_t* src = q_idx + (size_t)q * H_I * D + (size_t)c * 8;
+            int h = 0;
+            for (; h + 8 <= H_I; h += 8) {
+                u32x4 v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const u32x4*>(src + (size_t)(h + j) * D);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float f[8];
+                    Elem<bf16_t>::unpack(v[j], f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += f[e];
+                }
+            }
+            for (; h < H_I; ++h) {
+                float f[8];
+                Elem<bf16_t>::load16(src + (size_t)h * D, f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += f[e];
+            }
+        }
+        u32x4 hi, mid, lo;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            uint32_t wh = 0, wm = 0, wl = 0;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const float v = acc[2 * e2 + s];
+                const uint16_t bh = bf16_bits_rn(v);
+                const float r1 = v - bf16_value(bh);
+                const uint16_t bm = bf16_bits_rn(r1);
+                const float r2 = r1 - bf16_value(bm);
+                const uint16_t bl = bf16_bits_rn(r2);
+                wh |= (uint32_t)bh << (16 * s);
+                wm |= (uint32_t)bm << (16 * s);
+                wl |= (uint32_t)bl << (16 * s);
+            }
+            hi[e2] = wh; mid[e2] = wm; lo[e2] = wl;
+        }
+        *reinterpret_cast<u32x4*>(&qs[0][qq][c * 8]) = hi;
+        *reinterpret_cast<u32x4*>(&qs[1][qq][c * 8]) = mid;
+        *reinterpret_cast<u32x4*>(&qs[2][qq][c * 8]) = lo;
+    }
+    __syncthreads();
+    if (tid == 0) {  // distinct sequences of the workgroup, with their longest candidate range
+        int nl = 0;
+        for (int i = 0; i < kGemmQ; ++i) {
+            const int b = s_seq[i];
+            if (b < 0 || s_n[i] == 0) continue;
+            int j = 0;
+            while (j < nl && s_list[j] != b) ++j;
+            if (j == nl) {
+                s_list[nl] = b;
+                s_lmax[nl] = 0;
+                ++nl;
+            }
+            s_lmax[j] = max(s_lmax[j], s_n[i]);
+        }
+        s_nl = nl;
+    }
+    // wave w: queries 16*(w & 1) + hl, keys 64*(w >> 1) .. +63 of each block
+    const int qb = w & 1, kh = w >> 1;
+    bf16x8 bq[3][NKS];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            bq[t][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&qs[t][16 * qb + hl][32 * ks + 8 * quad]));
+    __syncthreads();
+    const int my_q = 16 * qb + hl;
+    const int my_seq = s_seq[my_q], my_n = s_n[my_q];
+    float* my_row = scores + (size_t)(q0 + my_q) * S_max;
+    const bool vec_ok = (S_max & 3) == 0;
+    const int nl = s_nl;
+    for (int li = 0; li < nl; ++li) {
+        const int bs = s_list[li], nmax = s_lmax[li];
+        const bf16_t* kseq = k_idx + (size_t)bs * S_max * D;
+        for (int k0 = 0; k0 < nmax; k0 += kGemmK) {
+            // stage key rows k0 .. k0+127 (rows past S_max read as zero)
+            for (int p = tid; p < kGemmK * CPR; p += kThreads) {
+                const int r = p / CPR, c = p % CPR, key = k0 + r;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (key < S_max) v = *reinterpret_cast<const u32x4*>(kseq + (size_t)key * D + c * 8);
+                *reinterpret_cast<u32x4*>(&kb[r][c * 8]) = v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const int kr = 64 * kh + 16 * kt;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&kb[kr + hl][32 * ks + 8 * quad]));
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[2][ks], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[1][ks], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[0][ks], acc, 0, 0, 0);
+                }
+                // acc[r] = score of key k0 + kr + 4*quad + r for query my_q
+                if (my_seq == bs) {
+                    const int key0 = k0 + kr + 4 * quad;
+                    if (vec_ok && key0 + 4 <= my_n) {
+                        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(my_row + key0));
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (key0 + r < my_n) my_row[key0 + r] = acc[r];
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 // ---- one workgroup per query, all keys in LDS ---------------------------------
 __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores,
                                                             const int32_t* __restrict__ n_cand,
@@ -497,7 +666,23 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     const bool multi = S_max > kRowSelectCap;
     uint8_t* w = static_cast<uint8_t*>(ws);
     hipError_t e = hipSuccess;
-    if (q_idx) {
+    if (q_idx && !multi && dtype == kBF16 && Nq >= kGemmMinQueries &&
+        (d_I == 64 || d_I == 128 || d_I == 256)) {
+        ProfScope prof(kProfScore, st);
+        const dim3 grid((unsigned)ceil_div(Nq, kGemmQ));
+        const bf16_t* qp = static_cast<const bf16_t*>(q_idx);
+        const bf16_t* kp = static_cast<const bf16_t*>(k_idx);
+        if (d_I == 64)
+            hipLaunchKernelGGL(score_gemm_kernel<64>, grid, dim3(kThreads), 0, st, qp, kp, q_seq,
+                               n_cand, scores, B, Nq, H_I, S_max);
+        else if (d_I == 128)
+            hipLaunchKernelGGL(score_gemm_kernel<128>, grid, dim3(kThreads), 0, st, qp, kp, q_seq,
+                               n_cand, scores, B, Nq, H_I, S_max);
+        else
+            hipLaunchKernelGGL(score_gemm_kernel<256>, grid, dim3(kThreads), 0, st, qp, kp, q_seq,
+                               n_cand, scores, B, Nq, H_I, S_max);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (q_idx) {
         e = dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores, w,
                                                    Nq, H_I, S_max, k, multi, st)
                           : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores,

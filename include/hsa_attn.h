@@ -94,8 +94,11 @@ int hsa_compress(int dtype, const void *x, const void *gate, const void *bias, v
  * Scores (score mode, q_idx != NULL):
  *   scores[q, s] = sum_{h<H_I} sum_{e<d_I} q_idx[q, h, e] * k_idx[q_seq[q], s, e]
  * for s < n_cand[q]; entries s >= n_cand[q] are left unspecified.  The sum
- * over heads is formed first (it is linear), so each score is one fp32 dot
- * product of length d_I; identical key rows give bitwise-identical scores.
+ * over heads is formed first in fp32 (it is linear), so each score is one dot
+ * product of length d_I with fp32 accumulation (with 64 or more bf16 queries
+ * and a select that fits one workgroup, on MFMA with the folded query carried
+ * as three bf16 terms); identical key rows of a sequence give
+ * bitwise-identical scores.
  *
  * Select (always): candidates s < n_cand[q]; order = score descending, equal
  * scores (IEEE, -0 == +0) by lower index first; NaN ranks below every

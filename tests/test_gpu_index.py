@@ -143,3 +143,64 @@ def test_scores_all_row_widths(oracle, dt, d_I, S_max):
         assert np.all(sg[i, 5:9] == sg[i, 100])
     want = oracle.topk(ref.astype(np.float32), n_cand.numpy(), k)
     assert _overlap(idx.cpu().numpy(), want) >= 0.999
+
+
+@pytest.mark.parametrize("d_I,S_max,routing", [(128, 3001, "mixed"), (64, 2048, "prefill"),
+                                               (256, 1500, "prefill"), (128, 777, "mixed")])
+def test_many_queries_per_sequence(oracle, d_I, S_max, routing):
+    """Many queries per sequence (the matrix-product scoring path): workgroups of 32
+    queries with one or several sequences, causal or random candidate counts, a key
+    width of 64, 128 or 256, S_max not a multiple of the key block, equal key rows."""
+    import hybrid_sparse_compressed_amd as hsa
+
+    g = torch.Generator().manual_seed(d_I * 7 + S_max)
+    B, Nq, H_I, k = 3, 100, 64, 64
+    q_idx = torch.randn(Nq, H_I, d_I, generator=g).to(torch.bfloat16)
+    k_idx = torch.randn(B, S_max, d_I, generator=g).to(torch.bfloat16)
+    k_idx[2, 40:45] = k_idx[2, 300]
+    if routing == "mixed":
+        q_seq = torch.randint(0, B, (Nq,), generator=g, dtype=torch.int32)
+        n_cand = torch.randint(0, S_max + 1, (Nq,), generator=g, dtype=torch.int32)
+        n_cand[:4] = torch.tensor([0, 1, k, S_max], dtype=torch.int32)
+    else:  # sequence-major, candidate count growing with the position
+        q_seq = (torch.arange(Nq) * B // Nq).to(torch.int32)
+        n_cand = torch.clamp((torch.arange(Nq) * 37) % (S_max + 1), max=S_max).to(torch.int32)
+    note("index many queries d_I=%d S=%d %s" % (d_I, S_max, routing))
+    s, idx = hsa.hsa_index_topk(q_idx.cuda(), k_idx.cuda(), n_cand, k, q_seq=q_seq)
+    torch.cuda.synchronize()
+    ref = oracle.index_scores(q_idx, k_idx, n_cand.numpy(), q_seq=q_seq.numpy())
+    worst = _check_scores(s, ref, q_idx, k_idx, q_seq.numpy(), n_cand.numpy())
+    want = oracle.topk(ref.astype(np.float32), n_cand.numpy(), k)
+    ov = _overlap(idx.cpu().numpy(), want)
+    print("score error / bound (worst) = %.3g, overlap = %.6f" % (worst, ov))
+    assert ov >= 0.999
+    sg = s.cpu().numpy()
+    for i in range(Nq):  # equal key rows score bitwise-equal
+        if int(q_seq[i]) == 2 and int(n_cand[i]) > 300:
+            assert np.all(sg[i, 40:45] == sg[i, 300])
+
+
+def test_prefill_32k_indexer_sampled(oracle):
+    """Full-size prefill indexer: 8 x 2048 query positions over 8 x 8192 C4 keys
+    (causal candidate counts); 24 sampled queries (first and last of sequences
+    included) checked against the oracle's scores and selection."""
+    import hybrid_sparse_compressed_amd as hsa
+    from hybrid_sparse_compressed_amd import workloads
+
+    w = workloads.prefill("cuda")
+    k = 512
+    note("index prefill_32k full size")
+    s, idx = hsa.hsa_index_topk(w["q_idx"], w["k_idx"], w["n_cand"], k, q_seq=w["q_seq"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    Nq = w["q_idx"].shape[0]
+    sel = sorted(set([0, 2047, 2048, Nq - 1] + rng.choice(Nq, 20, replace=False).tolist()))
+    qs = w["q_seq"].cpu()[sel]
+    nc = w["n_cand"].cpu()[sel]
+    q_sub = w["q_idx"][sel].cpu()
+    ref = oracle.index_scores(q_sub, w["k_idx"].cpu(), nc.numpy(), q_seq=qs.numpy())
+    worst = _check_scores(s[sel], ref, q_sub, w["k_idx"].cpu(), qs.numpy(), nc.numpy())
+    want = oracle.topk(ref.astype(np.float32), nc.numpy(), k)
+    ov = _overlap(idx[sel].cpu().numpy(), want)
+    print("score error / bound (worst) = %.3g, overlap = %.6f" % (worst, ov))
+    assert ov >= 0.999
