@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(
     __shared__ __align__(16) uint16_t qs[3][kGemmQ][SK];
     __shared__ int s_seq[kGemmQ], s_n[kGemmQ];
     __shared__ int s_list[kGemmQ], s_lmax[kGemmQ], s_nl;
+    __shared__ __align__(16) float so[kGemmQ][kGemmK + 4];  // scores of a block, by query
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int hl = lane & 15, quad = lane >> 4;
@@ -402,22 +403,33 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(
             bq[t][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&qs[t][16 * qb + hl][32 * ks + 8 * quad]));
     __syncthreads();
     const int my_q = 16 * qb + hl;
-    const int my_seq = s_seq[my_q], my_n = s_n[my_q];
-    float* my_row = scores + (size_t)(q0 + my_q) * S_max;
     const bool vec_ok = (S_max & 3) == 0;
     const int nl = s_nl;
+    // key block staging: thread moves chunks p = tid + j*256 (row p / CPR), the
+    // next block's chunks in flight while a block is computed
+    constexpr int KPT = kGemmK * CPR / kThreads;
+    static_assert(kGemmK * CPR % kThreads == 0, "staging map");
+    u32x4 kreg[KPT];
+    auto load_block = [&](const bf16_t* kseq, int k0) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int p = tid + j * kThreads, r = p / CPR, c = p % CPR, key = k0 + r;
+            kreg[j] = key < S_max ? *reinterpret_cast<const u32x4*>(kseq + (size_t)key * D + c * 8)
+                                  : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
     for (int li = 0; li < nl; ++li) {
         const int bs = s_list[li], nmax = s_lmax[li];
         const bf16_t* kseq = k_idx + (size_t)bs * S_max * D;
+        load_block(kseq, 0);
         for (int k0 = 0; k0 < nmax; k0 += kGemmK) {
-            // stage key rows k0 .. k0+127 (rows past S_max read as zero)
-            for (int p = tid; p < kGemmK * CPR; p += kThreads) {
-                const int r = p / CPR, c = p % CPR, key = k0 + r;
-                u32x4 v = u32x4{0u, 0u, 0u, 0u};
-                if (key < S_max) v = *reinterpret_cast<const u32x4*>(kseq + (size_t)key * D + c * 8);
-                *reinterpret_cast<u32x4*>(&kb[r][c * 8]) = v;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const int p = tid + j * kThreads;
+                *reinterpret_cast<u32x4*>(&kb[p / CPR][(p % CPR) * 8]) = kreg[j];
             }
             __syncthreads();
+            if (k0 + kGemmK < nmax) load_block(kseq, k0 + kGemmK);
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
                 const int kr = 64 * kh + 16 * kt;
@@ -430,18 +442,24 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[0][ks], acc, 0, 0, 0);
                 }
                 // acc[r] = score of key k0 + kr + 4*quad + r for query my_q
-                if (my_seq == bs) {
-                    const int key0 = k0 + kr + 4 * quad;
-                    if (vec_ok && key0 + 4 <= my_n) {
-                        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(my_row + key0));
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (key0 + r < my_n) my_row[key0 + r] = acc[r];
-                    }
-                }
+                *reinterpret_cast<f32x4*>(&so[my_q][kr + 4 * quad]) = acc;
             }
             __syncthreads();
+            // the block's scores leave as whole runs of each query's row
+            for (int p = tid; p < kGemmQ * (kGemmK / 4); p += kThreads) {
+                const int qq = p / (kGemmK / 4), key0 = k0 + (p % (kGemmK / 4)) * 4;
+                if (s_seq[qq] != bs) continue;
+                const int nq = s_n[qq];
+                float* row = scores + (size_t)(q0 + qq) * S_max;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&so[qq][key0 - k0]);
+                if (vec_ok && key0 + 4 <= nq) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(row + key0));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (key0 + r < nq) row[key0 + r] = v[r];
+                }
+            }
         }
     }
 }
@@ -451,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
                                                             const int32_t* __restrict__ n_cand,
                                                             int32_t* __restrict__ out, int S_max,
                                                             int k) {
-    __shared__ uint32_t keys[kRowSelectCap];
+    __shared__ __align__(16) uint32_t keys[kRowSelectCap];
     __shared__ uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
     const int q = blockIdx.x, tid = threadIdx.x;
@@ -462,7 +480,43 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
         for (int i = tid; i < k; i += kThreads) o[i] = i < n ? i : -1;
         return;
     }
-    for (int i = tid; i < n; i += kThreads) keys[i] = score_key(scores[(size_t)q * S_max + i]);
+    // the row's scores -> keys in LDS, 8 loads in flight per thread (16-byte
+    // loads when the row is 16-byte aligned)
+    const float* src = scores + (size_t)q * S_max;
+    int i0 = 0;
+    if ((S_max & 3) == 0) {
+        const int n4 = n / 4;
+        constexpr int U = 8;
+        for (int b0 = 0; b0 < n4; b0 += U * kThreads) {
+            f32x4 v[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int i4 = b0 + j * kThreads + tid;
+                if (i4 < n4) v[j] = *reinterpret_cast<const f32x4*>(src + 4 * i4);
+            }
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int i4 = b0 + j * kThreads + tid;
+                if (i4 < n4)
+                    *reinterpret_cast<u32x4*>(keys + 4 * i4) =
+                        u32x4{score_key(v[j][0]), score_key(v[j][1]), score_key(v[j][2]), score_key(v[j][3])};
+            }
+        }
+        i0 = 4 * n4;
+    }
+    for (int b0 = i0; b0 < n; b0 += 8 * kThreads) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = b0 + j * kThreads + tid;
+            if (i < n) v[j] = src[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = b0 + j * kThreads + tid;
+            if (i < n) keys[i] = score_key(v[j]);
+        }
+    }
     __syncthreads();
     int need = take, rem;
     const int d1 = radix_digit<kBins>(keys, n, 0u, 0u, 21, nullptr, 0u, need, h, tmp, &rem);
