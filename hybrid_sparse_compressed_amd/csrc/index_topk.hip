@@ -465,11 +465,35 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(
 }
 
 // ---- one workgroup per query, all keys in LDS ---------------------------------
+// Histogram of digit (key >> shift) & (NB-1) over the keys matching pref under
+// pmask, reading the LDS keys 16 bytes at a time; then the crossing bin.
+template <int NB>
+__device__ int row_digit(const uint32_t* keys, int n, uint32_t pmask, uint32_t pref, int shift,
+                         int need, uint32_t* h, uint32_t* tmp, int* rem) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < NB; i += kThreads) h[i] = 0;
+    __syncthreads();
+    const int n4 = n / 4;
+    for (int i4 = tid; i4 < n4; i4 += kThreads) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + 4 * i4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((kk[j] & pmask) == pref) atomicAdd(&h[(kk[j] >> shift) & (NB - 1)], 1u);
+    }
+    for (int i = 4 * n4 + tid; i < n; i += kThreads) {
+        const uint32_t kk = keys[i];
+        if ((kk & pmask) == pref) atomicAdd(&h[(kk >> shift) & (NB - 1)], 1u);
+    }
+    __syncthreads();
+    return find_crossing<NB>(h, need, tmp, rem);
+}
+
 __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores,
                                                             const int32_t* __restrict__ n_cand,
                                                             int32_t* __restrict__ out, int S_max,
                                                             int k) {
-    __shared__ __align__(16) uint32_t keys[kRowSelectCap];
+    // keys of the row: dynamic LDS sized by the launch to S_max (<= kRowSelectCap)
+    extern __shared__ __align__(16) uint32_t keys[];
     __shared__ uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
     const int q = blockIdx.x, tid = threadIdx.x;
@@ -480,8 +504,11 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
         for (int i = tid; i < k; i += kThreads) o[i] = i < n ? i : -1;
         return;
     }
-    // the row's scores -> keys in LDS, 8 loads in flight per thread (16-byte
-    // loads when the row is 16-byte aligned)
+    // the row's scores -> keys in LDS (8 loads in flight per thread, 16-byte
+    // loads when the row is 16-byte aligned) and the histogram of their top
+    // 11 bits on the way
+    for (int i = tid; i < kBins; i += kThreads) h[i] = 0;
+    __syncthreads();
     const float* src = scores + (size_t)q * S_max;
     int i0 = 0;
     if ((S_max & 3) == 0) {
@@ -497,9 +524,13 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
 #pragma unroll
             for (int j = 0; j < U; ++j) {
                 const int i4 = b0 + j * kThreads + tid;
-                if (i4 < n4)
-                    *reinterpret_cast<u32x4*>(keys + 4 * i4) =
-                        u32x4{score_key(v[j][0]), score_key(v[j][1]), score_key(v[j][2]), score_key(v[j][3])};
+                if (i4 < n4) {
+                    const u32x4 kk = u32x4{score_key(v[j][0]), score_key(v[j][1]), score_key(v[j][2]),
+                                           score_key(v[j][3])};
+                    *reinterpret_cast<u32x4*>(keys + 4 * i4) = kk;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) atomicAdd(&h[kk[e] >> 21], 1u);
+                }
             }
         }
         i0 = 4 * n4;
@@ -514,26 +545,40 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = b0 + j * kThreads + tid;
-            if (i < n) keys[i] = score_key(v[j]);
+            if (i < n) {
+                const uint32_t kk = score_key(v[j]);
+                keys[i] = kk;
+                atomicAdd(&h[kk >> 21], 1u);
+            }
         }
     }
     __syncthreads();
     int need = take, rem;
-    const int d1 = radix_digit<kBins>(keys, n, 0u, 0u, 21, nullptr, 0u, need, h, tmp, &rem);
+    const int d1 = find_crossing<kBins>(h, need, tmp, &rem);
     need = rem;
     uint32_t pref = (uint32_t)d1 << 21;
-    const int d2 = radix_digit<kBins>(keys, n, 0xffe00000u, pref, 10, nullptr, 0u, need, h, tmp, &rem);
+    const int d2 = row_digit<kBins>(keys, n, 0xffe00000u, pref, 10, need, h, tmp, &rem);
     need = rem;
     pref |= (uint32_t)d2 << 10;
-    const int d3 = radix_digit<1024>(keys, n, 0xfffffc00u, pref, 0, nullptr, 0u, need, h, tmp, &rem);
+    const int d3 = row_digit<1024>(keys, n, 0xfffffc00u, pref, 0, need, h, tmp, &rem);
     need = rem;  // how many keys equal to T are taken (the lowest indices)
     const uint32_t T = pref | (uint32_t)d3;
 
-    // ordered compaction over contiguous per-thread ranges
-    const int E = ceil_div(n, kThreads);
+    // ordered compaction over contiguous per-thread ranges (multiples of 4
+    // keys, read 16 bytes at a time)
+    const int E = 4 * ceil_div(n, 4 * kThreads);
     const int s0 = min(n, tid * E), s1 = min(n, s0 + E);
     uint32_t gt = 0, eq = 0;
-    for (int s = s0; s < s1; ++s) {
+    int s = s0;
+    for (; s + 4 <= s1; s += 4) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gt += kk[j] > T;
+            eq += kk[j] == T;
+        }
+    }
+    for (; s < s1; ++s) {
         const uint32_t kk = keys[s];
         gt += kk > T;
         eq += kk == T;
@@ -542,14 +587,28 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     const uint32_t eq_base = block_excl_scan<kThreads>(eq, tmp, &tot);
     const int eq_take = max(0, min((int)eq, need - (int)eq_base));
     const uint32_t pos0 = block_excl_scan<kThreads>(gt + (uint32_t)eq_take, tmp, &tot);
-    int pos = (int)pos0, e = 0;
-    for (int s = s0; s < s1; ++s) {
-        const uint32_t kk = keys[s];
-        if (kk > T) {
-            o[pos++] = s;
-        } else if (kk == T) {
-            if (e < eq_take) o[pos++] = s;
-            ++e;
+    if (gt + (uint32_t)eq_take > 0) {
+        int pos = (int)pos0, e = 0;
+        for (s = s0; s + 4 <= s1; s += 4) {
+            const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + s);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (kk[j] > T) {
+                    o[pos++] = s + j;
+                } else if (kk[j] == T) {
+                    if (e < eq_take) o[pos++] = s + j;
+                    ++e;
+                }
+            }
+        }
+        for (; s < s1; ++s) {
+            const uint32_t kk = keys[s];
+            if (kk > T) {
+                o[pos++] = s;
+            } else if (kk == T) {
+                if (e < eq_take) o[pos++] = s;
+                ++e;
+            }
         }
     }
     for (int i = take + tid; i < k; i += kThreads) o[i] = -1;
@@ -751,7 +810,9 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     }
     ProfScope prof(kProfSelect, st);
     if (!multi) {
-        hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)Nq), dim3(kThreads), 0, st, scores,
+        // LDS for S_max keys only, so that short rows fit more workgroups per CU
+        const size_t lds = (size_t)ceil_div(S_max, 4) * 16;
+        hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)Nq), dim3(kThreads), lds, st, scores,
                            n_cand, topk_idx, S_max, k);
     } else {
         const int G = ceil_div(S_max, kFilterChunk);
