@@ -45,6 +45,8 @@ def parse():
                     help="wall time over which the oracle layer-step is repeated")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-row measurements at the other workloads")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="only the per-row measurements (a JSON object of rows), for profiling them")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warm-up, run three plain device copies of this many MiB, so that "
                          "a hardware byte counter can be scaled by a transfer of known size")
@@ -79,6 +81,11 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.rows_only:
+        if args.copy_calibration_mib > 0:
+            copy_calibration(torch, dev, args.copy_calibration_mib)
+        print(json.dumps({"rows": other_rows(hsa, workloads)}), flush=True)
+        return
     name = "c4_decode_1m"
     w = workloads.c4_decode(name, dev)
     c = w["cfg"]
@@ -113,13 +120,7 @@ def main():
                               topk_idx=idx, out=out, lse=lse, workspace=ws)
 
     if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty(n, dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, dev, args.copy_calibration_mib)
 
     for i in range(args.warmup):
         step(i)
@@ -210,6 +211,18 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def copy_calibration(torch, dev, mib):
+    """Three plain device copies of mib MiB: a transfer of known size for scaling the
+    hardware byte counters."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def _median_us(torch, fn, reps):
