@@ -225,8 +225,10 @@ def copy_calibration(torch, dev, mib):
     del src, dst
 
 
-def _median_us(torch, fn, reps):
-    """Median wall time of fn() on the current stream, in microseconds (one warm-up call)."""
+def _median_us(torch, fn, reps, inner=1):
+    """Median time per call of fn() on the current stream, in microseconds: reps
+    measurements of `inner` back-to-back calls each (one warm-up call first), so that
+    short calls are timed as a stream of calls, not with the host's launch latency."""
     fn()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -234,10 +236,11 @@ def _median_us(torch, fn, reps):
     ts = []
     for _ in range(reps):
         e0.record()
-        fn()
+        for _ in range(inner):
+            fn()
         e1.record()
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1000.0)
+        ts.append(e0.elapsed_time(e1) * 1000.0 / inner)
     ts.sort()
     return ts[len(ts) // 2]
 
@@ -269,7 +272,7 @@ def other_rows(hsa, workloads):
     # each call reads x and its gate once and writes the entries once
     for m, g, b, out, key in ((4, w["gate4"], w["bias4"], c4, "a1_compress_c4"),
                               (128, w["gate128"], w["bias128"], c128, "a1_compress_c128")):
-        us = _median_us(torch, lambda: hsa.hsa_compress(w["x"], g, b, m, out=out), 7)
+        us = _median_us(torch, lambda: hsa.hsa_compress(w["x"], g, b, m, out=out), 5, 5)
         alg = 2 * n_seq * T * D * 2 + m * D * 2 + n_seq * (T // m) * D * 2
         rows[key] = _row("prefill_32k", us, "hbm", alg, "GB/s", HBM_PEAK_GBPS)
     Nq, S, k = 16384, T // 4, 512
@@ -297,17 +300,24 @@ def other_rows(hsa, workloads):
     d = workloads.c128_dense_decode("cuda")
     lens = d["lengths"]
     alg = sum((128 + L // 128) * 1152 + 139264 for L in lens)
+    outd = torch.empty((len(lens), 64, 512), dtype=torch.bfloat16, device="cuda")
+    lsed = torch.empty((len(lens), 64), dtype=torch.float32, device="cuda")
     us = _median_us(torch, lambda: hsa.hsa_attn_decode(d["q"], d["swa_kv"], d["swa_len"],
                                                        d["comp_kv"], d["comp_len"], d["scale"],
-                                                       512), 21)
+                                                       512, out=outd, lse=lsed), 7, 20)
     rows["a4_dense_decode_c128"] = _row("c128_dense_decode", us, "hbm", alg, "GB/s",
                                         HBM_PEAK_GBPS)
     del d
     e = workloads.c4_decode("c4_decode_64k", "cuda")
+    sc = torch.empty((1, e["comp_kv"].shape[1]), dtype=torch.float32, device="cuda")
+    ix = torch.empty((1, 512), dtype=torch.int32, device="cuda")
+    oe = torch.empty((1, 64, 512), dtype=torch.bfloat16, device="cuda")
+    le = torch.empty((1, 64), dtype=torch.float32, device="cuda")
     us = _median_us(torch, lambda: hsa.hsa_decode_sparse(e["q_idx"], e["k_idx"], e["n_cand"], 512,
                                                          e["q"], e["swa_kv"], e["swa_len"],
                                                          e["comp_kv"], e["comp_len"], e["scale"],
-                                                         512), 21)
+                                                         512, scores=sc, topk_idx=ix, out=oe,
+                                                         lse=le), 7, 20)
     rows["a2_a3_a4_decode_c4_64k"] = _row("c4_decode_64k", us, "hbm", 5089280, "GB/s",
                                           HBM_PEAK_GBPS)
     del e

@@ -488,12 +488,56 @@ __device__ int row_digit(const uint32_t* keys, int n, uint32_t pmask, uint32_t p
     return find_crossing<NB>(h, need, tmp, rem);
 }
 
+constexpr int kRowListCap = 4096;  // short list of the row select (entries at or above bin d1)
+
+// Ordered compaction of the selected keys of list (lk, li?) of length n: the
+// first min(k, ...) under (key desc, index asc) given the k-th key T and the
+// number `need` of keys equal to T to take; writes ascending indices.
+__device__ void row_write(const uint32_t* lk, const uint16_t* li, int n, uint32_t T, int need,
+                          uint32_t* tmp, int32_t* o) {
+    const int tid = threadIdx.x;
+    const int E = 4 * ceil_div(n, 4 * kThreads);
+    const int s0 = min(n, tid * E), s1 = min(n, s0 + E);
+    uint32_t gt = 0, eq = 0;
+    int s = s0;
+    for (; s + 4 <= s1; s += 4) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(lk + s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gt += kk[j] > T;
+            eq += kk[j] == T;
+        }
+    }
+    for (; s < s1; ++s) {
+        gt += lk[s] > T;
+        eq += lk[s] == T;
+    }
+    uint32_t tot;
+    const uint32_t eq_base = block_excl_scan<kThreads>(eq, tmp, &tot);
+    const int eq_take = max(0, min((int)eq, need - (int)eq_base));
+    const uint32_t pos0 = block_excl_scan<kThreads>(gt + (uint32_t)eq_take, tmp, &tot);
+    if (gt + (uint32_t)eq_take == 0) return;
+    int pos = (int)pos0, e = 0;
+    for (s = s0; s < s1; ++s) {
+        const uint32_t kk = lk[s];
+        const int idx = li ? (int)li[s] : s;
+        if (kk > T) {
+            o[pos++] = idx;
+        } else if (kk == T) {
+            if (e < eq_take) o[pos++] = idx;
+            ++e;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores,
                                                             const int32_t* __restrict__ n_cand,
                                                             int32_t* __restrict__ out, int S_max,
                                                             int k) {
-    // keys of the row: dynamic LDS sized by the launch to S_max (<= kRowSelectCap)
+    // dynamic LDS: the row's keys (S_max rounded up to 4), then the short
+    // list's indices (kRowListCap uint16)
     extern __shared__ __align__(16) uint32_t keys[];
+    uint16_t* lidx = reinterpret_cast<uint16_t*>(keys + 4 * ceil_div(S_max, 4));
     __shared__ uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
     const int q = blockIdx.x, tid = threadIdx.x;
@@ -555,62 +599,48 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     __syncthreads();
     int need = take, rem;
     const int d1 = find_crossing<kBins>(h, need, tmp, &rem);
+    const int m = (take - rem) + (int)h[d1];  // entries with bin >= d1
     need = rem;
-    uint32_t pref = (uint32_t)d1 << 21;
-    const int d2 = row_digit<kBins>(keys, n, 0xffe00000u, pref, 10, need, h, tmp, &rem);
+    const uint32_t lo1 = (uint32_t)d1 << 21;
+    // short list: the entries at or above bin d1, compacted in index order in
+    // place (every thread holds its range in registers before any write)
+    int nl = n;
+    const uint16_t* li = nullptr;
+    if (m <= kRowListCap) {
+        constexpr int RMAX = kRowSelectCap / kThreads;  // keys per thread at most (48)
+        const int E = 4 * ceil_div(n, 4 * kThreads);
+        const int s0 = min(n, tid * E), s1 = min(n, s0 + E);
+        uint32_t r[RMAX];
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < RMAX; ++j) {
+            const int s = s0 + j;
+            r[j] = s < s1 ? keys[s] : 0u;
+            cnt += (s < s1 && r[j] >= lo1) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t base = block_excl_scan<kThreads>(cnt, tmp, &tot);  // barriers: all reads done
+        uint32_t pos = base;
+#pragma unroll
+        for (int j = 0; j < RMAX; ++j) {
+            const int s = s0 + j;
+            if (s < s1 && r[j] >= lo1) {
+                keys[pos] = r[j];
+                lidx[pos] = (uint16_t)s;
+                ++pos;
+            }
+        }
+        __syncthreads();
+        nl = (int)tot;
+        li = lidx;
+    }
+    const int d2 = row_digit<kBins>(keys, nl, 0xffe00000u, lo1, 10, need, h, tmp, &rem);
     need = rem;
-    pref |= (uint32_t)d2 << 10;
-    const int d3 = row_digit<1024>(keys, n, 0xfffffc00u, pref, 0, need, h, tmp, &rem);
+    const uint32_t pref = lo1 | ((uint32_t)d2 << 10);
+    const int d3 = row_digit<1024>(keys, nl, 0xfffffc00u, pref, 0, need, h, tmp, &rem);
     need = rem;  // how many keys equal to T are taken (the lowest indices)
     const uint32_t T = pref | (uint32_t)d3;
-
-    // ordered compaction over contiguous per-thread ranges (multiples of 4
-    // keys, read 16 bytes at a time)
-    const int E = 4 * ceil_div(n, 4 * kThreads);
-    const int s0 = min(n, tid * E), s1 = min(n, s0 + E);
-    uint32_t gt = 0, eq = 0;
-    int s = s0;
-    for (; s + 4 <= s1; s += 4) {
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + s);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            gt += kk[j] > T;
-            eq += kk[j] == T;
-        }
-    }
-    for (; s < s1; ++s) {
-        const uint32_t kk = keys[s];
-        gt += kk > T;
-        eq += kk == T;
-    }
-    uint32_t tot;
-    const uint32_t eq_base = block_excl_scan<kThreads>(eq, tmp, &tot);
-    const int eq_take = max(0, min((int)eq, need - (int)eq_base));
-    const uint32_t pos0 = block_excl_scan<kThreads>(gt + (uint32_t)eq_take, tmp, &tot);
-    if (gt + (uint32_t)eq_take > 0) {
-        int pos = (int)pos0, e = 0;
-        for (s = s0; s + 4 <= s1; s += 4) {
-            const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + s);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (kk[j] > T) {
-                    o[pos++] = s + j;
-                } else if (kk[j] == T) {
-                    if (e < eq_take) o[pos++] = s + j;
-                    ++e;
-                }
-            }
-        }
-        for (; s < s1; ++s) {
-            const uint32_t kk = keys[s];
-            if (kk > T) {
-                o[pos++] = s;
-            } else if (kk == T) {
-                if (e < eq_take) o[pos++] = s;
-                ++e;
-            }
-        }
-    }
+    row_write(keys, li, nl, T, need, tmp, o);
     for (int i = take + tid; i < k; i += kThreads) o[i] = -1;
 }
 
@@ -810,8 +840,9 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     }
     ProfScope prof(kProfSelect, st);
     if (!multi) {
-        // LDS for S_max keys only, so that short rows fit more workgroups per CU
-        const size_t lds = (size_t)ceil_div(S_max, 4) * 16;
+        // LDS for S_max keys (and the short list's indices) only, so that short
+        // rows fit more workgroups per CU
+        const size_t lds = (size_t)ceil_div(S_max, 4) * 16 + (size_t)kRowListCap * 2;
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)Nq), dim3(kThreads), lds, st, scores,
                            n_cand, topk_idx, S_max, k);
     } else {
