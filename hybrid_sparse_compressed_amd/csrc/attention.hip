@@ -592,7 +592,7 @@ __device__ __forceinline__ uint32_t pair_word(const u32x4& a, const u32x4& b, in
                    : __builtin_amdgcn_perm(b[x >> 1], a[x >> 1], 0x05040100u);
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool DEC>
 __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     typedef bf16_t T;
     typedef P64Lds<DQK, DV> L;
@@ -619,38 +619,53 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     const int head = hb * 16 + hl;
     const bool head_ok = head < a.H;
 
-    // queries go to XCDs in contiguous ranges (workgroup L runs on XCD L % 8),
-    // so the windows of neighbouring positions meet in one L2
-    const int nq8 = ceil_div(a.n_queries, 8);
-    const int pq = ((int)blockIdx.x % 8) * nq8 + (int)blockIdx.x / 8;
-    if (pq >= a.n_queries) return;
-    const int b = pq / a.n_q;
-    const int qpos = a.q_start + pq % a.n_q;
-    int n_comp = (qpos + 1) / a.m;
-    n_comp = n_comp < a.S_max ? n_comp : a.S_max;
-    const int vr1 = a.max_rows;
+    int b, pq = 0, qpos = 0, n_comp, n_swa = 0, vr0 = 0, vr1 = a.max_rows;
+    if constexpr (DEC) {
+        // decode split: workgroup (split x, sequence y) takes rows [vr0, vr1)
+        b = blockIdx.y;
+        vr0 = (int)blockIdx.x * a.rows_per_split;
+        vr1 = min(a.max_rows, vr0 + a.rows_per_split);
+        n_swa = a.swa_len[b];
+        n_swa = n_swa < 0 ? 0 : (n_swa > a.W ? a.W : n_swa);
+        n_comp = a.comp_len[b];
+        n_comp = n_comp < 0 ? 0 : (n_comp > a.S_max ? a.S_max : n_comp);
+    } else {
+        // queries go to XCDs in contiguous ranges (workgroup L runs on XCD L % 8),
+        // so the windows of neighbouring positions meet in one L2
+        const int nq8 = ceil_div(a.n_queries, 8);
+        pq = ((int)blockIdx.x % 8) * nq8 + (int)blockIdx.x / 8;
+        if (pq >= a.n_queries) return;
+        b = pq / a.n_q;
+        qpos = a.q_start + pq % a.n_q;
+        n_comp = (qpos + 1) / a.m;
+        n_comp = n_comp < a.S_max ? n_comp : a.S_max;
+    }
 
     const T* win = reinterpret_cast<const T*>(a.win);
     const T* comp = reinterpret_cast<const T*>(a.comp);
     auto row_at = [&](int vr) -> const T* {
         if (vr >= vr1) return nullptr;
         if (vr < a.W) {
-            const int tok = qpos - a.W + 1 + vr;
-            return tok >= 0 ? win + ((size_t)b * a.T_len + tok) * DQK : nullptr;
+            if constexpr (DEC) {
+                return vr < n_swa ? win + ((size_t)b * a.W + vr) * DQK : nullptr;
+            } else {
+                const int tok = qpos - a.W + 1 + vr;
+                return tok >= 0 ? win + ((size_t)b * a.T_len + tok) * DQK : nullptr;
+            }
         }
         const int j = vr - a.W;
         int ci;
         if (a.comp_idx)
-            ci = j < a.k ? a.comp_idx[(size_t)pq * a.k + j] : -1;
+            ci = j < a.k ? a.comp_idx[(size_t)(DEC ? b : pq) * a.k + j] : -1;
         else
             ci = j;
         return (ci >= 0 && ci < n_comp) ? comp + ((size_t)b * a.S_max + ci) * DQK : nullptr;
     };
-    const T* first_row = row_at(tid);  // index loads before the Q loads
+    const T* first_row = row_at(vr0 + tid);  // index loads before the Q loads
 
     typename M::frag qf[NKK];
     {
-        const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)pq * a.H + (head_ok ? head : 0)) * DQK;
+        const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)(DEC ? b : pq) * a.H + (head_ok ? head : 0)) * DQK;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qrow + kk * M::kK + quad * 8)
@@ -683,10 +698,10 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
         }
     };
 
-    for (int c0 = 0; c0 < vr1; c0 += kP64Chunk) {
+    for (int c0 = vr0; c0 < vr1; c0 += kP64Chunk) {
         const int c1 = min(vr1, c0 + kP64Chunk);
         {
-            const T* p = c0 == 0 ? first_row : row_at(c0 + tid);
+            const T* p = c0 == vr0 ? first_row : row_at(c0 + tid);
             row_ptr[tid] = p;
         }
         if (tid < kP64Chunk / kP64Rows) tile_any[tid] = 0;
@@ -815,7 +830,18 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 
     // ---- epilogue.  acc[t][r] = O^T[256*half + 16t + 4quad + r][head]
     if (!head_ok) return;
-    const size_t orow = (size_t)pq * a.H + head;
+    if constexpr (DEC) {
+        if (a.n_split > 1) {  // unnormalised partials for the merge kernel
+            const size_t prow = ((size_t)b * a.n_split + blockIdx.x) * a.H + head;
+            if (half == 0 && quad == 0)
+                *reinterpret_cast<float2*>(a.part_ml + prow * 2) = float2{m_run, l_run};
+            float* po = a.part_o + prow * DV + half * DW;
+#pragma unroll
+            for (int t = 0; t < NMT; ++t) *reinterpret_cast<f32x4*>(po + t * 16 + quad * 4) = acc[t];
+            return;
+        }
+    }
+    const size_t orow = (size_t)(DEC ? b : pq) * a.H + head;
     T* o = reinterpret_cast<T*>(a.out) + orow * DV + half * DW;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
@@ -945,6 +971,41 @@ bool attn_shape_supported(int dtype, int d_qk, int d_v) {
     return dtype == kBF16 && d_qk == 576 && d_v == 512;  // fp32 at 576 would spill registers
 }
 
+template <bool DEC>
+hipError_t launch_p64(const AttnArgs& a, dim3 grid, hipStream_t st) {
+    constexpr size_t lds = P64Lds<576, 512>::kBytes;
+    static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill64_kernel<576, 512, DEC>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    ProfScope prof(kProfAttn, st);
+    hipLaunchKernelGGL((prefill64_kernel<576, 512, DEC>), grid, dim3(kP64Threads), lds, st, a);
+    return hipGetLastError();
+}
+
+// Dense decode with 64 bf16 heads over a 576/512 latent goes to the 64-head
+// kernel when its workgroups (one per split and sequence) fill the GPU.
+bool decode64_applies(int B, int H, int d_v, int max_rows, bool dense) {
+    return dense && H == kP64Heads && d_v == 512 && (long long)B * ceil_div(max_rows, kP64Rows) >= 256;
+}
+
+DecodePlan plan_decode64(int B, int max_rows) {
+    DecodePlan p;
+    p.max_rows = max_rows;
+    const int tiles = ceil_div(max_rows, kP64Rows);
+    int n_split = ceil_div(256, B);  // about one workgroup per compute unit
+    if (n_split > tiles) n_split = tiles;
+    if (n_split > kMaxSplit) n_split = kMaxSplit;
+    if (n_split < 1) n_split = 1;
+    p.rows_per_split = ceil_div(tiles, n_split) * kP64Rows;
+    p.n_split = ceil_div(max_rows, p.rows_per_split);
+    if (p.n_split < 1) p.n_split = 1;
+    return p;
+}
+
 DecodePlan plan_decode(int B, int H, int max_rows) {
     DecodePlan p;
     p.max_rows = max_rows;
@@ -970,9 +1031,17 @@ static size_t ml_bytes(int B, int n_split, int H) {
 }
 
 size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows) {
+    // enough for either plan (the 64-head one is chosen at launch, by shape)
     const DecodePlan p = plan_decode(B, H, max_rows);
-    if (p.n_split <= 1) return 0;
-    return ml_bytes(B, p.n_split, H) + (size_t)B * p.n_split * H * d_v * sizeof(float);
+    size_t bytes = p.n_split <= 1 ? 0 : ml_bytes(B, p.n_split, H) + (size_t)B * p.n_split * H * d_v * sizeof(float);
+    if (decode64_applies(B, H, d_v, max_rows, true)) {
+        const DecodePlan q = plan_decode64(B, max_rows);
+        if (q.n_split > 1) {
+            const size_t b64 = ml_bytes(B, q.n_split, H) + (size_t)B * q.n_split * H * d_v * sizeof(float);
+            bytes = b64 > bytes ? b64 : bytes;
+        }
+    }
+    return bytes;
 }
 
 static hipError_t launch_merge(int dtype, int d_v, const AttnArgs& a, int B, int H, int n_split,
@@ -1011,13 +1080,24 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
     a.k = k;
     a.m = 1;
     const int max_rows = W + (comp_idx ? k : S_max);
-    const DecodePlan p = plan_decode(B, H, max_rows);
     a.max_rows = max_rows;
+    a.scale_log2 = scale * kLog2e;
+    if (dtype == kBF16 && d_qk == 576 && decode64_applies(B, H, d_v, max_rows, comp_idx == nullptr)) {
+        const DecodePlan p = plan_decode64(B, max_rows);
+        a.rows_per_split = p.rows_per_split;
+        a.n_split = p.n_split;
+        a.part_o = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ml_bytes(B, p.n_split, H))
+                      : nullptr;
+        if (p.n_split > 1 && !ws) return hipErrorInvalidValue;
+        hipError_t e = launch_p64<true>(a, dim3((unsigned)p.n_split, (unsigned)B, 1u), st);
+        if (e != hipSuccess || p.n_split <= 1) return e;
+        return launch_merge(dtype, d_v, a, B, H, p.n_split, S_max, k, st);
+    }
+    const DecodePlan p = plan_decode(B, H, max_rows);
     a.rows_per_split = p.rows_per_split;
     a.n_split = p.n_split;
     a.part_o = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ml_bytes(B, p.n_split, H))
                   : nullptr;
-    a.scale_log2 = scale * kLog2e;
     dim3 grid((unsigned)p.n_split, (unsigned)B, (unsigned)ceil_div(H, kHeadsPerWG));
     hipError_t e = dispatch_attn<kModeDecode>(dtype, d_qk, d_v, a, grid, st);
     if (e != hipSuccess || p.n_split <= 1) return e;
@@ -1095,20 +1175,9 @@ hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const v
     a.hblocks = ceil_div(H, kHeadsPerWG);
     a.n_queries = n_seq * n_q;
     if (dtype == kBF16 && d_qk == 576 && d_v == 512 && H == kP64Heads) {
-        constexpr size_t lds = P64Lds<576, 512>::kBytes;
-        static bool attr_set = false;  // raise the dynamic-LDS limit once
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill64_kernel<576, 512>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
         const long long nwg = (long long)ceil_div(a.n_queries, 8) * 8;
         if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        ProfScope prof(kProfAttn, st);
-        hipLaunchKernelGGL((prefill64_kernel<576, 512>), dim3((unsigned)nwg), dim3(kP64Threads), lds,
-                           st, a);
-        return hipGetLastError();
+        return launch_p64<false>(a, dim3((unsigned)nwg), st);
     }
     const long long nwg = (long long)ceil_div(a.n_queries, 8) * 8 * a.hblocks;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -110,6 +110,35 @@ def test_decode_full_size_c128_dense(oracle):
     print(st)
 
 
+def test_decode_dense_64_heads_many_splits(oracle):
+    """Dense decode with 64 heads and enough rows to use the 64-head workgroups
+    (one per split and sequence): ragged window fill and compressed lengths,
+    including empty ones, merged over 22 splits."""
+    g = torch.Generator().manual_seed(321)
+    B, W, S = 8, 128, 4096
+    q = _rand((B, 64, 576), torch.bfloat16, g)
+    swa = _rand((B, W, 576), torch.bfloat16, g)
+    comp = _rand((B, S, 576), torch.bfloat16, g)
+    swa_len = torch.tensor([128, 5, 128, 0, 64, 128, 1, 128], dtype=torch.int32)
+    comp_len = torch.tensor([4096, 0, 1000, 4096, 17, 2048, 4095, 3000], dtype=torch.int32)
+    _check_decode(oracle, q, swa, swa_len, comp, comp_len, 1.0 / 24.0, 512, None,
+                  "dense 64-head splits")
+
+
+def test_decode_dense_64_heads_one_split(oracle):
+    """256 sequences of up to 160 rows: the 64-head workgroups need one split each
+    and write the normalised output directly."""
+    g = torch.Generator().manual_seed(654)
+    B, W, S = 256, 128, 32
+    q = _rand((B, 64, 576), torch.bfloat16, g)
+    swa = _rand((B, W, 576), torch.bfloat16, g)
+    comp = _rand((B, S, 576), torch.bfloat16, g)
+    swa_len = torch.randint(1, W + 1, (B,), generator=g, dtype=torch.int32)
+    comp_len = torch.randint(0, S + 1, (B,), generator=g, dtype=torch.int32)
+    _check_decode(oracle, q, swa, swa_len, comp, comp_len, 1.0 / 24.0, 512, None,
+                  "dense 64-head one split")
+
+
 def test_decode_is_deterministic():
     from hybrid_sparse_compressed_amd import workloads
 
