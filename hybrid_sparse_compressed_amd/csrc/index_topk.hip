@@ -657,8 +657,9 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
                                                                const int32_t* __restrict__ n_cand,
                                                                uint8_t* __restrict__ ws, int S_max,
                                                                int k) {
-    __shared__ uint32_t h[kBins];
+    __shared__ __align__(16) uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
+    static_assert(kBins == 8 * kThreads, "two 16-byte histogram loads per thread");
 
     const int q = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
@@ -671,8 +672,16 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
     }
     const int sb = s0 + tid * kPerThread;
 
-    // 1. this thread's scores (all loads in flight together) and the
-    //    threshold bin of the first digit from the completed histogram
+    // 1. the completed first-digit histogram (two 16-byte loads per thread)
+    //    and this thread's scores, all loads in flight together; then the
+    //    threshold bin
+    const bool partial = take < n;
+    u32x4 h0 = u32x4{0u, 0u, 0u, 0u}, h1 = u32x4{0u, 0u, 0u, 0u};
+    if (partial) {
+        const u32x4* hs = reinterpret_cast<const u32x4*>(W.hist);
+        h0 = hs[tid];
+        h1 = hs[tid + kThreads];
+    }
     float v[kPerThread];
     const float* src = scores + (size_t)q * S_max + sb;
     if (sb + kPerThread <= n && (((uintptr_t)src) & 15u) == 0) {
@@ -686,8 +695,9 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
         for (int i = 0; i < kPerThread; ++i) v[i] = sb + i < n ? src[i] : 0.f;
     }
     int t1 = -1;  // -1: every candidate is selected
-    if (take < n) {
-        for (int i = tid; i < kBins; i += kThreads) h[i] = W.hist[i];
+    if (partial) {
+        reinterpret_cast<u32x4*>(h)[tid] = h0;
+        reinterpret_cast<u32x4*>(h)[tid + kThreads] = h1;
         __syncthreads();
         int rem;
         t1 = find_crossing<kBins>(h, take, tmp, &rem);
