@@ -867,7 +867,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
                                                          void* __restrict__ out,
                                                          float* __restrict__ lse, int H,
                                                          int n_split) {
-    constexpr int kBatch = 32;  // split partials loaded per round
+    constexpr int kBatch = 16;  // split partials loaded per round
     auto load4 = [](const float* p) -> f32x4 { return *reinterpret_cast<const f32x4*>(p); };
     __shared__ float wsp[kMaxSplit], lsp[kMaxSplit];
     __shared__ float stat[2];
@@ -876,11 +876,13 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
     const size_t sstride = (size_t)H * DV;
     const int d = tid * 4;           // this thread's 4 channels (DV <= 512)
     const bool has_d = d < DV;
-    // first round of output partials in flight with the (max, sum) loads
+    const int dc = has_d ? d : 0;    // loads stay in bounds; results of !has_d are not stored
+    // first round of output partials in flight with the (max, sum) loads; the
+    // loads are unconditional (a slot past n_split reloads the last split and
+    // is not accumulated), so none of them waits for another
     f32x4 pv[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-        pv[j] = (has_d && j < n_split) ? load4(p0 + j * sstride + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kBatch; ++j) pv[j] = load4(p0 + (size_t)min(j, n_split - 1) * sstride + dc);
     float ms = -INFINITY, ls = 0.f;
     if (tid < n_split) {
         const float2 v = *reinterpret_cast<const float2*>(part_ml + (((size_t)b * n_split + tid) * H + h) * 2);
@@ -913,10 +915,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
     for (int s0 = 0; s0 < n_split; s0 += kBatch) {
         if (s0 > 0) {
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int s = s0 + j;
-                pv[j] = (has_d && s < n_split) ? load4(p0 + s * sstride + d) : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int j = 0; j < kBatch; ++j) pv[j] = load4(p0 + (size_t)min(s0 + j, n_split - 1) * sstride + dc);
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
