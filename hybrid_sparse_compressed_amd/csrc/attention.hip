@@ -384,13 +384,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             }
         }
         __syncthreads();
-        // the next tile of this chunk with valid rows goes out now
-        pre = -1;
-        for (int nb = tb + kTile; nb < c1 - c0; nb += kTile) {
-            if (tile_any[nb / kTile]) {
-                issue(nb);
-                pre = nb;
-                break;
+        // the next tile of this chunk with valid rows goes out now (prefill,
+        // whose workgroups walk many tiles; a decode split is mostly one tile,
+        // and the registers held through the tile would cost more there)
+        if constexpr (PREFILL) {
+            pre = -1;
+            for (int nb = tb + kTile; nb < c1 - c0; nb += kTile) {
+                if (tile_any[nb / kTile]) {
+                    issue(nb);
+                    pre = nb;
+                    break;
+                }
             }
         }
 
@@ -400,19 +404,31 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         {
             f32x4 c0v = f32x4{0.f, 0.f, 0.f, 0.f}, c1v = f32x4{0.f, 0.f, 0.f, 0.f};
             const T* krow = Ks + (size_t)(wave * 16 + hl) * L::kStrideK;
+            // K fragments are read from LDS a group at a time, all reads of a
+            // group in flight before its MFMAs
+            constexpr int KG = NKK % 6 == 0 ? 6 : (NKK % 4 == 0 ? 4 : 1);
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                typename M::frag af;
-                if constexpr (sizeof(T) == 2) {
-                    u32x4 v = *reinterpret_cast<const u32x4*>(krow + kk * M::kK + quad * 8);
-                    af = __builtin_bit_cast(bf16x8, v);
-                } else {
-                    af = reinterpret_cast<const float*>(krow)[kk * M::kK + quad];
+            for (int g0 = 0; g0 < NKK; g0 += KG) {
+                typename M::frag af[KG];
+#pragma unroll
+                for (int j = 0; j < KG; ++j) {
+                    const int kk = g0 + j;
+                    if constexpr (sizeof(T) == 2) {
+                        u32x4 v = *reinterpret_cast<const u32x4*>(krow + kk * M::kK + quad * 8);
+                        af[j] = __builtin_bit_cast(bf16x8, v);
+                    } else {
+                        af[j] = reinterpret_cast<const float*>(krow)[kk * M::kK + quad];
+                    }
                 }
-                if (kk & 1)
-                    c1v = M::mma(af, qf[kk], c1v);
-                else
-                    c0v = M::mma(af, qf[kk], c0v);
+                __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its MFMAs
+#pragma unroll
+                for (int j = 0; j < KG; ++j) {
+                    const int kk = g0 + j;
+                    if (kk & 1)
+                        c1v = M::mma(af[j], qf[kk], c1v);
+                    else
+                        c0v = M::mma(af[j], qf[kk], c0v);
+                }
             }
             s = c0v + c1v;
         }
@@ -484,12 +500,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int ks = 0; ks < kTile / 32; ++ks) {
+                // the step's P^T and V^T fragments are all read before its MFMAs
                 const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pbase + ks * 32 + quad * 8));
+                u32x4 vv[NMT];
 #pragma unroll
-                for (int t = 0; t < NMT; ++t) {
-                    const u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + (size_t)t * 16 * L::kStrideT + ks * 32 + quad * 8);
-                    acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv), pf, acc[t]);
-                }
+                for (int t = 0; t < NMT; ++t)
+                    vv[t] = *reinterpret_cast<const u32x4*>(vbase + (size_t)t * 16 * L::kStrideT + ks * 32 + quad * 8);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < NMT; ++t) acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv[t]), pf, acc[t]);
             }
         } else {
             // lane group q contracts rows 16q..16q+15 (one per step): 4 vector reads per operand
