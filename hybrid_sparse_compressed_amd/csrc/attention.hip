@@ -764,13 +764,22 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             for (int rb = 0; rb < 2; ++rb) {
                 f32x4 e0 = f32x4{0.f, 0.f, 0.f, 0.f}, e1 = f32x4{0.f, 0.f, 0.f, 0.f};
                 const T* krow = Ks + (size_t)(32 * half + 16 * rb + hl) * L::kStrideK;
+                constexpr int KG = NKK % 6 == 0 ? 6 : 1;  // K fragments read a group ahead
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(krow + kk * M::kK + quad * 8);
-                    if (kk & 1)
-                        e1 = M::mma(__builtin_bit_cast(bf16x8, v), qf[kk], e1);
-                    else
-                        e0 = M::mma(__builtin_bit_cast(bf16x8, v), qf[kk], e0);
+                for (int g0 = 0; g0 < NKK; g0 += KG) {
+                    u32x4 v[KG];
+#pragma unroll
+                    for (int j = 0; j < KG; ++j)
+                        v[j] = *reinterpret_cast<const u32x4*>(krow + (g0 + j) * M::kK + quad * 8);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < KG; ++j) {
+                        const int kk = g0 + j;
+                        if (kk & 1)
+                            e1 = M::mma(__builtin_bit_cast(bf16x8, v[j]), qf[kk], e1);
+                        else
+                            e0 = M::mma(__builtin_bit_cast(bf16x8, v[j]), qf[kk], e0);
+                    }
                 }
                 s[rb] = e0 + e1;
             }
@@ -837,10 +846,17 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 #pragma unroll
             for (int ks = 0; ks < kP64Rows / 32; ++ks) {
                 const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pbase + ks * 32 + quad * 8));
+                constexpr int VG = 4;  // V^T fragments read a group ahead of their MFMAs
 #pragma unroll
-                for (int t = 0; t < NMT; ++t) {
-                    const u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + (size_t)t * 16 * L::kStrideT + ks * 32 + quad * 8);
-                    acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv), pf, acc[t]);
+                for (int t0 = 0; t0 < NMT; t0 += VG) {
+                    u32x4 vv[VG];
+#pragma unroll
+                    for (int j = 0; j < VG; ++j)
+                        vv[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(t0 + j) * 16 * L::kStrideT + ks * 32 + quad * 8);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < VG; ++j)
+                        acc[t0 + j] = M::mma(__builtin_bit_cast(bf16x8, vv[j]), pf, acc[t0 + j]);
                 }
             }
             __syncthreads();  // the tile buffers are rewritten next
