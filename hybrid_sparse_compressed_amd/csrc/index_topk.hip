@@ -53,7 +53,7 @@ constexpr int kScoreRowsMulti = 2048;
 __device__ inline void clear_hist2_slice(uint8_t* ws, int q, int S_max, int k) {
     const int per = ceil_div(kBins, (int)gridDim.x);
     uint32_t* h2 = ws_of(ws, q, S_max, k).hist2;
-    for (int j = (int)threadIdx.x; j < per; j += (int)blockDim.x) {
+    for (int j = (int)threadIdx.x; j < per; j += kThreads) {  // every caller runs kThreads threads
         const int i = (int)blockIdx.x * per + j;
         if (i < kBins) h2[i] = 0;
     }
@@ -127,7 +127,6 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const int q = blockIdx.y;
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int sub = lane % LPR, rs = lane / LPR;
-    if constexpr (HIST) clear_hist2_slice(ws, q, S_max, k);
     const int bseq_raw = q_seq ? q_seq[q] : q;
     const int bseq = (bseq_raw < 0 || bseq_raw >= B) ? 0 : bseq_raw;
     const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)sub * V;
@@ -154,9 +153,29 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         }
     };
 
-    // first batch in flight before the candidate count and the head fold are known
+    // The head fold's first round of q_idx loads goes out first and the first
+    // key batch right after, so that waiting for the fold (loads retire in
+    // issue order) leaves the key batch in flight.  Loads are unconditional
+    // (clamped index, value zeroed after) so that none waits on another.
+    const int nchunks = H_I * LPR;
+    const T* qb = q_idx + (size_t)q * H_I * DI;
+    u32x4 f4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = tid + j * kThreads;
+        f4[j] = *reinterpret_cast<const u32x4*>(qb + (size_t)min(c, nchunks - 1) * V);
+    }
     u32x4 cur[U];
-    load_batch(cur, 0, r1m);
+    {   // the first batch in the clamped form: no branch, so the loads above
+        // keep an exact place in the in-order count
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + u * RPU + w * RPL + rs;
+            const int rc = r < r1m ? r : r1m - 1;
+            cur[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)rc * DI));
+        }
+    }
+    if constexpr (HIST) clear_hist2_slice(ws, q, S_max, k);
 
     int n = clamp_n(n_cand, q, S_max);
     if (bseq_raw < 0 || bseq_raw >= B) n = 0;
@@ -172,25 +191,33 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     // in a fixed order
     {
         const int ec = tid % LPR, grp = tid / LPR;
-        const int nchunks = H_I * LPR;
-        const T* qb = q_idx + (size_t)q * H_I * DI;
         float part[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) part[e] = 0.f;
-        for (int c0 = tid; c0 < nchunks; c0 += 4 * kThreads) {
-            u32x4 t4[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = c0 + j * kThreads;
-                t4[j] = c < nchunks ? *reinterpret_cast<const u32x4*>(qb + (size_t)c * V)
-                                    : u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 t = (tid + j * kThreads < nchunks) ? f4[j] : u32x4{0u, 0u, 0u, 0u};
+            float f[V];
+            Elem<T>::unpack(t, f);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float f[V];
-                Elem<T>::unpack(t4[j], f);
-#pragma unroll
-                for (int e = 0; e < V; ++e) part[e] += f[e];
+            for (int e = 0; e < V; ++e) part[e] += f[e];
+        }
+        if (nchunks > 4 * kThreads) {  // uniform; not taken at 64 heads x 128
+            for (int c0 = tid + 4 * kThreads; c0 < nchunks; c0 += 4 * kThreads) {
+                u32x4 t4[4];
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = c0 + j * kThreads;
+                    t4[j] = c < nchunks ? *reinterpret_cast<const u32x4*>(qb + (size_t)c * V)
+                                        : u32x4{0u, 0u, 0u, 0u};
+                }
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float f[V];
+                    Elem<T>::unpack(t4[j], f);
+    #pragma unroll
+                    for (int e = 0; e < V; ++e) part[e] += f[e];
+                }
             }
         }
 #pragma unroll
