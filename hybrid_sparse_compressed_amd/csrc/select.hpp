@@ -187,7 +187,7 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
     //    first kSpec of them are read before their count is known (they lie
     //    inside the segment's slots, so reading them is always in bounds)
     constexpr int SPT = kMaxSeg / kSelThreads;  // segments per thread in the scan (contiguous)
-    constexpr int kSpec = 8;
+    constexpr int kSpec = 12;
     int T_s = 1;
     while (T_s * 2 * R.nseg <= kSelThreads) T_s *= 2;
     R.T_s = T_s;
@@ -360,15 +360,38 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
             if (direct) return kk >= p2 + 1024u || ((kk & 0xfffffc00u) == p2 && L.flag[i] != 0);
             return kk > T || (kk == T && idx[i] <= imax);
         };
-        uint32_t cnt = 0;
-        for (int i = i0; i < i1; ++i) cnt += chosen(i);
+        // short list in LDS: at most kCandCap / kSelThreads = 16 entries per
+        // thread, whose chosen flags are read once (all reads in flight) into
+        // a mask; the flat copy keeps the two plain passes
+        constexpr int EMAX = kCandCap / kSelThreads;
+        static_assert(EMAX <= 32, "chosen mask is 32 bits");
+        uint32_t mask = 0, cnt = 0;
+        if (small) {
+#pragma unroll
+            for (int j = 0; j < EMAX; ++j) {
+                const int i = i0 + j;
+                if (i < i1 && chosen(i)) mask |= 1u << j;
+            }
+            cnt = (uint32_t)__popc(mask);
+        } else {
+            for (int i = i0; i < i1; ++i) cnt += chosen(i);
+        }
         uint32_t all;
         uint32_t pos = block_excl_scan<kSelThreads>(cnt, L.tmp, &all);
-        for (int i = i0; i < i1; ++i)
-            if (chosen(i)) {
-                if (pos < (uint32_t)kTopkMaxK) L.chs[pos] = (int32_t)idx[i];
+        if (small) {
+            while (mask) {
+                const int j = __ffs(mask) - 1;
+                mask &= mask - 1;
+                if (pos < (uint32_t)kTopkMaxK) L.chs[pos] = (int32_t)idx[i0 + j];
                 ++pos;
             }
+        } else {
+            for (int i = i0; i < i1; ++i)
+                if (chosen(i)) {
+                    if (pos < (uint32_t)kTopkMaxK) L.chs[pos] = (int32_t)idx[i];
+                    ++pos;
+                }
+        }
         if (tid == 0) L.misc[0] = all;
         __syncthreads();
         R.nch = min((int)L.misc[0], R.take - R.nsel);
