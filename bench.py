@@ -321,7 +321,43 @@ def other_rows(hsa, workloads):
     rows["a2_a3_a4_decode_c4_64k"] = _row("c4_decode_64k", us, "hbm", 5089280, "GB/s",
                                           HBM_PEAK_GBPS)
     del e
+    rows.update(append_rows(hsa, torch))
     torch.cuda.empty_cache()
+    return rows
+
+
+def append_rows(hsa, torch):
+    """Decode-time compression state: one token per sequence appended to its ring,
+    at the C4 decode batch (4 sequences, m=4) and the C128 one (32 sequences, m=128),
+    latent 576 bf16, both for a call that completes every sequence's block and for
+    one that does not.  Positions sit at the end of the long contexts."""
+    rows = {}
+    D = 576
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for B, m, n_blocks, key in ((4, 4, 262144, "c4"), (32, 128, 1024, "c128")):
+        rx = torch.randn(B, m, D, device="cuda", generator=g).to(torch.bfloat16)
+        rg = torch.randn(B, m, D, device="cuda", generator=g).to(torch.bfloat16)
+        xt = torch.randn(B, D, device="cuda", generator=g).to(torch.bfloat16)
+        gt = torch.randn(B, D, device="cuda", generator=g).to(torch.bfloat16)
+        bias = (torch.randn(m, D, device="cuda", generator=g) * 0.1).to(torch.bfloat16)
+        pool = torch.empty(B, n_blocks, D, dtype=torch.bfloat16, device="cuda")
+        last = (n_blocks - 1) * m
+        for tag, p in (("complete", last + m - 1), ("open", last)):
+            pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+            hsa.hsa_compress_append(xt, gt, bias, rx, rg, pos, pool)  # checks shapes once
+            # then straight through the C-ABI, so that the host's per-call cost of the
+            # Python checks does not pace a few-microsecond kernel
+            args = (hsa.HSA_BF16,) + tuple(t.data_ptr() for t in (xt, gt, bias, rx, rg, pos, pool)) \
+                + (B, D, m, n_blocks, torch.cuda.current_stream().cuda_stream)
+            us = _median_us(torch, lambda: hsa.lib.hsa_compress_append(*args), 7, 20)
+            # token in (x, g), ring slot out (x, g); on completion the other m-1 ring
+            # rows in, the entry out, and the bias once
+            per_seq = 4 * D * 2 + ((2 * (m - 1) + 1) * D * 2 if tag == "complete" else 0)
+            alg = B * per_seq + (m * D * 2 if tag == "complete" else 0)
+            rows["f1_compress_append_%s_%s" % (key, tag)] = _row(
+                "c4_decode_1m" if key == "c4" else "c128_dense_decode", us, "hbm", alg, "GB/s",
+                HBM_PEAK_GBPS)
+        del rx, rg, pool
     return rows
 
 

@@ -20,7 +20,8 @@ HSA_OK, HSA_ERR_INVALID_ARG, HSA_ERR_UNSUPPORTED, HSA_ERR_WORKSPACE, HSA_ERR_HIP
 HSA_F32, HSA_BF16 = 0, 1
 
 EXPORTED = (
-    "hsa_strerror", "hsa_version", "hsa_compress", "hsa_index_topk_workspace_size",
+    "hsa_strerror", "hsa_version", "hsa_compress", "hsa_compress_append",
+    "hsa_index_topk_workspace_size",
     "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
     "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
     "hsa_decode_sparse", "hsa_profile_enable", "hsa_profile_read",
@@ -49,6 +50,8 @@ def _load():
     lib.hsa_version.restype = I
     lib.hsa_compress.argtypes = [I, P, P, P, P, I32, I32, I32, I32, P]
     lib.hsa_compress.restype = I
+    lib.hsa_compress_append.argtypes = [I, P, P, P, P, P, P, P, I32, I32, I32, I32, P]
+    lib.hsa_compress_append.restype = I
     lib.hsa_index_topk_workspace_size.argtypes = [I32, I32, I32]
     lib.hsa_index_topk_workspace_size.restype = SZ
     lib.hsa_index_topk.argtypes = [I, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, U32, P, SZ, P]
@@ -155,6 +158,31 @@ def hsa_compress(x, gate, bias, m, out=None, stream=None):
     _check("hsa_compress", lib.hsa_compress(_dt(x), _ptr(x), _ptr(gate), _ptr(bias), _ptr(out),
                                             B, T, D, m, _stream(stream)))
     return out
+
+
+def hsa_compress_append(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, stream=None):
+    """Store each sequence's token into ring slot pos mod m; a token that
+    completes its block writes that block's entry to pool[b, pos // m].
+
+    x_tok, g_tok: [B, D]; bias: [m, D]; ring_x, ring_g: [B, m, D] (updated in
+    place); pos: [B] int32 (read only, < 0 = idle); pool: [B, S_max, D]."""
+    B, D = x_tok.shape
+    m = bias.shape[0]
+    S_max = pool.shape[1]
+    for t in (g_tok, bias, ring_x, ring_g, pool):
+        if t.dtype != x_tok.dtype:
+            raise TypeError("hsa_compress_append: all float tensors must share one dtype")
+    if (tuple(g_tok.shape) != (B, D) or tuple(bias.shape) != (m, D)
+            or tuple(ring_x.shape) != (B, m, D) or tuple(ring_g.shape) != (B, m, D)
+            or tuple(pool.shape) != (B, S_max, D) or tuple(pos.shape) != (B,)):
+        raise ValueError("hsa_compress_append: shape mismatch")
+    if pos.dtype != torch.int32:
+        raise TypeError("hsa_compress_append: pos must be int32")
+    _check("hsa_compress_append",
+           lib.hsa_compress_append(_dt(x_tok), _ptr(x_tok), _ptr(g_tok), _ptr(bias), _ptr(ring_x),
+                                   _ptr(ring_g), _ptr(pos), _ptr(pool), B, D, m, S_max,
+                                   _stream(stream)))
+    return pool
 
 
 def hsa_index_topk(q_idx, k_idx, n_cand, k, q_seq=None, scores=None, topk_idx=None,

@@ -341,7 +341,172 @@ hipError_t launch_compress_t(const void* x, const void* g, const void* bias, voi
     return launch_compress_p<T, 8, 2>(x, g, bias, out, B, T_len, D, m, st);
 }
 
+// ---- decode-time compression state ----
+// [NK "DeepSeek V4 的新架构", five state classes] and [KD "Arquitectura del
+// Sistema", compression-state ring buffers]: between block boundaries a
+// sequence's newest tokens wait in a ring of m slots; the token that fills
+// the last slot completes the block and its entry is formed.
+//
+// Workgroup (b, y) owns kAppendThreads / P consecutive chunks of sequence b;
+// thread (part j, chunk c).  Part-0 threads store the token's chunks into
+// slot pos mod m.  When the token completes its block, part j folds rows
+// j, j+P, j+2P, ... (kAppendRows of them in flight at a time) into a running
+// (max, sum, weighted sum) per channel, the completing row read from the
+// token itself, and the P partials of a chunk are merged in LDS in part order.
+// Different workgroups touch disjoint chunks, so nothing is shared between them.
+constexpr int kAppendThreads = 256;
+constexpr int kAppendRows = 4;
+
+template <typename T>
+__global__ __launch_bounds__(kAppendThreads) void compress_append_kernel(
+    const T* __restrict__ x_tok, const T* __restrict__ g_tok, const T* __restrict__ bias,
+    T* __restrict__ ring_x, T* __restrict__ ring_g, const int32_t* __restrict__ pos,
+    T* __restrict__ pool, int D, int m, int S_max, int parts) {
+    constexpr int V = Elem<T>::kPer16B;
+    __shared__ float part_max[V * kAppendThreads], part_sum[V * kAppendThreads],
+        part_acc[V * kAppendThreads];
+    const int b = blockIdx.x;
+    const int p = pos[b];
+    if (p < 0) return;  // idle sequence: takes no token
+    const int cw = kAppendThreads / parts;
+    const int part = threadIdx.x / cw;
+    const int cl = threadIdx.x - part * cw;
+    const int c = blockIdx.y * cw + cl;
+    const bool live = c < D / V;
+    const int s = p % m;
+    const size_t tok = (size_t)b * D + (size_t)c * V;
+    const size_t ring = (size_t)b * m * D + (size_t)c * V;
+    if (live && part == 0) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(x_tok + tok);
+        const u32x4 gv = *reinterpret_cast<const u32x4*>(g_tok + tok);
+        *reinterpret_cast<u32x4*>(ring_x + ring + (size_t)s * D) = xv;
+        *reinterpret_cast<u32x4*>(ring_g + ring + (size_t)s * D) = gv;
+    }
+    const int blk = p / m;
+    if (s != m - 1 || blk >= S_max) return;  // block still open, or past the pool
+
+    float mx[V], sm[V], acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        mx[e] = -INFINITY;
+        sm[e] = 0.f;
+        acc[e] = 0.f;
+    }
+    if (live) {
+        for (int r0 = part; r0 < m; r0 += kAppendRows * parts) {
+            u32x4 gw[kAppendRows], bw[kAppendRows], xw[kAppendRows];
+#pragma unroll
+            for (int k = 0; k < kAppendRows; ++k) {
+                const int r = r0 + k * parts;
+                if (r < m) {
+                    const bool own = r == s;  // the completing row is this call's token
+                    gw[k] = *reinterpret_cast<const u32x4*>(
+                        own ? g_tok + tok : ring_g + ring + (size_t)r * D);
+                    xw[k] = *reinterpret_cast<const u32x4*>(
+                        own ? x_tok + tok : ring_x + ring + (size_t)r * D);
+                    bw[k] = *reinterpret_cast<const u32x4*>(bias + (size_t)r * D + (size_t)c * V);
+                }
+            }
+            float z[kAppendRows][V];
+#pragma unroll
+            for (int k = 0; k < kAppendRows; ++k) {
+                if (r0 + k * parts < m) {
+                    float gv[V], bv[V];
+                    Elem<T>::unpack(gw[k], gv);
+                    Elem<T>::unpack(bw[k], bv);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) z[k][e] = (gv[e] + bv[e]) * kLog2e;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) z[k][e] = -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float gm = mx[e];
+#pragma unroll
+                for (int k = 0; k < kAppendRows; ++k) gm = fmaxf(gm, z[k][e]);
+                const float sc = exp2f(mx[e] - gm);  // 0 on the first group
+                float s_e = sm[e] * sc, a_e = acc[e] * sc;
+#pragma unroll
+                for (int k = 0; k < kAppendRows; ++k) {
+                    const float w = exp2f(z[k][e] - gm);  // 0 for rows past m
+                    s_e += w;
+                    if (r0 + k * parts < m) a_e = fmaf(w, chunk_elem<T>(xw[k], e), a_e);
+                }
+                mx[e] = gm;
+                sm[e] = s_e;
+                acc[e] = a_e;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        part_max[e * kAppendThreads + threadIdx.x] = mx[e];
+        part_sum[e * kAppendThreads + threadIdx.x] = sm[e];
+        part_acc[e * kAppendThreads + threadIdx.x] = acc[e];
+    }
+    __syncthreads();
+    // merge: one (channel element, chunk) pair per thread per pass, parts in order;
+    // the result overwrites part 0's weighted-sum slot
+    for (int q = threadIdx.x; q < V * cw; q += kAppendThreads) {
+        const int e = q / cw, ql = q - e * cw;
+        const int base = e * kAppendThreads + ql;
+        float gm = part_max[base];
+        for (int j = 1; j < parts; ++j) gm = fmaxf(gm, part_max[base + j * cw]);
+        float s_e = 0.f, a_e = 0.f;
+        for (int j = 0; j < parts; ++j) {
+            const float w = exp2f(part_max[base + j * cw] - gm);
+            s_e = fmaf(part_sum[base + j * cw], w, s_e);
+            a_e = fmaf(part_acc[base + j * cw], w, a_e);
+        }
+        part_max[base] = a_e / s_e;  // slot (e, part 0, ql) is read by its own thread only
+    }
+    __syncthreads();
+    if (live && part == 0) {
+        float res[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) res[e] = part_max[e * kAppendThreads + cl];
+        *reinterpret_cast<u32x4*>(pool + ((size_t)b * S_max + blk) * D + (size_t)c * V) =
+            pack16<T>(res);
+    }
+}
+
+// rows folded per thread: enough parts that each holds about kAppendRows rows
+int append_parts(int m) {
+    int want = std::min(32, (m + kAppendRows - 1) / kAppendRows);
+    int p = 1;
+    while (p * 2 <= want) p *= 2;
+    return p;
+}
+
+template <typename T>
+hipError_t launch_compress_append_t(const void* x_tok, const void* g_tok, const void* bias,
+                                    void* ring_x, void* ring_g, const int32_t* pos, void* pool,
+                                    int B, int D, int m, int S_max, hipStream_t st) {
+    const int parts = append_parts(m);
+    const int cw = kAppendThreads / parts;
+    const int nchunk = D / Elem<T>::kPer16B;
+    const int gy = (nchunk + cw - 1) / cw;
+    ProfScope prof(kProfCompress, st);
+    hipLaunchKernelGGL((compress_append_kernel<T>), dim3((unsigned)B, (unsigned)gy),
+                       dim3(kAppendThreads), 0, st, (const T*)x_tok, (const T*)g_tok,
+                       (const T*)bias, (T*)ring_x, (T*)ring_g, pos, (T*)pool, D, m, S_max, parts);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_compress_append(int dtype, const void* x_tok, const void* g_tok,
+                                  const void* bias, void* ring_x, void* ring_g,
+                                  const int32_t* pos, void* pool, int B, int D, int m, int S_max,
+                                  hipStream_t st) {
+    if (dtype == kF32)
+        return launch_compress_append_t<float>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B,
+                                               D, m, S_max, st);
+    return launch_compress_append_t<bf16_t>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D,
+                                            m, S_max, st);
+}
 
 hipError_t launch_compress(int dtype, const void* x, const void* g, const void* bias, void* out,
                            int B, int T_len, int D, int m, hipStream_t st) {

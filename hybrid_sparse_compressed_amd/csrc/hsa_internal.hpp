@@ -34,6 +34,12 @@ class ProfScope {
 // ---- compressor ----
 hipError_t launch_compress(int dtype, const void* x, const void* g, const void* bias, void* out,
                            int B, int T_len, int D, int m, hipStream_t st);
+// Decode-time compression state: one token per sequence into its ring, the
+// block's entry written to the pool when the token completes it.
+hipError_t launch_compress_append(int dtype, const void* x_tok, const void* g_tok,
+                                  const void* bias, void* ring_x, void* ring_g,
+                                  const int32_t* pos, void* pool, int B, int D, int m, int S_max,
+                                  hipStream_t st);
 
 // ---- indexer + top-k ----
 // Candidate lists up to this length are selected by one workgroup per query

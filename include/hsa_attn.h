@@ -84,6 +84,40 @@ int hsa_compress(int dtype, const void *x, const void *gate, const void *bias, v
                  int32_t B, int32_t T, int32_t D, int32_t m, void *stream);
 
 /*
+ * hsa_compress_append -- decode-time compression state, one token per sequence.
+ *
+ * [NK "DeepSeek V4 的新架构"]: besides the SWA, C4 and C128 pools a decoder
+ * keeps, for C4 and for C128, the in-flight tokens of the block not yet
+ * compressed; an entry is formed each time 4 (128) tokens have arrived.
+ * [KD "Arquitectura del Sistema"]: these compression states live in ring
+ * buffers of their own.
+ *
+ * For each sequence b with p = pos[b] >= 0 (the token's position: the number
+ * of tokens of b before it):
+ *   1. ring_x[b, p mod m, :] = x_tok[b, :];  ring_g[b, p mod m, :] = g_tok[b, :]
+ *   2. if p mod m == m - 1 (the token completes block i = p div m) and i < S_max:
+ *        pool[b, i, d] = sum_{j<m} softmax_j(ring_g[b, j, d] + bias[j, d]) * ring_x[b, j, d]
+ *      with the ring as left by step 1 -- the hsa_compress entry of that block.
+ * A sequence with pos[b] < 0 is left alone (its token is not read).  pos is
+ * read only: the caller advances its positions between calls.  Pool rows of
+ * blocks not completed by this call are not touched.
+ *
+ *   x_tok, g_tok   : [B, D]          dtype  (latent and gate logits of the new token)
+ *   bias           : [m, D]          dtype
+ *   ring_x, ring_g : [B, m, D]       dtype  in/out, owned by the caller, kept between
+ *                                           calls; slot j of an open block holds its
+ *                                           token at position (block start + j)
+ *   pos            : [B]             int32  device memory
+ *   pool           : [B, S_max, D]   dtype  out (completed rows only)
+ *   Sizes          : B >= 1, D >= 1 with D*sizeof(dtype) a multiple of 16, 1 <= m <= 1024,
+ *                    S_max >= 1.  Buffers must not overlap.  All float pointers 16-byte
+ *                    aligned (HSA_ERR_INVALID_ARG otherwise).
+ */
+int hsa_compress_append(int dtype, const void *x_tok, const void *g_tok, const void *bias,
+                        void *ring_x, void *ring_g, const int32_t *pos, void *pool, int32_t B,
+                        int32_t D, int32_t m, int32_t S_max, void *stream);
+
+/*
  * hsa_index_topk -- indexer scores and exact top-k select.
  *
  * [KD "Flujo de Inferencia", step "Indexer (TopK)"]: top-k over the

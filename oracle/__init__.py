@@ -116,19 +116,21 @@ def compress(x, gate, bias, m):
 def compress_append(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, m):
     """Decode-time compression state: append one token per sequence.
 
-    An entry of the compressed pool exists once the whole block of m tokens
-    behind it has arrived; until then the block's tokens wait in a per-sequence
-    ring.  State of sequence b: ring_x[b], ring_g[b] ([m, D]) hold the latents
-    and gate logits of the open block, slot = position mod m, and pos[b] counts
-    the tokens appended so far.  Appending at p = pos[b] stores the token in
-    slot p mod m; if that slot is the block's last one the ring holds tokens
-    p-m+1 .. p in order and compress() of it becomes pool[b, p div m] (unless
-    p div m is past the pool's last row); pos[b] becomes p + 1.  A sequence
-    with pos[b] < 0 is left untouched.
+    [NK "DeepSeek V4 的新架构", five state classes] and [KD "Arquitectura del
+    Sistema", compression-state ring buffers]: an entry of the compressed pool
+    exists once the whole block of m tokens behind it has arrived; until then
+    the block's tokens wait in a per-sequence ring.  State of sequence b:
+    ring_x[b], ring_g[b] ([m, D]) hold the latents and gate logits of the open
+    block, slot = position mod m.  The token of sequence b has position
+    p = pos[b] (tokens before it; the caller advances its positions).  It is
+    stored in slot p mod m; if that slot is the block's last one the ring holds
+    tokens p-m+1 .. p in order and compress() of it becomes pool[b, p div m]
+    (unless p div m is past the pool's last row).  A sequence with pos[b] < 0
+    takes no token.
 
     x_tok, g_tok: [B, D]; bias: [m, D]; ring_x, ring_g: [B, m, D], same element
     type as the tokens (CPU torch tensors or numpy arrays, updated in place);
-    pos: int32 [B] (updated in place); pool: float64 numpy [B, S_max, D].
+    pos: int32 [B]; pool: float64 numpy [B, S_max, D] (completed rows written).
     Returns the (b, row) pairs written to pool."""
     B = x_tok.shape[0]
     if tuple(ring_x.shape) != (B, m, x_tok.shape[1]) or tuple(ring_g.shape) != tuple(ring_x.shape):
@@ -143,7 +145,6 @@ def compress_append(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, m):
         if p % m == m - 1 and p // m < pool.shape[1]:
             pool[b, p // m] = compress(ring_x[b:b + 1], ring_g[b:b + 1], bias, m)[0, 0]
             written.append((b, p // m))
-        pos[b] = p + 1
     return written
 
 
