@@ -6,16 +6,20 @@ each, 64 heads over a 576-wide latent (value 512), window 128, indexer
 
 One step = one decode layer-step: indexer scores over every C4 key, exact
 radix top-512 select, and the SWA + selected-C4 attention with split-KV merge,
-all in one hsa_decode_sparse call (scoring, filter, attention that finishes
-the select, merge), and, on every 4th step, the compression of the 4
-just-completed 4-token blocks (hsa_compress).  Two copies of the
+together with the decode-time compression state update, all in one
+hsa_decode_step call (scoring; filter, with the compression-state append
+riding in the same launch; attention that finishes the select; merge): each
+sequence's new token enters its 4-token ring and on every 4th step completes
+the block, whose C4 entry is written to the pool before the attention runs.
+Two copies of the
 indexer inputs alternate between steps so the 268 MB key stream is larger
 than the on-die cache across a pair of steps.
 
 After the metric, "rows" measures every other row of the path at its own
 full-size workload (compressor, prefill indexer + top-k and prefill attention
-at prefill_32k, dense C128 decode, fused sparse decode at c4_decode_64k), each
-against its own roofline; --no-rows skips them.
+at prefill_32k, dense C128 decode, fused sparse decode at c4_decode_64k, the
+compression-state append at the C4 and C128 decode batches), each against its
+own roofline; --no-rows skips them.
 
 Prints ONE JSON line (rank 0).  --gpus N > 1 is not supported: the path is
 measured on one GPU.
@@ -97,11 +101,16 @@ def main():
     q_idx2 = torch.randn(w["q_idx"].shape, generator=g2, device=dev).to(torch.bfloat16)
     workloads.plant_duplicate_rows(k_idx2, c["dup_frac"], workloads._Draw(c["seed"] + 100, dev))
     sets = [(w["q_idx"], w["k_idx"]), (q_idx2, k_idx2)]
-    # decode-time compression of the block each sequence just completed
-    xb = torch.randn((B, 4, d_qk), generator=g2, device=dev).to(torch.bfloat16)
-    gb = torch.randn((B, 4, d_qk), generator=g2, device=dev).to(torch.bfloat16)
+    # decode-time compression state: every step appends each sequence's token to its
+    # 4-token ring; one step in four completes the block and writes its C4 entry
+    xt = torch.randn((B, d_qk), generator=g2, device=dev).to(torch.bfloat16)
+    gt = torch.randn((B, d_qk), generator=g2, device=dev).to(torch.bfloat16)
     bb = (torch.randn((4, d_qk), generator=g2, device=dev) * 0.1).to(torch.bfloat16)
-    cb = torch.empty((B, 1, d_qk), dtype=torch.bfloat16, device=dev)
+    ring_x = torch.randn((B, 4, d_qk), generator=g2, device=dev).to(torch.bfloat16)
+    ring_g = torch.randn((B, 4, d_qk), generator=g2, device=dev).to(torch.bfloat16)
+    # positions at the end of the context: the completed block's entry lands in the
+    # C4 pool's last row
+    pos4 = [torch.full((B,), 4 * (S - 1) + j, dtype=torch.int32, device=dev) for j in range(4)]
 
     stream = torch.cuda.current_stream()
     scores = torch.empty((B, S), dtype=torch.float32, device=dev)
@@ -113,11 +122,10 @@ def main():
 
     def step(i):
         qi, ki = sets[i & 1]
-        if i % 4 == 3:
-            hsa.hsa_compress(xb, gb, bb, 4, out=cb)
-        hsa.hsa_decode_sparse(qi, ki, w["n_cand"], k, w["q"], w["swa_kv"], w["swa_len"],
-                              w["comp_kv"], w["comp_len"], w["scale"], d_v, scores=scores,
-                              topk_idx=idx, out=out, lse=lse, workspace=ws)
+        hsa.hsa_decode_step(xt, gt, bb, ring_x, ring_g, pos4[i & 3], qi, ki, w["n_cand"], k,
+                            w["q"], w["swa_kv"], w["swa_len"], w["comp_kv"], w["comp_len"],
+                            w["scale"], d_v, scores=scores, topk_idx=idx, out=out, lse=lse,
+                            workspace=ws)
 
     if args.copy_calibration_mib > 0:
         copy_calibration(torch, dev, args.copy_calibration_mib)
@@ -245,6 +253,36 @@ def _median_us(torch, fn, reps, inner=1):
     return ts[len(ts) // 2]
 
 
+def _graph_us(torch, fn, reps, inner):
+    """Median time per call of fn() for calls of a few microseconds: `inner` calls are
+    captured once into a HIP graph (after one eager warm-up call), and each of the reps
+    measurements replays it, so the host's per-call cost does not set the pace."""
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1000.0 / inner)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
 def _row(workload, us, bound, alg, unit, peak, **extra):
     if unit == "GB/s":
         achieved = alg / (us * 1e-6) / 1e9
@@ -344,12 +382,8 @@ def append_rows(hsa, torch):
         last = (n_blocks - 1) * m
         for tag, p in (("complete", last + m - 1), ("open", last)):
             pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
-            hsa.hsa_compress_append(xt, gt, bias, rx, rg, pos, pool)  # checks shapes once
-            # then straight through the C-ABI, so that the host's per-call cost of the
-            # Python checks does not pace a few-microsecond kernel
-            args = (hsa.HSA_BF16,) + tuple(t.data_ptr() for t in (xt, gt, bias, rx, rg, pos, pool)) \
-                + (B, D, m, n_blocks, torch.cuda.current_stream().cuda_stream)
-            us = _median_us(torch, lambda: hsa.lib.hsa_compress_append(*args), 7, 20)
+            us = _graph_us(torch, lambda: hsa.hsa_compress_append(xt, gt, bias, rx, rg, pos, pool),
+                           7, 50)
             # token in (x, g), ring slot out (x, g); on completion the other m-1 ring
             # rows in, the entry out, and the bias once
             per_seq = 4 * D * 2 + ((2 * (m - 1) + 1) * D * 2 if tag == "complete" else 0)
@@ -364,6 +398,7 @@ def append_rows(hsa, torch):
 def cpu_baseline(w, min_seconds):
     """The oracle's whole decode layer-step (all sequences), repeated for ~min_seconds."""
     import numpy as np
+    import torch
 
     import oracle
 
@@ -374,8 +409,16 @@ def cpu_baseline(w, min_seconds):
     q, swa, comp = w["q"].cpu(), w["swa_kv"].cpu(), w["comp_kv"].cpu()
     n_cand = w["n_cand"].cpu().numpy()
     swa_len, comp_len = w["swa_len"].cpu().numpy(), w["comp_len"].cpu().numpy()
+    B, S, D = comp.shape
+    g = torch.Generator().manual_seed(5)
+    xt, gt = (torch.randn(B, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    bias = (torch.randn(4, D, generator=g) * 0.1).to(torch.bfloat16)
+    ring_x, ring_g = (torch.randn(B, 4, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    pool = np.zeros((B, S, D))  # zero pages: only the rows written get memory
     reps, t = 0, time.perf_counter()
     while True:
+        pos = np.full(B, 4 * (S - 1) + (reps & 3), np.int32)
+        oracle.compress_append(xt, gt, bias, ring_x, ring_g, pos, pool, 4)
         sc = oracle.index_scores(q_idx, k_idx, n_cand)
         idx = oracle.topk(sc.astype(np.float32), n_cand, k)
         oracle.attn_decode(q, swa, swa_len, comp, comp_len, w["scale"], c["d_v"], comp_idx=idx)
@@ -392,8 +435,9 @@ def cpu_baseline(w, min_seconds):
         cores = min(cores, int(omp))
     return {"value": round(reps / dt, 5), "unit": "layer-steps/s", "cores": cores,
             "kind": "oracle",
-            "sample": "%d repetition(s) of the whole c4_decode_1m layer-step (fp64 scores over all "
-                      "4 x 262,144 C4 keys, select, attention) in %.1f s" % (reps, dt)}
+            "sample": "%d repetition(s) of the whole c4_decode_1m layer-step (compression-state "
+                      "append, fp64 scores over all 4 x 262,144 C4 keys, select, attention) in "
+                      "%.1f s" % (reps, dt)}
 
 
 if __name__ == "__main__":

@@ -24,7 +24,7 @@ EXPORTED = (
     "hsa_index_topk_workspace_size",
     "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
     "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
-    "hsa_decode_sparse", "hsa_profile_enable", "hsa_profile_read",
+    "hsa_decode_sparse", "hsa_decode_step", "hsa_profile_enable", "hsa_profile_read",
 )
 HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
 
@@ -65,6 +65,8 @@ def _load():
     lib.hsa_decode_sparse_workspace_size.restype = SZ
     lib.hsa_decode_sparse.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, P] + [I32] * 9 + [F, P, SZ, P]
     lib.hsa_decode_sparse.restype = I
+    lib.hsa_decode_step.argtypes = [I] + [P] * 18 + [I32] * 9 + [F, P, SZ, P]
+    lib.hsa_decode_step.restype = I
     lib.hsa_attn_prefill_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.hsa_attn_prefill_workspace_size.restype = SZ
     lib.hsa_attn_prefill.argtypes = [I, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
@@ -283,6 +285,52 @@ def hsa_decode_sparse(q_idx, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("hsa_decode_sparse", lib.hsa_decode_sparse(
         _dt(q), _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
+        _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
+        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)))
+    return scores, topk_idx, out, lse
+
+
+def hsa_decode_step(x_tok, g_tok, bias, ring_x, ring_g, pos, q_idx, k_idx, n_cand, k, q, swa_kv,
+                    swa_len, comp_kv, comp_len, scale, d_v, scores=None, topk_idx=None, out=None,
+                    lse=None, workspace=None, stream=None):
+    """hsa_compress_append (C4: m = 4, into comp_kv) followed by hsa_decode_sparse, in
+    one call.  x_tok, g_tok: [B, d_qk]; bias: [4, d_qk]; ring_x, ring_g: [B, 4, d_qk]
+    (updated); pos: [B] int32 (read only); comp_kv: [B, S_max, d_qk] (completed rows
+    written); other arguments as hsa_decode_sparse.  Returns (scores, topk_idx, out, lse)."""
+    B, H_I, d_I = q_idx.shape
+    _, S_max, _ = k_idx.shape
+    _, H, d_qk = q.shape
+    W = swa_kv.shape[1]
+    if comp_kv.shape[1] != S_max or k_idx.dtype != q_idx.dtype or q.dtype != q_idx.dtype:
+        raise ValueError("hsa_decode_step: shape or dtype mismatch")
+    for t in (x_tok, g_tok, bias, ring_x, ring_g, comp_kv):
+        if t.dtype != q.dtype:
+            raise TypeError("hsa_decode_step: append tensors must have the query dtype")
+    if (tuple(x_tok.shape) != (B, d_qk) or tuple(g_tok.shape) != (B, d_qk)
+            or tuple(bias.shape) != (4, d_qk) or tuple(ring_x.shape) != (B, 4, d_qk)
+            or tuple(ring_g.shape) != (B, 4, d_qk) or tuple(pos.shape) != (B,)):
+        raise ValueError("hsa_decode_step: append shape mismatch")
+    if pos.dtype != torch.int32:
+        raise TypeError("hsa_decode_step: pos must be int32")
+    dev = q.device
+    n_cand, swa_len, comp_len = _i32(n_cand, dev), _i32(swa_len, dev), _i32(comp_len, dev)
+    if scores is None:
+        scores = torch.empty((B, S_max), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream() if stream is None else stream
+    need = lib.hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k)
+    if workspace is None:
+        workspace = Workspace.get("decode_sparse:%d:%d:%d:%d:%d" % (B, H, d_v, W, S_max * 4096 + k),
+                                  need, dev, st)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hsa_decode_step", lib.hsa_decode_step(
+        _dt(q), _ptr(x_tok), _ptr(g_tok), _ptr(bias), _ptr(ring_x), _ptr(ring_g), _ptr(pos),
+        _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
         _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
         d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)))
     return scores, topk_idx, out, lse

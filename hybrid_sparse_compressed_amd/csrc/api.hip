@@ -141,6 +141,64 @@ size_t hsa_decode_sparse_workspace_size(int32_t B, int32_t H, int32_t d_v, int32
     return round256(hsa::topk_workspace_bytes(B, S_max, k)) + hsa::decode_workspace_bytes(B, H, d_v, W + k);
 }
 
+namespace {
+
+// hsa_decode_sparse, preceded by the decode-time C4 append of `job` when it is
+// not null (its arguments already checked)
+int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const int32_t* n_cand,
+                       float* scores, int32_t* topk_idx, const void* q, const void* swa_kv,
+                       const int32_t* swa_len, const void* comp_kv, const int32_t* comp_len,
+                       void* out, float* lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
+                       int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
+                       float scale, void* workspace, size_t workspace_bytes, void* stream,
+                       const hsa::AppendJob* job) {
+    // indexer + select arguments (as hsa_index_topk with Nq = B, no q_seq)
+    if (!dtype_ok(dtype) || !q_idx || !k_idx || !n_cand || !scores || !topk_idx)
+        return HSA_ERR_INVALID_ARG;
+    if (B < 1 || H_I < 1 || d_I < 1 || S_max < 1 || k < 1 || k > hsa::kTopkMaxK)
+        return HSA_ERR_INVALID_ARG;
+    if (S_max > hsa::kTopkMaxSegments * 4096) return HSA_ERR_UNSUPPORTED;
+    if (!aligned16(q_idx) || !aligned16(k_idx)) return HSA_ERR_INVALID_ARG;
+    const int row_bytes = d_I * esize(dtype);
+    if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512) return HSA_ERR_UNSUPPORTED;
+    // attention arguments (as hsa_attn_decode, sparse mode)
+    if (!q || !swa_kv || !swa_len || !comp_kv || !comp_len || !out) return HSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(swa_kv) || !aligned16(out) || !aligned16(comp_kv))
+        return HSA_ERR_INVALID_ARG;
+    if (H < 1 || H > 1024 || d_qk < 1 || d_v < 1 || d_v > d_qk || W < 1) return HSA_ERR_INVALID_ARG;
+    if (!(scale == scale)) return HSA_ERR_INVALID_ARG;
+    if (!hsa::attn_shape_supported(dtype, d_qk, d_v)) return HSA_ERR_UNSUPPORTED;
+    const size_t need = hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k);
+    if (!workspace || workspace_bytes < need) return HSA_ERR_WORKSPACE;
+    hipStream_t st = as_stream(stream);
+    uint8_t* ws_sel = static_cast<uint8_t*>(workspace);
+    uint8_t* ws_attn = ws_sel + round256(hsa::topk_workspace_bytes(B, S_max, k));
+    if (S_max > hsa::kRowSelectCap && hsa::fused_decode_supported(B, H, W, k)) {
+        // the append rides in the filter launch, which ends before the attention
+        // reads the pool; scoring and filter never read it
+        hipError_t e = hsa::launch_index_filter(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
+                                                d_I, S_max, k, ws_sel, job, st);
+        if (e != hipSuccess) return finish(e);
+        return finish(hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len,
+                                                    n_cand, ws_sel, topk_idx, out, lse, B, H,
+                                                    d_qk, d_v, W, S_max, k, scale, ws_attn, st));
+    }
+    if (job) {
+        hipError_t e = hsa::launch_compress_append(dtype, job->x_tok, job->g_tok, job->bias,
+                                                   job->ring_x, job->ring_g, job->pos, job->pool,
+                                                   job->B, job->D, 4, job->S_max, st);
+        if (e != hipSuccess) return finish(e);
+    }
+    hipError_t e = hsa::launch_index_topk(dtype, q_idx, k_idx, B, nullptr, n_cand, scores,
+                                          topk_idx, B, H_I, d_I, S_max, k, ws_sel, st);
+    if (e != hipSuccess) return finish(e);
+    return finish(hsa::launch_attn_decode(dtype, q, swa_kv, swa_len, comp_kv, topk_idx,
+                                          comp_len, out, lse, B, H, d_qk, d_v, W, S_max, k,
+                                          scale, ws_attn, st));
+}
+
+}  // namespace
+
 int hsa_decode_sparse(int dtype, const void* q_idx, const void* k_idx, const int32_t* n_cand,
                       float* scores, int32_t* topk_idx, const void* q, const void* swa_kv,
                       const int32_t* swa_len, const void* comp_kv, const int32_t* comp_len,
@@ -148,41 +206,36 @@ int hsa_decode_sparse(int dtype, const void* q_idx, const void* k_idx, const int
                       int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
                       float scale, void* workspace, size_t workspace_bytes, void* stream) {
     try {
-        // indexer + select arguments (as hsa_index_topk with Nq = B, no q_seq)
-        if (!dtype_ok(dtype) || !q_idx || !k_idx || !n_cand || !scores || !topk_idx)
+        return decode_sparse_impl(dtype, q_idx, k_idx, n_cand, scores, topk_idx, q, swa_kv,
+                                  swa_len, comp_kv, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
+                                  W, S_max, k, scale, workspace, workspace_bytes, stream, nullptr);
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+int hsa_decode_step(int dtype, const void* x_tok, const void* g_tok, const void* bias,
+                    void* ring_x, void* ring_g, const int32_t* pos, const void* q_idx,
+                    const void* k_idx, const int32_t* n_cand, float* scores, int32_t* topk_idx,
+                    const void* q, const void* swa_kv, const int32_t* swa_len, void* comp_kv,
+                    const int32_t* comp_len, void* out, float* lse, int32_t B, int32_t H_I,
+                    int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max,
+                    int32_t k, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    try {
+        // append arguments (as hsa_compress_append with m = 4, pool = comp_kv, D = d_qk)
+        if (!dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!x_tok || !g_tok || !bias || !ring_x || !ring_g || !pos || !comp_kv)
             return HSA_ERR_INVALID_ARG;
-        if (B < 1 || H_I < 1 || d_I < 1 || S_max < 1 || k < 1 || k > hsa::kTopkMaxK)
+        if (!aligned16(x_tok) || !aligned16(g_tok) || !aligned16(bias) || !aligned16(ring_x) ||
+            !aligned16(ring_g) || !aligned16(comp_kv))
             return HSA_ERR_INVALID_ARG;
-        if (S_max > hsa::kTopkMaxSegments * 4096) return HSA_ERR_UNSUPPORTED;
-        if (!aligned16(q_idx) || !aligned16(k_idx)) return HSA_ERR_INVALID_ARG;
-        const int row_bytes = d_I * esize(dtype);
-        if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512) return HSA_ERR_UNSUPPORTED;
-        // attention arguments (as hsa_attn_decode, sparse mode)
-        if (!q || !swa_kv || !swa_len || !comp_kv || !comp_len || !out) return HSA_ERR_INVALID_ARG;
-        if (!aligned16(q) || !aligned16(swa_kv) || !aligned16(out) || !aligned16(comp_kv))
-            return HSA_ERR_INVALID_ARG;
-        if (H < 1 || H > 1024 || d_qk < 1 || d_v < 1 || d_v > d_qk || W < 1) return HSA_ERR_INVALID_ARG;
-        if (!(scale == scale)) return HSA_ERR_INVALID_ARG;
-        if (!hsa::attn_shape_supported(dtype, d_qk, d_v)) return HSA_ERR_UNSUPPORTED;
-        const size_t need = hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k);
-        if (!workspace || workspace_bytes < need) return HSA_ERR_WORKSPACE;
-        hipStream_t st = as_stream(stream);
-        uint8_t* ws_sel = static_cast<uint8_t*>(workspace);
-        uint8_t* ws_attn = ws_sel + round256(hsa::topk_workspace_bytes(B, S_max, k));
-        if (S_max > hsa::kRowSelectCap && hsa::fused_decode_supported(B, H, W, k)) {
-            hipError_t e = hsa::launch_index_filter(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
-                                                    d_I, S_max, k, ws_sel, st);
-            if (e != hipSuccess) return finish(e);
-            return finish(hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len,
-                                                        n_cand, ws_sel, topk_idx, out, lse, B, H,
-                                                        d_qk, d_v, W, S_max, k, scale, ws_attn, st));
-        }
-        hipError_t e = hsa::launch_index_topk(dtype, q_idx, k_idx, B, nullptr, n_cand, scores,
-                                              topk_idx, B, H_I, d_I, S_max, k, ws_sel, st);
-        if (e != hipSuccess) return finish(e);
-        return finish(hsa::launch_attn_decode(dtype, q, swa_kv, swa_len, comp_kv, topk_idx,
-                                              comp_len, out, lse, B, H, d_qk, d_v, W, S_max, k,
-                                              scale, ws_attn, st));
+        if (B < 1 || d_qk < 1 || S_max < 1) return HSA_ERR_INVALID_ARG;
+        if ((d_qk * esize(dtype)) % 16 != 0) return HSA_ERR_UNSUPPORTED;
+        const hsa::AppendJob job{x_tok, g_tok, bias, ring_x, ring_g, pos, comp_kv, B, d_qk, S_max};
+        return decode_sparse_impl(dtype, q_idx, k_idx, n_cand, scores, topk_idx, q, swa_kv,
+                                  swa_len, comp_kv, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
+                                  W, S_max, k, scale, workspace, workspace_bytes, stream, &job);
     } catch (...) {
         return HSA_ERR_HIP;
     }

@@ -21,6 +21,7 @@
 // Registers are kept at <= 128 per lane (four waves per SIMD): the latents
 // stay packed until their product is taken, and entries leave as one
 // 16-byte store per chunk.
+#include "compress_append.hpp"
 #include "hsa_common.hpp"
 #include "hsa_internal.hpp"
 
@@ -33,30 +34,6 @@ namespace hsa {
 namespace {
 
 constexpr int kCompressThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
-
-// V floats -> the 16 bytes of one chunk in the storage dtype
-template <typename T> __device__ __forceinline__ u32x4 pack16(const float* v);
-template <> __device__ __forceinline__ u32x4 pack16<float>(const float* v) {
-    return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                 __float_as_uint(v[3])};
-}
-template <> __device__ __forceinline__ u32x4 pack16<bf16_t>(const float* v) {
-    u32x4 r;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-        r[w] = (uint32_t)f32_to_bf16(v[2 * w]) | ((uint32_t)f32_to_bf16(v[2 * w + 1]) << 16);
-    return r;
-}
-
-// element e of a raw 16-byte chunk, widened to fp32
-template <typename T> __device__ __forceinline__ float chunk_elem(const u32x4& t, int e);
-template <> __device__ __forceinline__ float chunk_elem<float>(const u32x4& t, int e) {
-    return __uint_as_float(t[e]);
-}
-template <> __device__ __forceinline__ float chunk_elem<bf16_t>(const u32x4& t, int e) {
-    return (e & 1) ? __uint_as_float(t[e >> 1] & 0xffff0000u) : __uint_as_float(t[e >> 1] << 16);
-}
 
 // G rows of one chunk, as loaded: gate and latent words (the short-block
 // kernel holds its bias words apart), and gate, bias and latent words.
@@ -472,6 +449,29 @@ __global__ __launch_bounds__(kAppendThreads) void compress_append_kernel(
     }
 }
 
+// m = M <= 4 (the C4 case): one thread per chunk, the whole block in its
+// registers (append_short_chunk).
+template <typename T, int M>
+__global__ __launch_bounds__(kAppendThreads) void compress_append_short_kernel(
+    const T* x_tok, const T* g_tok, const T* bias, T* ring_x, T* ring_g, const int32_t* pos,
+    T* pool, int D, int S_max) {
+    append_short_chunk<T, M>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, D, S_max, blockIdx.x,
+                             blockIdx.y * kAppendThreads + threadIdx.x);
+}
+
+template <typename T, int M>
+hipError_t launch_append_short(const void* x_tok, const void* g_tok, const void* bias,
+                               void* ring_x, void* ring_g, const int32_t* pos, void* pool, int B,
+                               int D, int S_max, hipStream_t st) {
+    const int nchunk = D / Elem<T>::kPer16B;
+    const int gy = (nchunk + kAppendThreads - 1) / kAppendThreads;
+    ProfScope prof(kProfCompress, st);
+    hipLaunchKernelGGL((compress_append_short_kernel<T, M>), dim3((unsigned)B, (unsigned)gy),
+                       dim3(kAppendThreads), 0, st, (const T*)x_tok, (const T*)g_tok,
+                       (const T*)bias, (T*)ring_x, (T*)ring_g, pos, (T*)pool, D, S_max);
+    return hipGetLastError();
+}
+
 // rows folded per thread: enough parts that each holds about kAppendRows rows
 int append_parts(int m) {
     int want = std::min(32, (m + kAppendRows - 1) / kAppendRows);
@@ -484,9 +484,16 @@ template <typename T>
 hipError_t launch_compress_append_t(const void* x_tok, const void* g_tok, const void* bias,
                                     void* ring_x, void* ring_g, const int32_t* pos, void* pool,
                                     int B, int D, int m, int S_max, hipStream_t st) {
+    switch (m) {
+        case 1: return launch_append_short<T, 1>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+        case 2: return launch_append_short<T, 2>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+        case 3: return launch_append_short<T, 3>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+        case 4: return launch_append_short<T, 4>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+        default: break;
+    }
+    const int nchunk = D / Elem<T>::kPer16B;
     const int parts = append_parts(m);
     const int cw = kAppendThreads / parts;
-    const int nchunk = D / Elem<T>::kPer16B;
     const int gy = (nchunk + cw - 1) / cw;
     ProfScope prof(kProfCompress, st);
     hipLaunchKernelGGL((compress_append_kernel<T>), dim3((unsigned)B, (unsigned)gy),

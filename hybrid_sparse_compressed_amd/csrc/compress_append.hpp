@@ -1,0 +1,100 @@
+// compress_append.hpp -- compressor helpers shared by compress.hip and the
+// decode layer-step kernels: chunk packing/widening and the short-block
+// decode-time append of one (sequence, 16-byte channel chunk).
+#pragma once
+
+#include "hsa_common.hpp"
+
+namespace hsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// V floats -> the 16 bytes of one chunk in the storage dtype
+template <typename T> __device__ __forceinline__ u32x4 pack16(const float* v);
+template <> __device__ __forceinline__ u32x4 pack16<float>(const float* v) {
+    return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                 __float_as_uint(v[3])};
+}
+template <> __device__ __forceinline__ u32x4 pack16<bf16_t>(const float* v) {
+    u32x4 r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        r[w] = (uint32_t)f32_to_bf16(v[2 * w]) | ((uint32_t)f32_to_bf16(v[2 * w + 1]) << 16);
+    return r;
+}
+
+// element e of a raw 16-byte chunk, widened to fp32
+template <typename T> __device__ __forceinline__ float chunk_elem(const u32x4& t, int e);
+template <> __device__ __forceinline__ float chunk_elem<float>(const u32x4& t, int e) {
+    return __uint_as_float(t[e]);
+}
+template <> __device__ __forceinline__ float chunk_elem<bf16_t>(const u32x4& t, int e) {
+    return (e & 1) ? __uint_as_float(t[e >> 1] & 0xffff0000u) : __uint_as_float(t[e >> 1] << 16);
+}
+
+// Decode-time compression state, block length M <= 4 (the C4 case), for chunk
+// c of sequence b ([NK "DeepSeek V4 的新架构", five state classes]; [KD
+// "Arquitectura del Sistema", compression-state ring buffers]).  The token at
+// position p = pos[b] goes to ring slot p mod M; when it is the block's last
+// token the block's entry, sum_j softmax_j(g_j + bias_j) * x_j per channel
+// (fp32, base-2 exponentials), is written to pool row p div M if that row
+// exists.  p < 0: nothing.
+//
+// One thread holds the whole block.  No load address depends on the position:
+// the token, the ring's first M-1 rows (the completing token is always row
+// M-1) and the bias are requested together with pos[b], so a call costs one
+// memory round trip; when the token does not complete its block the ring and
+// bias words are dropped.  The empty asm with a memory clobber keeps those
+// loads in front of the position test (otherwise the compiler issues pos[b]
+// first and moves the other loads behind the branch on it); for that the
+// pointers must not be __restrict__, whose loads the compiler moves past any
+// barrier.
+template <typename T, int M>
+__device__ __forceinline__ void append_short_chunk(const T* x_tok, const T* g_tok, const T* bias,
+                                                   T* ring_x, T* ring_g, const int32_t* pos,
+                                                   T* pool, int D, int S_max, int b, int c) {
+    constexpr int V = Elem<T>::kPer16B;
+    if (c >= D / V) return;  // a chunk past the row
+    const size_t tok = (size_t)b * D + (size_t)c * V;
+    const size_t ring = (size_t)b * M * D + (size_t)c * V;
+    u32x4 xw[M], gw[M], bw[M];  // row M-1 is the token
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        const T* sg = r == M - 1 ? g_tok + tok : ring_g + ring + (size_t)r * D;
+        const T* sx = r == M - 1 ? x_tok + tok : ring_x + ring + (size_t)r * D;
+        gw[r] = *reinterpret_cast<const u32x4*>(sg);
+        xw[r] = *reinterpret_cast<const u32x4*>(sx);
+        bw[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)r * D + (size_t)c * V);
+    }
+    asm volatile("" ::: "memory");
+    const int p = pos[b];
+    if (p < 0) return;  // idle sequence
+    const int s = p % M;
+    *reinterpret_cast<u32x4*>(ring_x + ring + (size_t)s * D) = xw[M - 1];
+    *reinterpret_cast<u32x4*>(ring_g + ring + (size_t)s * D) = gw[M - 1];
+    const int blk = p / M;
+    if (s != M - 1 || blk >= S_max) return;
+    float res[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float z[M];
+#pragma unroll
+        for (int r = 0; r < M; ++r)
+            z[r] = (chunk_elem<T>(gw[r], e) + chunk_elem<T>(bw[r], e)) * kLog2e;
+        float gm = z[0];
+#pragma unroll
+        for (int r = 1; r < M; ++r) gm = fmaxf(gm, z[r]);
+        float sm = 0.f, acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            const float w = exp2f(z[r] - gm);
+            sm += w;
+            acc = fmaf(w, chunk_elem<T>(xw[r], e), acc);
+        }
+        res[e] = acc / sm;
+    }
+    *reinterpret_cast<u32x4*>(pool + ((size_t)b * S_max + blk) * D + (size_t)c * V) =
+        pack16<T>(res);
+}
+
+}  // namespace hsa

@@ -53,11 +53,24 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
                              const int32_t* q_seq, const int32_t* n_cand, float* scores,
                              int32_t* topk_idx, int Nq, int H_I, int d_I, int S_max, int k,
                              void* ws, hipStream_t st);
+// A decode-time C4 append (block length 4) handed to a decode layer-step:
+// the arguments of launch_compress_append with m = 4.
+struct AppendJob {
+    const void* x_tok;
+    const void* g_tok;
+    const void* bias;
+    void* ring_x;
+    void* ring_g;
+    const int32_t* pos;
+    void* pool;
+    int B, D, S_max;
+};
 // Scoring (with the first-digit histogram) and the filter kernel only, for
 // S_max > kRowSelectCap: the select is finished by the fused decode attention.
+// job != nullptr: the append runs as extra workgroups of the filter launch.
 hipError_t launch_index_filter(int dtype, const void* q_idx, const void* k_idx, int B,
                                const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
-                               int S_max, int k, void* ws, hipStream_t st);
+                               int S_max, int k, void* ws, const AppendJob* job, hipStream_t st);
 
 // ---- attention ----
 struct DecodePlan {

@@ -33,9 +33,12 @@
 //    into the output and zeroes what the call wrote in the workspace.  The
 //    kernel boundaries order every hand-off, so no workgroup waits on or
 //    fences for another.
+#include "compress_append.hpp"
 #include "hsa_common.hpp"
 #include "hsa_internal.hpp"
 #include "select.hpp"
+
+#include <type_traits>
 
 namespace hsa {
 
@@ -680,14 +683,33 @@ static_assert(kPerThread == 16, "per-thread masks and counts are 16 bits wide");
 // bin, so one block prefix sum over (selected, short) counts places every
 // entry in index order.  Segment g's short list goes to cand_[4096 g ...),
 // its selected indices right after it, and its two counts to seg[g].
+//
+// AP != 0: grid rows y >= Nq carry a decode-time C4 append (AP = 1: fp32,
+// 2: bf16), one (sequence, 256-chunk span) per workgroup; it touches only the
+// append's own buffers, so it runs beside the filter in the same launch.
+template <int AP>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ n_cand,
                                                                uint8_t* __restrict__ ws, int S_max,
-                                                               int k) {
+                                                               int k, int Nq, AppendJob job) {
     __shared__ __align__(16) uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
     static_assert(kBins == 8 * kThreads, "two 16-byte histogram loads per thread");
 
+    if constexpr (AP != 0) {
+        if ((int)blockIdx.y >= Nq) {
+            using AT = typename std::conditional<AP == 1, float, bf16_t>::type;
+            const int spans = (job.D / Elem<AT>::kPer16B + kThreads - 1) / kThreads;
+            const int j = ((int)blockIdx.y - Nq) * (int)gridDim.x + (int)blockIdx.x;
+            if (j < job.B * spans)
+                append_short_chunk<AT, 4>(
+                    static_cast<const AT*>(job.x_tok), static_cast<const AT*>(job.g_tok),
+                    static_cast<const AT*>(job.bias), static_cast<AT*>(job.ring_x),
+                    static_cast<AT*>(job.ring_g), job.pos, static_cast<AT*>(job.pool), job.D,
+                    job.S_max, j / spans, (j % spans) * kThreads + threadIdx.x);
+            return;
+        }
+    }
     const int q = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
     const int n = clamp_n(n_cand, q, S_max);
@@ -826,7 +848,8 @@ size_t topk_workspace_bytes(int Nq, int S_max, int k) {
 
 hipError_t launch_index_filter(int dtype, const void* q_idx, const void* k_idx, int B,
                                const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
-                               int S_max, int k, void* ws, hipStream_t st) {
+                               int S_max, int k, void* ws, const AppendJob* job,
+                               hipStream_t st) {
     uint8_t* w = static_cast<uint8_t*>(ws);
     hipError_t e = dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
                                                          Nq, H_I, S_max, k, true, st)
@@ -834,8 +857,21 @@ hipError_t launch_index_filter(int dtype, const void* q_idx, const void* k_idx, 
                                                           w, Nq, H_I, S_max, k, true, st);
     if (e != hipSuccess) return e;
     ProfScope prof(kProfSelect, st);
-    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)n_segments(S_max), (unsigned)Nq), dim3(kThreads),
-                       0, st, scores, n_cand, w, S_max, k);
+    const int G = n_segments(S_max);
+    if (job) {
+        const int V = dtype == kF32 ? 4 : 8;
+        const int units = job->B * ((job->D / V + kThreads - 1) / kThreads);
+        const unsigned rows = (unsigned)((units + G - 1) / G);
+        if (dtype == kF32)
+            hipLaunchKernelGGL(topk_filter_kernel<1>, dim3((unsigned)G, (unsigned)Nq + rows),
+                               dim3(kThreads), 0, st, scores, n_cand, w, S_max, k, Nq, *job);
+        else
+            hipLaunchKernelGGL(topk_filter_kernel<2>, dim3((unsigned)G, (unsigned)Nq + rows),
+                               dim3(kThreads), 0, st, scores, n_cand, w, S_max, k, Nq, *job);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(topk_filter_kernel<0>, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0, st,
+                       scores, n_cand, w, S_max, k, Nq, AppendJob{});
     return hipGetLastError();
 }
 
@@ -884,8 +920,8 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
                            n_cand, topk_idx, S_max, k);
     } else {
         const int G = ceil_div(S_max, kFilterChunk);
-        hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0,
-                           st, scores, n_cand, w, S_max, k);
+        hipLaunchKernelGGL(topk_filter_kernel<0>, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0,
+                           st, scores, n_cand, w, S_max, k, Nq, AppendJob{});
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)Nq), dim3(kThreads), 0, st, n_cand,
                            topk_idx, w, S_max, k);

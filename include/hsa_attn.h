@@ -238,6 +238,37 @@ int hsa_decode_sparse(int dtype, const void *q_idx, const void *k_idx, const int
                       float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * hsa_decode_step -- the C4 decode layer-step with its compression-state
+ * update: the new token of every sequence enters its C4 ring (and completes
+ * a block every 4th position), then indexer, select and attention run.
+ *
+ * [NK "DeepSeek V4 的新架构", five state classes]: SWA and C4 pools plus the
+ * in-flight C4 block; [KD "Arquitectura del Sistema", Hierarchical
+ * Multi-Stream Overlap]: attention preparation overlapped with other work --
+ * here the append runs inside the launch that finishes the candidate filter.
+ *
+ * Results equal hsa_compress_append(dtype, x_tok, g_tok, bias, ring_x,
+ * ring_g, pos, comp_kv, B, d_qk, 4, S_max) followed by hsa_decode_sparse(...)
+ * with the remaining arguments: a block completed by this call's token is in
+ * comp_kv before the attention reads it (whether the attention selects it
+ * depends on comp_len and n_cand, which the caller sets).
+ *
+ *   x_tok, g_tok, bias, ring_x, ring_g, pos: as hsa_compress_append with
+ *              m = 4, D = d_qk; bias is [4, d_qk].
+ *   comp_kv  : [B, S_max, d_qk], the C4 pool: read by the attention, its
+ *              completed-block rows written by the append.
+ *   Other arguments, workspace and limits: as hsa_decode_sparse.
+ */
+int hsa_decode_step(int dtype, const void *x_tok, const void *g_tok, const void *bias,
+                    void *ring_x, void *ring_g, const int32_t *pos, const void *q_idx,
+                    const void *k_idx, const int32_t *n_cand, float *scores, int32_t *topk_idx,
+                    const void *q, const void *swa_kv, const int32_t *swa_len, void *comp_kv,
+                    const int32_t *comp_len, void *out, float *lse, int32_t B, int32_t H_I,
+                    int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max,
+                    int32_t k, float scale, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
  * hsa_attn_prefill -- a chunk of n_q consecutive query positions per
  * sequence, each with its own causal SWA window and its own compressed rows.
  *
