@@ -173,15 +173,16 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
     hipStream_t st = as_stream(stream);
     uint8_t* ws_sel = static_cast<uint8_t*>(workspace);
     uint8_t* ws_attn = ws_sel + round256(hsa::topk_workspace_bytes(B, S_max, k));
-    if (S_max > hsa::kRowSelectCap && hsa::fused_decode_supported(B, H, W, k)) {
-        // the append rides in the filter launch, which ends before the attention
-        // reads the pool; scoring and filter never read it
-        hipError_t e = hsa::launch_index_filter(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
-                                                d_I, S_max, k, ws_sel, job, st);
+    if (S_max > hsa::kRowSelectCap && hsa::index_lists_apply(S_max, k) &&
+        hsa::fused_decode_supported(B, H, W, k)) {
+        // the append rides in the scoring launch, which ends before the attention
+        // reads the pool; scoring never reads it
+        hipError_t e = hsa::launch_index_lists(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
+                                               d_I, S_max, k, ws_sel, job, st);
         if (e != hipSuccess) return finish(e);
         return finish(hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len,
-                                                    n_cand, ws_sel, topk_idx, out, lse, B, H,
-                                                    d_qk, d_v, W, S_max, k, scale, ws_attn, st));
+                                                    n_cand, ws_sel, scores, topk_idx, out, lse, B,
+                                                    H, d_qk, d_v, W, S_max, k, scale, ws_attn, st));
     }
     if (job) {
         hipError_t e = hsa::launch_compress_append(dtype, job->x_tok, job->g_tok, job->bias,

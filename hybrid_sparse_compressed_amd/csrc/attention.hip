@@ -91,7 +91,8 @@ template <> struct Pair<float> {
 
 struct AttnArgs {
     const void* q;
-    uint8_t* sel_ws;      // fused decode: top-k workspace (filter output)
+    uint8_t* sel_ws;      // fused decode: top-k workspace (histogram, candidate lists)
+    const float* scores;  // fused decode: [B, S_max] indexer scores (the select's fallback)
     const int32_t* n_cand;
     int32_t* topk_out;    // fused decode: [B, k] ascending top-k indices
     const void* win;      // decode: swa ring [B, W, d_qk]; prefill: token kv [n_seq, T, d_qk]
@@ -134,6 +135,9 @@ constexpr int kModeDecode = 0, kModePrefill = 1, kModeFused = 2;
 constexpr size_t kSelLdsBytes = (size_t)sel::kBins * 4 + (2 * sel::kSelNW + 2) * 4 + 3 * (size_t)sel::kMaxSeg * 4 +
                                 2 * (size_t)sel::kCandCap * 4 + 2 * (size_t)kTopkMaxK * 4 + 16 +
                                 3 * (size_t)sel::kSelThreads * 4 + (size_t)sel::kCandCap;
+// LDS of the list entries one read round of the fused select stages (after the above)
+constexpr size_t kSelStageOff = (kSelLdsBytes + 15) & ~(size_t)15;
+constexpr size_t kSelStageBytes = (size_t)sel::kSelThreads * 16 * 16;
 __device__ inline sel::SelLds sel_lds_at(unsigned char* base) {
     sel::SelLds L;
     uint32_t* p = reinterpret_cast<uint32_t*>(base);
@@ -149,6 +153,7 @@ __device__ inline sel::SelLds sel_lds_at(unsigned char* base) {
     L.mem = p; p += 3 * sel::kSelThreads;
     L.tmp = p; p += 2 * sel::kSelNW + 2;
     L.flag = reinterpret_cast<uint8_t*>(p);
+    L.stage = reinterpret_cast<u32x4*>(base + kSelStageOff);
     return L;
 }
 
@@ -230,11 +235,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         const int n = sel::clamp_n(a.n_cand, b, a.S_max);
         if ((int)blockIdx.x == a.n_split) {  // the sequence's ascending top-k output
             if (hb != 0) return;
-            const sel::SelResult R = sel::select_query(Wq, n, a.S_max, a.k, a.k, SL);
+            const sel::SelResult R = sel::select_query_lists(
+                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, a.k, SL);
             sel::select_write_sorted(SL, R, a.topk_out + (size_t)b * a.k, a.k);
-            // the first-digit histogram's readers (the filter) are done: clear it for
-            // the next call's scoring (the score kernel clears the second digit's)
-            for (int i = tid; i < sel::kBins; i += kAttnThreads) Wq.hist[i] = 0;
             return;
         }
     }
@@ -307,7 +310,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         if (vr1 > a.W) {  // uniform: this workgroup has compressed rows
             f_j0 = max(0, vr0 - a.W);
             const int j1 = min(a.k, vr1 - a.W);
-            const sel::SelResult R = sel::select_query(Wq, n, a.S_max, a.k, j1, SL);
+            const sel::SelResult R = sel::select_query_lists(
+                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, j1, SL);
             f_jn = j1 - f_j0;
             for (int t = tid; t < f_jn; t += kAttnThreads) {
                 const int j = f_j0 + t;
@@ -901,7 +905,8 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
                                                          const float* __restrict__ part_o,
                                                          void* __restrict__ out,
                                                          float* __restrict__ lse, int H,
-                                                         int n_split) {
+                                                         int n_split, uint8_t* __restrict__ sel_ws,
+                                                         int S_max, int k) {
     constexpr int kBatch = 16;  // split partials loaded per round
     auto load4 = [](const float* p) -> f32x4 { return *reinterpret_cast<const f32x4*>(p); };
     __shared__ float wsp[kMaxSplit], lsp[kMaxSplit];
@@ -968,12 +973,18 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
         for (int e = 0; e < 4; ++e) Elem<T>::store(o, d + e, acc[e] * inv);
     }
     if (lse && tid == 0) lse[(size_t)b * H + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    // fused decode: every reader of the sequence's first-digit histogram (the
+    // attention workgroups) has finished; clear it for the next call's scoring
+    if (sel_ws && h == 0) {
+        uint32_t* hist = sel::ws_of(sel_ws, b, S_max, k).hist;
+        for (int i = tid; i < sel::kBins; i += 128) hist[i] = 0;
+    }
 }
 
 template <typename T, int DQK, int DV, int MODE>
 hipError_t launch_attn_kernel(const AttnArgs& a, dim3 grid, hipStream_t st) {
     size_t lds = TileLds<T, DQK, DV>::kBytes;
-    if (MODE == kModeFused && lds < kSelLdsBytes) lds = kSelLdsBytes;
+    if (MODE == kModeFused && lds < kSelStageOff + kSelStageBytes) lds = kSelStageOff + kSelStageBytes;
     static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
@@ -1084,11 +1095,14 @@ static hipError_t launch_merge(int dtype, int d_v, const AttnArgs& a, int B, int
     ProfScope prof(kProfMerge, st);
     if (dtype == kBF16) {
         if (d_v == 512)
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split);
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split,
+                               a.sel_ws, S_max, k);
         else
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split);
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split,
+                               a.sel_ws, S_max, k);
     } else {
-        hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split);
+        hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split,
+                               a.sel_ws, S_max, k);
     }
     return hipGetLastError();
 }
@@ -1146,7 +1160,7 @@ bool fused_decode_supported(int B, int H, int W, int k) {
 hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv,
                                     const int32_t* swa_len, const void* comp_kv,
                                     const int32_t* comp_len, const int32_t* n_cand, void* sel_ws,
-                                    int32_t* topk_out, void* out, float* lse, int B, int H,
+                                    const float* scores, int32_t* topk_out, void* out, float* lse, int B, int H,
                                     int d_qk, int d_v, int W, int S_max, int k, float scale,
                                     void* ws, hipStream_t st) {
     AttnArgs a = {};
@@ -1157,6 +1171,7 @@ hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv
     a.comp_idx = nullptr;
     a.comp_len = comp_len;
     a.sel_ws = static_cast<uint8_t*>(sel_ws);
+    a.scores = scores;
     a.n_cand = n_cand;
     a.topk_out = topk_out;
     a.out = out;

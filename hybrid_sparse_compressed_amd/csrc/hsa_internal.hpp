@@ -65,12 +65,14 @@ struct AppendJob {
     void* pool;
     int B, D, S_max;
 };
-// Scoring (with the first-digit histogram) and the filter kernel only, for
-// S_max > kRowSelectCap: the select is finished by the fused decode attention.
-// job != nullptr: the append runs as extra workgroups of the filter launch.
-hipError_t launch_index_filter(int dtype, const void* q_idx, const void* k_idx, int B,
-                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
-                               int S_max, int k, void* ws, const AppendJob* job, hipStream_t st);
+// Scoring with the first-digit histogram and each scoring workgroup's
+// candidate list, for S_max > kRowSelectCap where sel::lists_apply holds: the
+// select is finished by the fused decode attention.  job != nullptr: the
+// append runs as extra workgroups of the same launch.
+bool index_lists_apply(int S_max, int k);
+hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
+                              const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
+                              int S_max, int k, void* ws, const AppendJob* job, hipStream_t st);
 
 // ---- attention ----
 struct DecodePlan {
@@ -86,14 +88,15 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
                               const int32_t* comp_idx, const int32_t* comp_len, void* out,
                               float* lse, int B, int H, int d_qk, int d_v, int W, int S_max,
                               int k, float scale, void* ws, hipStream_t st);
-// Fused sparse decode after launch_index_filter (one query per sequence):
-// finishes the select inside the attention kernel, writes topk_out ascending,
-// and zeroes the select workspace in the merge kernel.
+// Fused sparse decode after launch_index_lists (one query per sequence):
+// finishes the select inside the attention kernel (from the lists, or from
+// the score rows when a list is short), writes topk_out ascending, and clears
+// the first-digit histogram in the merge kernel.
 bool fused_decode_supported(int B, int H, int W, int k);
 hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv,
                                     const int32_t* swa_len, const void* comp_kv,
                                     const int32_t* comp_len, const int32_t* n_cand, void* sel_ws,
-                                    int32_t* topk_out, void* out, float* lse, int B, int H,
+                                    const float* scores, int32_t* topk_out, void* out, float* lse, int B, int H,
                                     int d_qk, int d_v, int W, int S_max, int k, float scale,
                                     void* ws, hipStream_t st);
 hipError_t launch_attn_prefill(int dtype, const void* q, const void* kv, const void* comp_kv,

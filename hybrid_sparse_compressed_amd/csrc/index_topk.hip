@@ -109,11 +109,17 @@ __device__ __forceinline__ float reduce_scatter8(float (&v)[8], int sub) {
     return r;  // the row (sub >> (LB - 3)) of the batch
 }
 
-template <typename T, int LPR, bool HIST>
+// SEL: 0 scores only; 1 also the first-digit histogram; 2 also the
+// workgroup's candidate list (select.hpp), and grid rows y >= Nq carry the
+// decode-time C4 append of `job` (one (sequence, 256-chunk span) per
+// workgroup; it touches only the append's own buffers).
+template <typename T, int LPR, int SEL>
 __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ n_cand, float* __restrict__ scores, uint8_t* __restrict__ ws,
-    int B, int H_I, int S_max, int k, int rows_per_wg) {
+    int B, int H_I, int S_max, int k, int rows_per_wg, int Nq, AppendJob job) {
+    constexpr bool HIST = SEL >= 1;
+    constexpr bool LIST = SEL == 2;
     constexpr int V = Elem<T>::kPer16B;
     constexpr int DI = LPR * V;            // indexer width
     constexpr int RPL = kWave / LPR;       // rows covered by one wave-wide load
@@ -125,8 +131,23 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     __shared__ float qpart[NG][DI];
     __shared__ float qsum[DI];
     __shared__ uint32_t hist[HIST ? kBins : 1];
+    __shared__ uint32_t scan_tmp[LIST ? kNW + 2 : 1];
+    __shared__ uint32_t cut_res;
     extern __shared__ __align__(16) float stage[];  // this workgroup's scores (rows_per_wg)
 
+    if constexpr (LIST) {
+        if ((int)blockIdx.y >= Nq) {
+            const int spans = (job.D / Elem<T>::kPer16B + kThreads - 1) / kThreads;
+            const int j = ((int)blockIdx.y - Nq) * (int)gridDim.x + (int)blockIdx.x;
+            if (j < job.B * spans)
+                append_short_chunk<T, 4>(
+                    static_cast<const T*>(job.x_tok), static_cast<const T*>(job.g_tok),
+                    static_cast<const T*>(job.bias), static_cast<T*>(job.ring_x),
+                    static_cast<T*>(job.ring_g), job.pos, static_cast<T*>(job.pool), job.D,
+                    job.S_max, j / spans, (j % spans) * kThreads + threadIdx.x);
+            return;
+        }
+    }
     const int q = blockIdx.y;
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int sub = lane % LPR, rs = lane / LPR;
@@ -185,6 +206,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const int r1 = min(n, r0 + rows_per_wg);
     if (r0 >= r1) {  // uniform over the workgroup: no candidate rows here
         __builtin_amdgcn_s_waitcnt(0);  // retire the speculative loads first
+        if constexpr (LIST) {  // an empty list that left nothing out, every call
+            if (tid == 0) lists_of(ws_of(ws, q, S_max, k), S_max, k).hdr[blockIdx.x] = 0u;
+        }
         return;
     }
     const int nb = ceil_div(r1 - r0, RPB);
@@ -281,6 +305,52 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
             const uint32_t c = hist[i];
             if (c) atomicAdd(&W.hist[i], c);
         }
+    }
+    if constexpr (LIST) {
+        // the cut a: the lowest bin with at most `cap` of this workgroup's
+        // candidates at or above it (thread t sums the 8 bins of group
+        // 255 - t, so the scan runs from the top bin down)
+        const Lists Ls = lists_of(ws_of(ws, q, S_max, k), S_max, k);
+        const uint32_t cap = (uint32_t)Ls.cap;
+        const int grp = kThreads - 1 - tid;
+        uint32_t hb[8], s8 = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { hb[j] = hist[grp * 8 + j]; s8 += hb[j]; }
+        if (tid == 0) cut_res = 0;
+        uint32_t all;
+        const uint32_t above = block_excl_scan<kThreads>(s8, scan_tmp, &all);
+        if (above <= cap && above + s8 > cap) {
+            uint32_t cum = above;
+#pragma unroll
+            for (int j = 7; j >= 0; --j) {
+                if (cum + hb[j] > cap) { cut_res = (uint32_t)(grp * 8 + j + 1); break; }
+                cum += hb[j];
+            }
+        }
+        __syncthreads();
+        const uint32_t a = cut_res;
+        // rows 8t .. 8t+7 of the workgroup at or above the cut, in index order
+        static_assert(kScoreRowsMulti == 8 * kThreads && kScoreRowsMulti == kListRows, "8 rows per thread");
+        uint32_t kk[8], m = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = tid * 8 + j;
+            kk[j] = score_key(stage[i]);
+            if (i < nr && (kk[j] >> 21) >= a) m |= 1u << j;
+        }
+        uint32_t cnt;
+        uint32_t pos = block_excl_scan<kThreads>((uint32_t)__popc(m), scan_tmp, &cnt);
+        const uint32_t e0 = (uint32_t)blockIdx.x * cap;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if ((m >> j) & 1u) {
+                const uint32_t at = list_pos(e0 + pos);
+                Ls.key[at] = kk[j];
+                Ls.idx[at] = (uint32_t)(r0 + tid * 8 + j);
+                ++pos;
+            }
+        }
+        if (tid == 0) Ls.hdr[blockIdx.x] = cnt | (a << 16);
     }
 }
 
@@ -683,33 +753,14 @@ static_assert(kPerThread == 16, "per-thread masks and counts are 16 bits wide");
 // bin, so one block prefix sum over (selected, short) counts places every
 // entry in index order.  Segment g's short list goes to cand_[4096 g ...),
 // its selected indices right after it, and its two counts to seg[g].
-//
-// AP != 0: grid rows y >= Nq carry a decode-time C4 append (AP = 1: fp32,
-// 2: bf16), one (sequence, 256-chunk span) per workgroup; it touches only the
-// append's own buffers, so it runs beside the filter in the same launch.
-template <int AP>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ n_cand,
                                                                uint8_t* __restrict__ ws, int S_max,
-                                                               int k, int Nq, AppendJob job) {
+                                                               int k) {
     __shared__ __align__(16) uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
     static_assert(kBins == 8 * kThreads, "two 16-byte histogram loads per thread");
 
-    if constexpr (AP != 0) {
-        if ((int)blockIdx.y >= Nq) {
-            using AT = typename std::conditional<AP == 1, float, bf16_t>::type;
-            const int spans = (job.D / Elem<AT>::kPer16B + kThreads - 1) / kThreads;
-            const int j = ((int)blockIdx.y - Nq) * (int)gridDim.x + (int)blockIdx.x;
-            if (j < job.B * spans)
-                append_short_chunk<AT, 4>(
-                    static_cast<const AT*>(job.x_tok), static_cast<const AT*>(job.g_tok),
-                    static_cast<const AT*>(job.bias), static_cast<AT*>(job.ring_x),
-                    static_cast<AT*>(job.ring_g), job.pos, static_cast<AT*>(job.pool), job.D,
-                    job.S_max, j / spans, (j % spans) * kThreads + threadIdx.x);
-            return;
-        }
-    }
     const int q = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
     const int n = clamp_n(n_cand, q, S_max);
@@ -801,7 +852,7 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
 
     const int q = blockIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
-    const SelLds L = {h, tmp, segc, sbase, lbase, ck, ci, selv, chs, misc, mem, flag};
+    const SelLds L = {h, tmp, segc, sbase, lbase, ck, ci, selv, chs, misc, mem, flag, nullptr};
     const SelResult R = select_query(W, clamp_n(n_cand, q, S_max), S_max, k, k, L);
     select_write_sorted(L, R, out + (size_t)q * k, k);
     __syncthreads();
@@ -811,32 +862,43 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
 template <typename T, int LPR>
 hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32_t* q_seq,
                         const int32_t* n_cand, float* scores, uint8_t* ws, int Nq, int H_I,
-                        int S_max, int k, bool hist, hipStream_t st) {
-    const int rows = hist ? kScoreRowsMulti : min(S_max, 8192);
+                        int S_max, int k, int sel, const AppendJob* job, hipStream_t st) {
+    const int rows = sel ? kScoreRowsMulti : min(S_max, 8192);
     dim3 grid((unsigned)ceil_div(S_max, rows), (unsigned)Nq);
+    if (sel == 2 && job) {  // append rows after the query rows
+        const int units = job->B * ((job->D / Elem<T>::kPer16B + kThreads - 1) / kThreads);
+        grid.y += (unsigned)ceil_div(units, (int)grid.x);
+    }
+    const AppendJob none{};
+    const AppendJob& aj = job ? *job : none;
     const size_t lds = (size_t)rows * sizeof(float);  // staged scores
     ProfScope prof(kProfScore, st);
-    if (hist)
-        hipLaunchKernelGGL((score_kernel<T, LPR, true>), grid, dim3(kThreads), lds, st,
+    if (sel == 2)
+        hipLaunchKernelGGL((score_kernel<T, LPR, 2>), grid, dim3(kThreads), lds, st,
                            (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows);
+                           S_max, k, rows, Nq, aj);
+    else if (sel == 1)
+        hipLaunchKernelGGL((score_kernel<T, LPR, 1>), grid, dim3(kThreads), lds, st,
+                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
+                           S_max, k, rows, Nq, aj);
     else
-        hipLaunchKernelGGL((score_kernel<T, LPR, false>), grid, dim3(kThreads), lds, st,
+        hipLaunchKernelGGL((score_kernel<T, LPR, 0>), grid, dim3(kThreads), lds, st,
                            (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows);
+                           S_max, k, rows, Nq, aj);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_score_t(int d_I, const void* q_idx, const void* k_idx, int B,
                           const int32_t* q_seq, const int32_t* n_cand, float* scores, uint8_t* ws,
-                          int Nq, int H_I, int S_max, int k, bool hist, hipStream_t st) {
+                          int Nq, int H_I, int S_max, int k, int sel, const AppendJob* job,
+                          hipStream_t st) {
     const int lpr = d_I * (int)sizeof(T) / 16;
     if (lpr == 8)
-        return launch_score<T, 8>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, hist, st);
+        return launch_score<T, 8>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st);
     if (lpr == 16)
-        return launch_score<T, 16>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, hist, st);
-    return launch_score<T, 32>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, hist, st);
+        return launch_score<T, 16>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st);
+    return launch_score<T, 32>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st);
 }
 
 }  // namespace
@@ -846,33 +908,19 @@ size_t topk_workspace_bytes(int Nq, int S_max, int k) {
     return (size_t)Nq * ws_per_query(S_max, k);
 }
 
-hipError_t launch_index_filter(int dtype, const void* q_idx, const void* k_idx, int B,
-                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
-                               int S_max, int k, void* ws, const AppendJob* job,
-                               hipStream_t st) {
+// Scores, first-digit histogram and per-workgroup candidate lists (the fused
+// decode select reads them), with the decode-time C4 append of `job` (may be
+// null) in the same launch.
+bool index_lists_apply(int S_max, int k) { return lists_apply(S_max, k); }
+
+hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
+                              const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
+                              int S_max, int k, void* ws, const AppendJob* job, hipStream_t st) {
     uint8_t* w = static_cast<uint8_t*>(ws);
-    hipError_t e = dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
-                                                         Nq, H_I, S_max, k, true, st)
-                                 : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores,
-                                                          w, Nq, H_I, S_max, k, true, st);
-    if (e != hipSuccess) return e;
-    ProfScope prof(kProfSelect, st);
-    const int G = n_segments(S_max);
-    if (job) {
-        const int V = dtype == kF32 ? 4 : 8;
-        const int units = job->B * ((job->D / V + kThreads - 1) / kThreads);
-        const unsigned rows = (unsigned)((units + G - 1) / G);
-        if (dtype == kF32)
-            hipLaunchKernelGGL(topk_filter_kernel<1>, dim3((unsigned)G, (unsigned)Nq + rows),
-                               dim3(kThreads), 0, st, scores, n_cand, w, S_max, k, Nq, *job);
-        else
-            hipLaunchKernelGGL(topk_filter_kernel<2>, dim3((unsigned)G, (unsigned)Nq + rows),
-                               dim3(kThreads), 0, st, scores, n_cand, w, S_max, k, Nq, *job);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(topk_filter_kernel<0>, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0, st,
-                       scores, n_cand, w, S_max, k, Nq, AppendJob{});
-    return hipGetLastError();
+    return dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
+                                                  Nq, H_I, S_max, k, 2, job, st)
+                         : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
+                                                   Nq, H_I, S_max, k, 2, job, st);
 }
 
 hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, int B,
@@ -900,9 +948,9 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (q_idx) {
         e = dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores, w,
-                                                   Nq, H_I, S_max, k, multi, st)
+                                                   Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st)
                           : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores,
-                                                   w, Nq, H_I, S_max, k, multi, st);
+                                                   w, Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st);
         if (e != hipSuccess) return e;
     } else if (multi) {
         dim3 grid((unsigned)ceil_div(S_max, kFilterChunk), (unsigned)Nq);
@@ -920,8 +968,8 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
                            n_cand, topk_idx, S_max, k);
     } else {
         const int G = ceil_div(S_max, kFilterChunk);
-        hipLaunchKernelGGL(topk_filter_kernel<0>, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0,
-                           st, scores, n_cand, w, S_max, k, Nq, AppendJob{});
+        hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0,
+                           st, scores, n_cand, w, S_max, k);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)Nq), dim3(kThreads), 0, st, n_cand,
                            topk_idx, w, S_max, k);

@@ -150,6 +150,7 @@ struct SelLds {
     uint32_t* misc;   // [4]
     uint32_t* mem;    // [3 * kSelThreads] crossing-bucket members: position, key, index
     uint8_t* flag;    // [kCandCap] chosen flags of crossing-bucket members
+    u32x4* stage;     // [kSelThreads * 16] list entries of one read round (select_query_lists)
 };
 
 struct SelResult {
@@ -161,115 +162,15 @@ struct SelResult {
     int T_s;     // threads per segment in the gather / zero mapping
 };
 
-// Gathers the selected list (ascending, all of it) and, when positions past
-// it are needed (j_need > its length), the short list, then resolves the
-// short list from the second-digit histogram: buckets above the crossing
-// bucket are taken, and the crossing bucket is taken whole, or its members
-// (at most kSelThreads of them, short list in LDS) are ranked directly under
-// (key desc, index asc), or else one 10-bit pass gives the k-th key and three
-// passes over complemented indices settle a tie that straddles rank k.  The
-// chosen short-list entries are then compacted in order.  The result lists
-// are L.sel[0..nsel) and
-// L.chs[0..nch), both ascending; the first take = nsel + nch entries of the
-// query's top-k are their union.  Short lists longer than kCandCap go through
-// W.flat_key / W.flat_idx (every caller that reaches that path writes the
-// same values).  Every thread calls it.
-__device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, int j_need,
-                                        const SelLds& L) {
+// The steps after the runs are placed.  L.h holds the second-digit
+// histogram (key bits 20..10) of the short list, whose members all share the
+// threshold bin; the short list is in L.ck / L.ci (small) or in W.flat_key /
+// W.flat_idx; R.nc and R.nsel are set and `need` = R.take - R.nsel > 0 of the
+// short list are to be chosen.  Leaves the chosen entries in L.chs, ascending,
+// and sets R.nch.  Every thread calls it.
+__device__ inline void select_finish(const QWs& W, SelResult& R, int need, bool small,
+                                     const SelLds& L) {
     const int tid = threadIdx.x;
-    SelResult R;
-    R.nseg = n_segments(S_max);
-    R.take = min(k, n);
-
-    // 1. segment counts, the second-digit histogram and the first entries of
-    //    every segment's runs, all loads in flight together: T_s threads per
-    //    segment, thread r of a segment takes entries r, r + T_s, ... and the
-    //    first kSpec of them are read before their count is known (they lie
-    //    inside the segment's slots, so reading them is always in bounds)
-    constexpr int SPT = kMaxSeg / kSelThreads;  // segments per thread in the scan (contiguous)
-    constexpr int kSpec = 12;
-    int T_s = 1;
-    while (T_s * 2 * R.nseg <= kSelThreads) T_s *= 2;
-    R.T_s = T_s;
-    const int par = kSelThreads / T_s, r = tid % T_s, g0 = tid / T_s;
-    uint32_t c[SPT], hv[kBins / kSelThreads], kk[kSpec], ii[kSpec];
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-        const int gg = tid * SPT + j;
-        c[j] = gg < R.nseg ? W.seg[gg] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < kBins / kSelThreads; ++j) hv[j] = W.hist2[tid + j * kSelThreads];
-    if (g0 < R.nseg) {
-        const uint32_t base = (uint32_t)g0 * kFilterChunk;
-        const uint32_t room = (uint32_t)min(kFilterChunk, S_max - g0 * kFilterChunk);  // slots of the segment
-#pragma unroll
-        for (int u = 0; u < kSpec; ++u) {
-            const uint32_t j = (uint32_t)(r + u * T_s);
-            ii[u] = j < room ? W.cand_idx[base + j] : 0u;
-            kk[u] = j < room ? W.cand_key[base + j] : 0u;
-        }
-    }
-    uint32_t s_short = 0, s_sel = 0;
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) { s_short += c[j] & 0xffffu; s_sel += c[j] >> 16; }
-    uint32_t nc_all, nsel_all;
-    uint32_t b_short, b_sel;
-    block_excl_scan2<kSelThreads>(s_short, s_sel, L.tmp, &b_short, &b_sel, &nc_all, &nsel_all);
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-        const int gg = tid * SPT + j;
-        if (gg < R.nseg) { L.segc[gg] = c[j]; L.sbase[gg] = b_short; L.lbase[gg] = b_sel; }
-        b_short += c[j] & 0xffffu;
-        b_sel += c[j] >> 16;
-    }
-#pragma unroll
-    for (int j = 0; j < kBins / kSelThreads; ++j) L.h[tid + j * kSelThreads] = hv[j];
-    __syncthreads();
-    R.nc = (int)nc_all;
-    R.nsel = min((int)nsel_all, R.take);
-    const bool small = R.nc <= kCandCap;
-    int need = R.take - R.nsel;
-    const bool refine = need > 0 && R.nc > 0 && j_need > R.nsel;  // uniform
-
-    // 2. place the runs: the speculative entries first, then whatever lies past them
-    auto place = [&](int gg, uint32_t j, uint32_t kv, uint32_t iv) {
-        const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
-        if (j < cs) {
-            if (refine) {
-                const uint32_t d = L.sbase[gg] + j;
-                if (small) { L.ck[d] = kv; L.ci[d] = iv; }
-                else { W.flat_key[d] = kv; W.flat_idx[d] = iv; }
-            }
-        } else if (j < cnt) {
-            const uint32_t d = L.lbase[gg] + (j - cs);
-            if (d < (uint32_t)kTopkMaxK) L.sel[d] = (int32_t)iv;
-        }
-    };
-    if (g0 < R.nseg) {
-#pragma unroll
-        for (int u = 0; u < kSpec; ++u) place(g0, (uint32_t)(r + u * T_s), kk[u], ii[u]);
-    }
-    for (int gg = g0; gg < R.nseg; gg += par) {
-        const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
-        const uint32_t base = (uint32_t)gg * kFilterChunk;
-        const uint32_t jstart = (uint32_t)r + (gg == g0 ? (uint32_t)(kSpec * T_s) : 0u);
-        for (uint32_t j0 = jstart; j0 < cnt; j0 += 8u * (uint32_t)T_s) {
-            uint32_t k8[8], i8[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t j = j0 + (uint32_t)(u * T_s);
-                i8[u] = j < cnt ? W.cand_idx[base + j] : 0u;
-                k8[u] = (refine && j < cs) ? W.cand_key[base + j] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) place(gg, j0 + (uint32_t)(u * T_s), k8[u], i8[u]);
-        }
-    }
-    __syncthreads();
-    R.nch = 0;
-    if (!refine) return R;
-
     // 3. the crossing bucket of the second digit and how much of it is taken
     const uint32_t* key = small ? L.ck : W.flat_key;
     const uint32_t* idx = small ? L.ci : W.flat_idx;
@@ -396,6 +297,423 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
         __syncthreads();
         R.nch = min((int)L.misc[0], R.take - R.nsel);
     }
+}
+
+// Gathers the selected list (ascending, all of it) and, when positions past
+// it are needed (j_need > its length), the short list, then resolves the
+// short list from the second-digit histogram: buckets above the crossing
+// bucket are taken, and the crossing bucket is taken whole, or its members
+// (at most kSelThreads of them, short list in LDS) are ranked directly under
+// (key desc, index asc), or else one 10-bit pass gives the k-th key and three
+// passes over complemented indices settle a tie that straddles rank k.  The
+// chosen short-list entries are then compacted in order.  The result lists
+// are L.sel[0..nsel) and
+// L.chs[0..nch), both ascending; the first take = nsel + nch entries of the
+// query's top-k are their union.  Short lists longer than kCandCap go through
+// W.flat_key / W.flat_idx (every caller that reaches that path writes the
+// same values).  Every thread calls it.
+__device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, int j_need,
+                                        const SelLds& L) {
+    const int tid = threadIdx.x;
+    SelResult R;
+    R.nseg = n_segments(S_max);
+    R.take = min(k, n);
+
+    // 1. segment counts, the second-digit histogram and the first entries of
+    //    every segment's runs, all loads in flight together: T_s threads per
+    //    segment, thread r of a segment takes entries r, r + T_s, ... and the
+    //    first kSpec of them are read before their count is known (they lie
+    //    inside the segment's slots, so reading them is always in bounds)
+    constexpr int SPT = kMaxSeg / kSelThreads;  // segments per thread in the scan (contiguous)
+    constexpr int kSpec = 12;
+    int T_s = 1;
+    while (T_s * 2 * R.nseg <= kSelThreads) T_s *= 2;
+    R.T_s = T_s;
+    const int par = kSelThreads / T_s, r = tid % T_s, g0 = tid / T_s;
+    uint32_t c[SPT], hv[kBins / kSelThreads], kk[kSpec], ii[kSpec];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int gg = tid * SPT + j;
+        c[j] = gg < R.nseg ? W.seg[gg] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kBins / kSelThreads; ++j) hv[j] = W.hist2[tid + j * kSelThreads];
+    if (g0 < R.nseg) {
+        const uint32_t base = (uint32_t)g0 * kFilterChunk;
+        const uint32_t room = (uint32_t)min(kFilterChunk, S_max - g0 * kFilterChunk);  // slots of the segment
+#pragma unroll
+        for (int u = 0; u < kSpec; ++u) {
+            const uint32_t j = (uint32_t)(r + u * T_s);
+            ii[u] = j < room ? W.cand_idx[base + j] : 0u;
+            kk[u] = j < room ? W.cand_key[base + j] : 0u;
+        }
+    }
+    uint32_t s_short = 0, s_sel = 0;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) { s_short += c[j] & 0xffffu; s_sel += c[j] >> 16; }
+    uint32_t nc_all, nsel_all;
+    uint32_t b_short, b_sel;
+    block_excl_scan2<kSelThreads>(s_short, s_sel, L.tmp, &b_short, &b_sel, &nc_all, &nsel_all);
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        const int gg = tid * SPT + j;
+        if (gg < R.nseg) { L.segc[gg] = c[j]; L.sbase[gg] = b_short; L.lbase[gg] = b_sel; }
+        b_short += c[j] & 0xffffu;
+        b_sel += c[j] >> 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kBins / kSelThreads; ++j) L.h[tid + j * kSelThreads] = hv[j];
+    __syncthreads();
+    R.nc = (int)nc_all;
+    R.nsel = min((int)nsel_all, R.take);
+    const bool small = R.nc <= kCandCap;
+    int need = R.take - R.nsel;
+    const bool refine = need > 0 && R.nc > 0 && j_need > R.nsel;  // uniform
+
+    // 2. place the runs: the speculative entries first, then whatever lies past them
+    auto place = [&](int gg, uint32_t j, uint32_t kv, uint32_t iv) {
+        const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
+        if (j < cs) {
+            if (refine) {
+                const uint32_t d = L.sbase[gg] + j;
+                if (small) { L.ck[d] = kv; L.ci[d] = iv; }
+                else { W.flat_key[d] = kv; W.flat_idx[d] = iv; }
+            }
+        } else if (j < cnt) {
+            const uint32_t d = L.lbase[gg] + (j - cs);
+            if (d < (uint32_t)kTopkMaxK) L.sel[d] = (int32_t)iv;
+        }
+    };
+    if (g0 < R.nseg) {
+#pragma unroll
+        for (int u = 0; u < kSpec; ++u) place(g0, (uint32_t)(r + u * T_s), kk[u], ii[u]);
+    }
+    for (int gg = g0; gg < R.nseg; gg += par) {
+        const uint32_t cs = L.segc[gg] & 0xffffu, cnt = cs + (L.segc[gg] >> 16);
+        const uint32_t base = (uint32_t)gg * kFilterChunk;
+        const uint32_t jstart = (uint32_t)r + (gg == g0 ? (uint32_t)(kSpec * T_s) : 0u);
+        for (uint32_t j0 = jstart; j0 < cnt; j0 += 8u * (uint32_t)T_s) {
+            uint32_t k8[8], i8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t j = j0 + (uint32_t)(u * T_s);
+                i8[u] = j < cnt ? W.cand_idx[base + j] : 0u;
+                k8[u] = (refine && j < cs) ? W.cand_key[base + j] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) place(gg, j0 + (uint32_t)(u * T_s), k8[u], i8[u]);
+        }
+    }
+    __syncthreads();
+    R.nch = 0;
+    if (!refine) return R;
+
+    select_finish(W, R, need, small, L);
+    return R;
+}
+
+// ---- per-workgroup candidate lists (fused decode select) ----------------------
+// Scoring workgroup g covers rows [2048 g, 2048 g + 2048) of its query.  Next
+// to the first-digit histogram it leaves a list, in index order, of its
+// candidates whose first digit (key bits 31..21) is at least a_g, the lowest
+// bin that has at most `cap` of its candidates at or above it, and records
+// a_g: candidates it left out have first digits below a_g.  If the query's
+// threshold bin t1 (the bin where the top-k crosses, from the completed
+// histogram) is at least every a_g, the lists hold every candidate in t1 or
+// above, which is all the select reads; the filter pass over the whole score
+// row is then not needed.  When some a_g exceeds t1 (a workgroup holds more
+// than `cap` candidates at or above t1: far more than its share on typical
+// rows, but possible for adversarial or tied scores) the select falls back to
+// passes over the score row itself, with the same result.
+constexpr int kListRows = 2048;   // rows per scoring workgroup
+constexpr int kListEPT = 32;      // list entries per thread per read round
+
+__host__ __device__ inline int list_slots(int S_max) { return (S_max + kListRows - 1) / kListRows; }
+
+// list capacity per workgroup: about four times a workgroup's even share of
+// the top-k, a power of two in [64, 256]
+__host__ __device__ inline int list_cap(int S_max, int k) {
+    const long long share4 = ((long long)4 * k * kListRows + S_max - 1) / S_max;
+    int c = 64;
+    while (c < share4 && c < 256) c *= 2;
+    return c;
+}
+
+// the lists are used when that capacity covers four even shares
+__host__ __device__ inline bool lists_apply(int S_max, int k) {
+    return S_max > kRowSelectCap && (long long)4 * k * kListRows <= 256LL * S_max;
+}
+
+// Lists live in the query's candidate area (cand_key / cand_idx, 2 S_max
+// words): hdr[nslot] (count | a_g << 16), then key[] and idx[] (16-byte
+// aligned), nslot * cap words each rounded up to whole rounds of 8192 (at
+// most S_max / 2 + 16384 words in all, within 2 S_max for S_max > 12288).
+// Entry j of slot g has the flat number
+// e = g * cap + j; the reader takes rounds of 8192 entries, thread t the 32
+// consecutive entries 32t .. 32t + 31 of a round in eight 16-byte loads, and
+// the words are stored so that load u of every thread of the workgroup is
+// one contiguous 4 KB run: e sits at list_pos(e), with entries 4u .. 4u + 3
+// of thread t at words 1024 u + 4 t .. + 3 of the round.
+__host__ __device__ inline uint32_t list_pos(uint32_t e) {
+    return (e & ~8191u) | (((e >> 2) & 7u) << 10) | (((e >> 5) & 255u) << 2) | (e & 3u);
+}
+static_assert(kListEPT == 32 && kSelThreads == 256, "list_pos assumes 256 readers x 32 entries");
+
+struct Lists {
+    uint32_t* hdr;
+    uint32_t* key;
+    uint32_t* idx;
+    int nslot, cap;
+};
+__device__ inline Lists lists_of(const QWs& W, int S_max, int k) {
+    Lists l;
+    l.nslot = list_slots(S_max);
+    l.cap = list_cap(S_max, k);
+    l.hdr = W.cand_key;
+    l.key = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(l.hdr + l.nslot) + 15) & ~(uintptr_t)15);
+    // list_pos spreads a round over 8192 words: whole rounds are reserved
+    l.idx = l.key + (size_t)ceil_div(l.nslot * l.cap, kListEPT * kSelThreads) * (kListEPT * kSelThreads);
+    return l;
+}
+
+// Exact select by passes over the query's score row (the lists' fallback):
+// t1 / rem1 are the threshold bin and how many of it are taken (take < n).
+// Leaves the whole selection in L.sel[0..take), ascending (R.nch = 0).
+__device__ inline void select_scan(const float* srow, int n, int t1, int rem1, const SelLds& L,
+                                   SelResult& R) {
+    const int tid = threadIdx.x;
+    uint32_t* h = L.h;
+    uint32_t pref = (uint32_t)t1 << 21, pmask = 0xffe00000u;
+    int need = rem1, rem;
+    uint32_t eq = 0;  // candidates equal to the k-th key
+    // second digit (bits 20..10) and third digit (bits 9..0) of the threshold
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 10 : 0;
+        const uint32_t nbm = pass == 0 ? (uint32_t)(kBins - 1) : 1023u;
+        for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kSelThreads) {
+            const uint32_t kk = score_key(srow[i]);
+            if ((kk & pmask) == pref) atomicAdd(&h[(kk >> shift) & nbm], 1u);
+        }
+        __syncthreads();
+        const int d = pass == 0 ? find_crossing<kBins>(h, need, L.tmp, &rem)
+                                : find_crossing<1024>(h, need, L.tmp, &rem);
+        if (pass == 1) eq = h[d];
+        __syncthreads();  // h read by all before the next pass clears it
+        need = rem;
+        pref |= (uint32_t)d << shift;
+        pmask |= nbm << shift;
+    }
+    const uint32_t T = pref;
+    uint32_t imax = 0xffffffffu;
+    if (eq > (uint32_t)need) {
+        // the `need` lowest indices among those equal to T: digits of ~index
+        int rr = need;
+        uint32_t pr = 0, pm = 0;
+#pragma unroll 1
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);  // 11, 11, 10 bits
+            const uint32_t nbm = pass == 2 ? 1023u : (uint32_t)(kBins - 1);
+            for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0;
+            __syncthreads();
+            for (int i = tid; i < n; i += kSelThreads) {
+                if (score_key(srow[i]) != T) continue;
+                const uint32_t ni = ~(uint32_t)i;
+                if ((ni & pm) == pr) atomicAdd(&h[(ni >> shift) & nbm], 1u);
+            }
+            __syncthreads();
+            const int d = pass < 2 ? find_crossing<kBins>(h, rr, L.tmp, &rem)
+                                   : find_crossing<1024>(h, rr, L.tmp, &rem);
+            rr = rem;
+            pr |= (uint32_t)d << shift;
+            pm |= nbm << shift;
+        }
+        imax = ~pr;
+    }
+    // every chosen candidate in index order, 16 consecutive per thread and round
+    constexpr int E = 16;
+    uint32_t base = 0;
+#pragma unroll 1
+    for (int r0 = 0; r0 < n; r0 += E * kSelThreads) {
+        const int i0 = r0 + tid * E;
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const int i = i0 + j;
+            if (i < n) {
+                const uint32_t kk = score_key(srow[i]);
+                if (kk > T || (kk == T && (uint32_t)i <= imax)) m |= 1u << j;
+            }
+        }
+        uint32_t all;
+        uint32_t pos = base + block_excl_scan<kSelThreads>((uint32_t)__popc(m), L.tmp, &all);
+        while (m) {
+            const int j = __ffs(m) - 1;
+            m &= m - 1;
+            if (pos < (uint32_t)kTopkMaxK) L.sel[pos] = i0 + j;
+            ++pos;
+        }
+        base += all;
+    }
+    __syncthreads();
+    R.nsel = R.take;
+    R.nc = 0;
+    R.nch = 0;
+}
+
+// One query's select inside one workgroup from the scoring workgroups' lists
+// (the fused decode path): the completed first-digit histogram gives the
+// threshold bin t1; the lists' candidates above it form the selected list and
+// those inside it the short list (both ascending), whose second-digit
+// histogram is built here; then as select_query.  Positions below j_need of
+// the result are what the caller needs (the short list is resolved only if
+// they reach past the selected list).  srow: the query's scores (fallback).
+__device__ inline SelResult select_query_lists(const QWs& W, const float* srow, int n, int S_max,
+                                               int k, int j_need, const SelLds& L) {
+    const int tid = threadIdx.x;
+    SelResult R;
+    R.nseg = 0;
+    R.T_s = 1;
+    R.take = min(k, n);
+    R.nc = 0;
+    R.nsel = 0;
+    R.nch = 0;
+    if (R.take == n) {  // every candidate is taken (also n = 0)
+        for (int i = tid; i < n; i += kSelThreads) L.sel[i] = i;
+        __syncthreads();
+        R.nsel = n;
+        return R;
+    }
+    const Lists Ls = lists_of(W, S_max, k);
+    const int total = Ls.nslot * Ls.cap;
+    const int rounds = ceil_div(total, kListEPT * kSelThreads);
+
+    // 1. histogram, every list header and the first round of list entries,
+    //    all loads in flight together (entries past the lists are clamped in
+    //    bounds and ignored)
+    u32x4 h0, h1;
+    {
+        const u32x4* hs = reinterpret_cast<const u32x4*>(W.hist);
+        h0 = hs[tid];
+        h1 = hs[tid + kSelThreads];
+    }
+    constexpr int kHdrPT = 8;  // headers per thread per pass (2048 slots in one pass)
+    uint32_t hv[kHdrPT];
+#pragma unroll
+    for (int j = 0; j < kHdrPT; ++j) {
+        const int s = tid + j * kSelThreads;
+        hv[j] = s < Ls.nslot ? Ls.hdr[s] : 0u;
+    }
+    for (int s = tid + kHdrPT * kSelThreads; s < Ls.nslot; s += kSelThreads)  // not taken below 4M rows
+        hv[0] = max(hv[0], Ls.hdr[s] & 0xffff0000u);
+    u32x4 kq[kListEPT / 4], iq[kListEPT / 4];
+    uint32_t own_hdr;
+    // a thread past the lists reads its round's first entries (in bounds:
+    // rounds are reserved whole) and ignores them
+    auto load_round = [&](int rd) {
+        const int e0 = rd * kListEPT * kSelThreads + tid * kListEPT;
+        const bool in = e0 < total;
+        own_hdr = in ? Ls.hdr[e0 / Ls.cap] : 0u;
+        const int rb = rd * kListEPT * kSelThreads;
+        const int t = in ? tid : 0;
+#pragma unroll
+        for (int j = 0; j < kListEPT / 4; ++j) {
+            const int w = rb + j * 4 * kSelThreads + 4 * t;
+            kq[j] = *reinterpret_cast<const u32x4*>(Ls.key + w);
+            iq[j] = *reinterpret_cast<const u32x4*>(Ls.idx + w);
+        }
+    };
+    load_round(0);
+
+    // 2. threshold bin and the check that no list left out a candidate in it or above
+    reinterpret_cast<u32x4*>(L.h)[tid] = h0;
+    reinterpret_cast<u32x4*>(L.h)[tid + kSelThreads] = h1;
+    __syncthreads();
+    int rem1;
+    const int t1 = find_crossing<kBins>(L.h, R.take, L.tmp, &rem1);
+    const uint32_t nc = L.h[t1];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kHdrPT; ++j) bad |= (int)(hv[j] >> 16) > t1;
+    if (tid == 0) L.misc[2] = 0;
+    __syncthreads();  // L.h read by all, misc[2] cleared
+    if (bad) L.misc[2] = 1;  // benign race: all write 1
+    __syncthreads();
+    if (L.misc[2] != 0) {  // uniform
+        select_scan(srow, n, t1, rem1, L, R);
+        return R;
+    }
+    R.nc = (int)nc;
+    R.nsel = R.take - rem1;
+    const int need = rem1;
+    const bool refine = j_need > R.nsel;  // uniform; need >= 1 and nc >= need here
+    const bool small = R.nc <= kCandCap;
+    if (refine)
+        for (int i = tid; i < kBins; i += kSelThreads) L.h[i] = 0;
+    __syncthreads();
+
+    // 3. route each round's entries: above t1 -> selected list, t1 -> short list
+    uint32_t bsel = 0, bsh = 0;
+#pragma unroll 1
+    for (int rd = 0; rd < rounds; ++rd) {
+        if (rd > 0) load_round(rd);
+        const int e0 = rd * kListEPT * kSelThreads + tid * kListEPT;
+        const int cnt = e0 < total ? (int)(own_hdr & 0xffffu) - e0 % Ls.cap : 0;  // valid entries here
+        uint32_t selm = 0, shm = 0;
+#pragma unroll
+        for (int j = 0; j < kListEPT; ++j) {
+            const uint32_t kk = kq[j / 4][j % 4];
+            const int bin = (int)(kk >> 21);
+            if (j < cnt && bin > t1) selm |= 1u << j;
+            if (j < cnt && bin == t1) shm |= 1u << j;
+        }
+        if (!refine) shm = 0;
+        // the thread's 32 keys and indices go to its own 256 bytes of LDS
+        // (chunk c at slot c ^ (t & 15): the 16 lanes of an LDS pass hit 16
+        // different columns), so the few set bits below are visited with
+        // dynamic indices that stay out of scratch memory
+        u32x4* st = L.stage + tid * 16;
+        const int sw = tid & 15;
+#pragma unroll
+        for (int j = 0; j < kListEPT / 4; ++j) {
+            st[j ^ sw] = kq[j];
+            st[(8 + j) ^ sw] = iq[j];
+        }
+        uint32_t ps, pc, ts, tc;
+        block_excl_scan2<kSelThreads>((uint32_t)__popc(selm), (uint32_t)__popc(shm), L.tmp, &ps, &pc,
+                                      &ts, &tc);
+        ps += bsel;
+        pc += bsh;
+        const uint32_t* sw32 = reinterpret_cast<const uint32_t*>(st);
+        auto stage_at = [&](int c, int j) { return sw32[((c ^ sw) << 2) | (j & 3)]; };
+        while (selm) {
+            const int j = __ffs(selm) - 1;
+            selm &= selm - 1;
+            if (ps < (uint32_t)kTopkMaxK) L.sel[ps] = (int32_t)stage_at(8 + (j >> 2), j);
+            ++ps;
+        }
+        while (shm) {
+            const int j = __ffs(shm) - 1;
+            shm &= shm - 1;
+            const uint32_t kk = stage_at(j >> 2, j), ii = stage_at(8 + (j >> 2), j);
+            if (small) {
+                if (pc < (uint32_t)kCandCap) { L.ck[pc] = kk; L.ci[pc] = ii; }
+            } else if (pc < (uint32_t)S_max) {
+                W.flat_key[pc] = kk;
+                W.flat_idx[pc] = ii;
+            }
+            atomicAdd(&L.h[(kk >> 10) & (kBins - 1)], 1u);
+            ++pc;
+        }
+        __syncthreads();  // the next round reuses the stage
+        bsel += ts;
+        bsh += tc;
+    }
+    __syncthreads();
+    if (!refine) return R;
+    select_finish(W, R, need, small, L);
     return R;
 }
 

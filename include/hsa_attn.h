@@ -215,9 +215,16 @@ int hsa_attn_decode(int dtype, const void *q, const void *swa_kv, const int32_t 
  * q, swa_kv, swa_len, comp_kv, topk_idx, comp_len, out, lse, B, H, d_qk, d_v,
  * W, S_max, k, scale, ...): scores and topk_idx identically; out and lse up
  * to rounding, since the attention may sum the selected rows in another
- * order (for S_max > 12,288 the select is finished inside the attention
- * kernel and the rows are taken as the selected-above-threshold list followed
- * by the chosen threshold-bin entries, each in index order).
+ * order.  For S_max > 12,288 and S_max >= 32 k (and B, H, W, k that split
+ * the rows over at least two workgroups per sequence) the scoring launch
+ * also leaves, per 2048 candidates, a list of those whose top 11 key bits
+ * reach that block's own cut (at most 64..256 of them), and the select is
+ * finished inside the attention kernel from those lists and the completed
+ * first-digit histogram; if some block's list cannot hold the top-k's
+ * threshold bin, the attention kernel selects from the score row instead
+ * (slower, same result).  The rows are then taken as the selected-above-
+ * threshold list followed by the chosen threshold-bin entries, each in index
+ * order.  Other shapes run the two calls above.
  *
  *   Arguments: as in hsa_index_topk (q_idx must not be NULL) and
  *              hsa_attn_decode (sparse mode), same layouts and limits.

@@ -135,6 +135,30 @@ def test_all_candidates_tie():
     np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (B, 1)))
 
 
+def test_concentrated_top_rows_take_the_score_row_path(oracle):
+    """Most of the top-k inside one scoring workgroup's 2048 rows: that
+    workgroup's candidate list cannot hold the threshold bin, so the select
+    reads the score row itself; results stay exact (against the separate
+    calls and the oracle's top-k), with duplicated rows for ties."""
+    import hybrid_sparse_compressed_amd as hsa
+
+    B, S, k = 2, 40000, 512
+    w = _small_case(14, B, S, dup=True)
+    w["k_idx"][0, 6144:6744] *= 8  # ~300 of sequence 0's top-k in rows 6144..8191
+    w["k_idx"][1, 30000:30900] *= 8
+    w["k_idx"][1, 30900:30910] = w["k_idx"][1, 30000:30010]  # exact ties among them
+    w["n_cand"] = torch.tensor([S, S - 1111], dtype=torch.int32, device="cuda")
+    w["swa_len"] = torch.tensor([128, 128], dtype=torch.int32, device="cuda")
+    w["comp_len"] = torch.tensor([S, S], dtype=torch.int32, device="cuda")
+    note("decode_sparse concentrated top rows")
+    idx, o, lse = _check_against_separate(hsa, w, k, "concentrated")
+    nc = w["n_cand"].cpu().numpy()
+    rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
+    ridx = oracle.topk(rs.astype(np.float32), nc, k)
+    inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(idx.cpu().numpy(), ridx))
+    assert inter / int((ridx >= 0).sum()) >= 0.999
+
+
 def test_small_pool_takes_the_separate_path():
     import hybrid_sparse_compressed_amd as hsa
 
