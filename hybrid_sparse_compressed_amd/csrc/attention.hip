@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     // Q fragments for this lane's head: k-slots of lane group `quad` (every
     // wave holds the same 16 heads)
     typename M::frag qf[NKK];
-    {
+    auto load_q = [&]() {
         const T* qrow;
         if constexpr (PREFILL)
             qrow = reinterpret_cast<const T*>(a.q) + ((size_t)qid * a.H + (head_ok ? head : 0)) * DQK;
@@ -300,8 +300,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
                 qf[kk] = head_ok ? reinterpret_cast<const float*>(qrow)[kk * M::kK + quad] : 0.f;
             }
         }
-    }
-
+    };
+    // fused: the select's loads go first, so that its waits do not wait
+    // for Q (the vector-memory counter retires in order); Q arrives during
+    // the row gather
+    if constexpr (!FUSED) load_q();
 
     if constexpr (FUSED) {
         const sel::QWs Wq = sel::ws_of(a.sel_ws, b, a.S_max, a.k);
@@ -320,7 +323,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             __syncthreads();  // fidx published; the select LDS goes back to the tiles
         }
     }
-    if constexpr (FUSED) row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
+    if constexpr (FUSED) {
+        load_q();
+        row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
+    }
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[NMT];

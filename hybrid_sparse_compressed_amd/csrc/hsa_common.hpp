@@ -68,15 +68,19 @@ template <> struct Elem<bf16_t> {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
-// inclusive prefix sum over the 64 lanes of a wave
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 lanes within each row of 16
+// (lanes without a source read 0), then the last lane of row 0 is added to
+// rows 1 and 3 and the last lane of row 1 (rows 0-1 total) to rows 2 and 3.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t o = __shfl_up(v, d, kWave);
-        if (l >= d) v += o;
-    }
-    return v;
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
+    return (uint32_t)x;
 }
 
 // Exclusive prefix sum over a workgroup of NT threads (NT multiple of 64).
