@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         if ((int)blockIdx.x == a.n_split) {  // the sequence's ascending top-k output
             if (hb != 0) return;
             const sel::SelResult R = sel::select_query_lists(
-                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, a.k, SL);
+                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, a.k, SL, [] {});
             sel::select_write_sorted(SL, R, a.topk_out + (size_t)b * a.k, a.k);
             return;
         }
@@ -301,9 +301,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             }
         }
     };
-    // fused: the select's loads go first, so that its waits do not wait
-    // for Q (the vector-memory counter retires in order); Q arrives during
-    // the row gather
+    // fused: Q is loaded inside the select, behind its first loads (the
+    // vector-memory counter retires in order), or right away if there is none
     if constexpr (!FUSED) load_q();
 
     if constexpr (FUSED) {
@@ -313,8 +312,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         if (vr1 > a.W) {  // uniform: this workgroup has compressed rows
             f_j0 = max(0, vr0 - a.W);
             const int j1 = min(a.k, vr1 - a.W);
+            // Q goes out right behind the select's first loads: the select
+            // never waits for it, and it arrives during the select
             const sel::SelResult R = sel::select_query_lists(
-                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, j1, SL);
+                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, j1, SL, load_q);
             f_jn = j1 - f_j0;
             for (int t = tid; t < f_jn; t += kAttnThreads) {
                 const int j = f_j0 + t;
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         }
     }
     if constexpr (FUSED) {
-        load_q();
+        if (vr1 <= a.W) load_q();  // uniform: a window-only split runs no select
         row_entry(vr0 + tid, min(vr1, vr0 + kChunkRows), first_off, first_src);
     }
 

@@ -288,17 +288,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
     __syncthreads();
-    // the workgroup's scores leave in one coalesced burst
-    float* srow = scores + (size_t)q * S_max + r0;
     const int nr = r1 - r0;
-    for (int i = tid * 4; i < nr; i += kThreads * 4) {
-        if (i + 4 <= nr && (((uintptr_t)(srow + i)) & 15u) == 0) {
-            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage + i),
-                                        reinterpret_cast<f32x4*>(srow + i));
-        } else {
-            for (int j = i; j < min(nr, i + 4); ++j) srow[j] = stage[j];
-        }
-    }
     if constexpr (HIST) {
         QWs W = ws_of(ws, q, S_max, k);
         for (int i = tid; i < kBins; i += kThreads) {
@@ -351,6 +341,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
             }
         }
         if (tid == 0) Ls.hdr[blockIdx.x] = cnt | (a << 16);
+    }
+    // the workgroup's scores leave in one coalesced burst
+    float* srow = scores + (size_t)q * S_max + r0;
+    for (int i = tid * 4; i < nr; i += kThreads * 4) {
+        if (i + 4 <= nr && (((uintptr_t)(srow + i)) & 15u) == 0) {
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage + i),
+                                        reinterpret_cast<f32x4*>(srow + i));
+        } else {
+            for (int j = i; j < min(nr, i + 4); ++j) srow[j] = stage[j];
+        }
     }
 }
 

@@ -570,8 +570,11 @@ __device__ inline void select_scan(const float* srow, int n, int t1, int rem1, c
 // histogram is built here; then as select_query.  Positions below j_need of
 // the result are what the caller needs (the short list is resolved only if
 // they reach past the selected list).  srow: the query's scores (fallback).
+//   after_loads(): called once every thread's first list loads are issued
+//   (the caller's own loads that the select does not wait for go there)
+template <typename F>
 __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, int n, int S_max,
-                                               int k, int j_need, const SelLds& L) {
+                                               int k, int j_need, const SelLds& L, F&& after_loads) {
     const int tid = threadIdx.x;
     SelResult R;
     R.nseg = 0;
@@ -581,6 +584,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     R.nsel = 0;
     R.nch = 0;
     if (R.take == n) {  // every candidate is taken (also n = 0)
+        after_loads();
         for (int i = tid; i < n; i += kSelThreads) L.sel[i] = i;
         __syncthreads();
         R.nsel = n;
@@ -626,6 +630,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
         }
     };
     load_round(0);
+    after_loads();
 
     // 2. threshold bin and the check that no list left out a candidate in it or above
     reinterpret_cast<u32x4*>(L.h)[tid] = h0;
