@@ -428,16 +428,19 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
 constexpr int kListRows = 2048;   // rows per scoring workgroup
 constexpr int kListEPT = 32;      // list entries per thread per read round
 
-__host__ __device__ inline int list_slots(int S_max) { return (S_max + kListRows - 1) / kListRows; }
+__host__ __device__ inline int list_slots(int S_max) { return (S_max + kListRows - 1) >> 11; }
+static_assert(kListRows == 2048, "list_slots shifts by 11");
 
-// list capacity per workgroup: about four times a workgroup's even share of
-// the top-k, a power of two in [64, 256]
-__host__ __device__ inline int list_cap(int S_max, int k) {
-    const long long share4 = ((long long)4 * k * kListRows + S_max - 1) / S_max;
-    int c = 64;
-    while (c < share4 && c < 256) c *= 2;
-    return c;
+// log2 of the list capacity per workgroup: the smallest power of two in
+// [64, 256] that is at least four times a workgroup's even share of the
+// top-k, 4 k 2048 / S_max (compared by products: no division on the device)
+__host__ __device__ inline int list_cap_log2(int S_max, int k) {
+    const long long need = (long long)4 * k * kListRows;
+    int lg = 6;
+    while (lg < 8 && ((long long)S_max << lg) < need) ++lg;
+    return lg;
 }
+__host__ __device__ inline int list_cap(int S_max, int k) { return 1 << list_cap_log2(S_max, k); }
 
 // the lists are used when that capacity covers four even shares
 __host__ __device__ inline bool lists_apply(int S_max, int k) {
@@ -463,16 +466,17 @@ struct Lists {
     uint32_t* hdr;
     uint32_t* key;
     uint32_t* idx;
-    int nslot, cap;
+    int nslot, cap, cap_lg;
 };
 __device__ inline Lists lists_of(const QWs& W, int S_max, int k) {
     Lists l;
     l.nslot = list_slots(S_max);
-    l.cap = list_cap(S_max, k);
+    l.cap_lg = list_cap_log2(S_max, k);
+    l.cap = 1 << l.cap_lg;
     l.hdr = W.cand_key;
     l.key = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(l.hdr + l.nslot) + 15) & ~(uintptr_t)15);
     // list_pos spreads a round over 8192 words: whole rounds are reserved
-    l.idx = l.key + (size_t)ceil_div(l.nslot * l.cap, kListEPT * kSelThreads) * (kListEPT * kSelThreads);
+    l.idx = l.key + ((((size_t)l.nslot << l.cap_lg) + 8191) & ~(size_t)8191);
     return l;
 }
 
@@ -591,8 +595,9 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
         return R;
     }
     const Lists Ls = lists_of(W, S_max, k);
-    const int total = Ls.nslot * Ls.cap;
-    const int rounds = ceil_div(total, kListEPT * kSelThreads);
+    const int total = Ls.nslot << Ls.cap_lg;
+    const int rounds = (total + kListEPT * kSelThreads - 1) >> 13;
+    static_assert(kListEPT * kSelThreads == 8192, "rounds of 8192 entries");
 
     // 1. histogram, every list header and the first round of list entries,
     //    all loads in flight together (entries past the lists are clamped in
@@ -619,7 +624,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     auto load_round = [&](int rd) {
         const int e0 = rd * kListEPT * kSelThreads + tid * kListEPT;
         const bool in = e0 < total;
-        own_hdr = in ? Ls.hdr[e0 / Ls.cap] : 0u;
+        own_hdr = in ? Ls.hdr[e0 >> Ls.cap_lg] : 0u;
         const int rb = rd * kListEPT * kSelThreads;
         const int t = in ? tid : 0;
 #pragma unroll
@@ -665,7 +670,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     for (int rd = 0; rd < rounds; ++rd) {
         if (rd > 0) load_round(rd);
         const int e0 = rd * kListEPT * kSelThreads + tid * kListEPT;
-        const int cnt = e0 < total ? (int)(own_hdr & 0xffffu) - e0 % Ls.cap : 0;  // valid entries here
+        const int cnt = e0 < total ? (int)(own_hdr & 0xffffu) - (e0 & (Ls.cap - 1)) : 0;  // valid entries here
         uint32_t selm = 0, shm = 0;
 #pragma unroll
         for (int j = 0; j < kListEPT; ++j) {
