@@ -907,14 +907,15 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 // combining them.
 constexpr int kMaxSplit = 128;
 
-template <typename T, int DV>
+template <typename T, int DV, int kBatch>
 __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_ml,
                                                          const float* __restrict__ part_o,
                                                          void* __restrict__ out,
                                                          float* __restrict__ lse, int H,
                                                          int n_split, uint8_t* __restrict__ sel_ws,
                                                          int S_max, int k) {
-    constexpr int kBatch = 16;  // split partials loaded per round
+    // kBatch: split partials loaded per round (the launch picks the
+    // smallest of 4, 8, 12, 16 that covers the splits, or 16)
     auto load4 = [](const float* p) -> f32x4 { return *reinterpret_cast<const f32x4*>(p); };
     __shared__ float wsp[kMaxSplit], lsp[kMaxSplit];
     __shared__ float stat[2];
@@ -1096,21 +1097,30 @@ size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows) {
     return bytes;
 }
 
-static hipError_t launch_merge(int dtype, int d_v, const AttnArgs& a, int B, int H, int n_split,
-                               int S_max, int k, hipStream_t st) {
+template <int NB>
+static void launch_merge_nb(int dtype, int d_v, const AttnArgs& a, int B, int H, int n_split,
+                            int S_max, int k, hipStream_t st) {
     dim3 mg((unsigned)H, (unsigned)B);
-    ProfScope prof(kProfMerge, st);
     if (dtype == kBF16) {
         if (d_v == 512)
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split,
-                               a.sel_ws, S_max, k);
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512, NB>), mg, dim3(128), 0, st, a.part_ml,
+                               a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k);
         else
-            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split,
-                               a.sel_ws, S_max, k);
+            hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128, NB>), mg, dim3(128), 0, st, a.part_ml,
+                               a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k);
     } else {
-        hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mg, dim3(128), 0, st, a.part_ml, a.part_o, a.out, a.lse, H, n_split,
-                               a.sel_ws, S_max, k);
+        hipLaunchKernelGGL((attn_merge_kernel<float, 128, NB>), mg, dim3(128), 0, st, a.part_ml,
+                           a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k);
     }
+}
+
+static hipError_t launch_merge(int dtype, int d_v, const AttnArgs& a, int B, int H, int n_split,
+                               int S_max, int k, hipStream_t st) {
+    ProfScope prof(kProfMerge, st);
+    if (n_split <= 4) launch_merge_nb<4>(dtype, d_v, a, B, H, n_split, S_max, k, st);
+    else if (n_split <= 8) launch_merge_nb<8>(dtype, d_v, a, B, H, n_split, S_max, k, st);
+    else if (n_split <= 12) launch_merge_nb<12>(dtype, d_v, a, B, H, n_split, S_max, k, st);
+    else launch_merge_nb<16>(dtype, d_v, a, B, H, n_split, S_max, k, st);
     return hipGetLastError();
 }
 
