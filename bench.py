@@ -67,7 +67,8 @@ def source_hash(paths):
 
 def score_kernel_sources():
     c = os.path.join(ROOT, "hybrid_sparse_compressed_amd", "csrc")
-    return [os.path.join(c, f) for f in ("index_topk.hip", "hsa_common.hpp")]
+    return [os.path.join(c, f) for f in ("index_topk.hip", "hsa_common.hpp", "hsa_internal.hpp",
+                                         "select.hpp", "compress_append.hpp")]
 
 
 def main():
@@ -184,7 +185,7 @@ def main():
             traffic = pmc.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "score_kernel (indexer scores + first-digit histogram)",
+                "kernel": "score_kernel (indexer scores, first-digit histogram, candidate lists)",
                 "alg_bytes_per_launch": alg_bytes}
 
     step_bytes = (B * S * d_I * 2 + B * (W + k) * d_qk * 2 + B * H * d_qk * 2 + B * H * d_v * 2
