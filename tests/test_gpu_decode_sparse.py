@@ -6,6 +6,8 @@ bf16 bound (the fused attention sums the selected rows in another order).
 Against the oracle chain: selected-set overlap and out / lse as in the
 separate-call end-to-end test.  The workspace is zero-filled once and then
 reused: calls must be repeatable on it."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -152,6 +154,51 @@ def test_concentrated_top_rows_take_the_score_row_path(oracle):
     w["comp_len"] = torch.tensor([S, S], dtype=torch.int32, device="cuda")
     note("decode_sparse concentrated top rows")
     idx, o, lse = _check_against_separate(hsa, w, k, "concentrated")
+    nc = w["n_cand"].cpu().numpy()
+    rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
+    ridx = oracle.topk(rs.astype(np.float32), nc, k)
+    inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(idx.cpu().numpy(), ridx))
+    assert inter / int((ridx >= 0).sum()) >= 0.999
+
+
+def test_fused_lists_fp32_and_large_k(oracle):
+    """The list-based fused select at other shapes: fp32 with 128-wide latents
+    and 8 heads (list capacity 64, select finished in the attention kernel),
+    and bf16 576/512 with k = 2048 (selected list up to 2047 entries)."""
+    import hybrid_sparse_compressed_amd as hsa
+
+    g = torch.Generator().manual_seed(15)
+    B, S, H, W, k = 3, 20000, 8, 128, 64
+    w = dict(q=torch.randn(B, H, 128, generator=g), swa_kv=torch.randn(B, W, 128, generator=g),
+             comp_kv=torch.randn(B, S, 128, generator=g), q_idx=torch.randn(B, 4, 64, generator=g),
+             k_idx=torch.randn(B, S, 64, generator=g), scale=1.0 / math.sqrt(128))
+    w = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in w.items()}
+    w["n_cand"] = torch.tensor([S, S - 5, 12345], dtype=torch.int32, device="cuda")
+    w["swa_len"] = torch.tensor([128, 100, 1], dtype=torch.int32, device="cuda")
+    w["comp_len"] = torch.tensor([S, S, S], dtype=torch.int32, device="cuda")
+    note("decode_sparse fp32 lists")
+    ws, _ = _workspace(hsa, w, k, d_v=128)
+    s1, i1, o1, l1 = _separate(hsa, w, k, d_v=128)
+    s2, i2, o2, l2 = _fused(hsa, w, k, d_v=128, workspace=ws)
+    torch.cuda.synchronize()
+    for b, nb in enumerate(w["n_cand"].cpu().tolist()):
+        assert torch.equal(s1[b, :nb], s2[b, :nb])
+    np.testing.assert_array_equal(i2.cpu().numpy(), i1.cpu().numpy())
+    print(compare(o2, o1, (1e-5, 1e-5), "fp32 lists out vs separate"))
+    print(compare(l2, l1, (1e-5, 1e-5), "fp32 lists lse vs separate"))
+    nc = w["n_cand"].cpu().numpy()
+    rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
+    ridx = oracle.topk(rs.astype(np.float32), nc, k)
+    inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(i2.cpu().numpy(), ridx))
+    assert inter / int((ridx >= 0).sum()) >= 0.999
+
+    B, S, k = 2, 70000, 2048
+    w = _small_case(16, B, S, k=k, dup=True)
+    w["n_cand"] = torch.tensor([S, S - 3000], dtype=torch.int32, device="cuda")
+    w["swa_len"] = torch.tensor([128, 77], dtype=torch.int32, device="cuda")
+    w["comp_len"] = torch.tensor([S, S], dtype=torch.int32, device="cuda")
+    note("decode_sparse k=2048 lists")
+    idx, o, lse = _check_against_separate(hsa, w, k, "k2048")
     nc = w["n_cand"].cpu().numpy()
     rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
     ridx = oracle.topk(rs.astype(np.float32), nc, k)
