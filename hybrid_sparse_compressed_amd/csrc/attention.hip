@@ -292,12 +292,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             qrow = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.H + (head_ok ? head : 0)) * DQK;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
+            // unconditional loads (row clamped to head 0), zeroed after: a
+            // load inside a branch would get a wait for every load before it
             if constexpr (sizeof(T) == 2) {
-                u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qrow + kk * M::kK + quad * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
+                u32x4 v = *reinterpret_cast<const u32x4*>(qrow + kk * M::kK + quad * 8);
+                if (!head_ok) v = u32x4{0u, 0u, 0u, 0u};
                 qf[kk] = __builtin_bit_cast(bf16x8, v);
             } else {
-                qf[kk] = head_ok ? reinterpret_cast<const float*>(qrow)[kk * M::kK + quad] : 0.f;
+                const float v = reinterpret_cast<const float*>(qrow)[kk * M::kK + quad];
+                qf[kk] = head_ok ? v : 0.f;
             }
         }
     };

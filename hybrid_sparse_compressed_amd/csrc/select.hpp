@@ -168,12 +168,16 @@ struct SelResult {
 // W.flat_idx; R.nc and R.nsel are set and `need` = R.take - R.nsel > 0 of the
 // short list are to be chosen.  Leaves the chosen entries in L.chs, ascending,
 // and sets R.nch.  Every thread calls it.
-__device__ inline void select_finish(const QWs& W, SelResult& R, int need, bool small,
-                                     const SelLds& L) {
+// SMALL (the short list is in LDS) is a template argument so that the list
+// pointers are known to be LDS or global: a pointer that may be either makes
+// every access a flat one.
+template <bool SMALL>
+__device__ inline void select_finish_t(const QWs& W, SelResult& R, int need, const SelLds& L) {
     const int tid = threadIdx.x;
+    constexpr bool small = SMALL;
     // 3. the crossing bucket of the second digit and how much of it is taken
-    const uint32_t* key = small ? L.ck : W.flat_key;
-    const uint32_t* idx = small ? L.ci : W.flat_idx;
+    const uint32_t* key = SMALL ? L.ck : W.flat_key;
+    const uint32_t* idx = SMALL ? L.ci : W.flat_idx;
     const int nc = R.nc;
     uint32_t* h = L.h;
     bool whole, direct = false;
@@ -297,6 +301,12 @@ __device__ inline void select_finish(const QWs& W, SelResult& R, int need, bool 
         __syncthreads();
         R.nch = min((int)L.misc[0], R.take - R.nsel);
     }
+}
+
+__device__ inline void select_finish(const QWs& W, SelResult& R, int need, bool small,
+                                     const SelLds& L) {
+    if (small) select_finish_t<true>(W, R, need, L);
+    else select_finish_t<false>(W, R, need, L);
 }
 
 // Gathers the selected list (ascending, all of it) and, when positions past
@@ -474,10 +484,31 @@ __device__ inline Lists lists_of(const QWs& W, int S_max, int k) {
     l.cap_lg = list_cap_log2(S_max, k);
     l.cap = 1 << l.cap_lg;
     l.hdr = W.cand_key;
-    l.key = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(l.hdr + l.nslot) + 15) & ~(uintptr_t)15);
+    // 16-byte alignment by an index offset (a pointer rebuilt from an integer
+    // would lose its global address space and turn the loads into flat ones)
+    const int pad = (int)((0u - (uint32_t)(reinterpret_cast<uintptr_t>(l.hdr + l.nslot) >> 2)) & 3u);
+    l.key = l.hdr + l.nslot + pad;
     // list_pos spreads a round over 8192 words: whole rounds are reserved
     l.idx = l.key + ((((size_t)l.nslot << l.cap_lg) + 8191) & ~(size_t)8191);
     return l;
+}
+
+// f(i, key) for every candidate i < n (n >= 1) of a score row, all threads:
+// eight coalesced loads per thread in flight at once (clamped indices past
+// the row are loaded and skipped)
+template <typename F>
+__device__ __forceinline__ void for_each_key(const float* srow, int n, F&& f) {
+    constexpr int U = 8;
+    for (int i0 = (int)threadIdx.x; i0 < n; i0 += U * kSelThreads) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = srow[min(i0 + u * kSelThreads, n - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kSelThreads;
+            if (i < n) f(i, score_key(v[u]));
+        }
+    }
 }
 
 // Exact select by passes over the query's score row (the lists' fallback):
@@ -497,10 +528,9 @@ __device__ inline void select_scan(const float* srow, int n, int t1, int rem1, c
         const uint32_t nbm = pass == 0 ? (uint32_t)(kBins - 1) : 1023u;
         for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kSelThreads) {
-            const uint32_t kk = score_key(srow[i]);
+        for_each_key(srow, n, [&](int, uint32_t kk) {
             if ((kk & pmask) == pref) atomicAdd(&h[(kk >> shift) & nbm], 1u);
-        }
+        });
         __syncthreads();
         const int d = pass == 0 ? find_crossing<kBins>(h, need, L.tmp, &rem)
                                 : find_crossing<1024>(h, need, L.tmp, &rem);
@@ -522,11 +552,10 @@ __device__ inline void select_scan(const float* srow, int n, int t1, int rem1, c
             const uint32_t nbm = pass == 2 ? 1023u : (uint32_t)(kBins - 1);
             for (int i = tid; i < kBins; i += kSelThreads) h[i] = 0;
             __syncthreads();
-            for (int i = tid; i < n; i += kSelThreads) {
-                if (score_key(srow[i]) != T) continue;
+            for_each_key(srow, n, [&](int i, uint32_t kk) {
                 const uint32_t ni = ~(uint32_t)i;
-                if ((ni & pm) == pr) atomicAdd(&h[(ni >> shift) & nbm], 1u);
-            }
+                if (kk == T && (ni & pm) == pr) atomicAdd(&h[(ni >> shift) & nbm], 1u);
+            });
             __syncthreads();
             const int d = pass < 2 ? find_crossing<kBins>(h, rr, L.tmp, &rem)
                                    : find_crossing<1024>(h, rr, L.tmp, &rem);
@@ -542,14 +571,15 @@ __device__ inline void select_scan(const float* srow, int n, int t1, int rem1, c
 #pragma unroll 1
     for (int r0 = 0; r0 < n; r0 += E * kSelThreads) {
         const int i0 = r0 + tid * E;
+        float v[E];  // all loads in flight first (clamped indices past the row)
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = srow[min(i0 + j, n - 1)];
         uint32_t m = 0;
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const int i = i0 + j;
-            if (i < n) {
-                const uint32_t kk = score_key(srow[i]);
-                if (kk > T || (kk == T && (uint32_t)i <= imax)) m |= 1u << j;
-            }
+            const uint32_t kk = score_key(v[j]);
+            if (i < n && (kk > T || (kk == T && (uint32_t)i <= imax))) m |= 1u << j;
         }
         uint32_t all;
         uint32_t pos = base + block_excl_scan<kSelThreads>((uint32_t)__popc(m), L.tmp, &all);
@@ -608,13 +638,13 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
         h0 = hs[tid];
         h1 = hs[tid + kSelThreads];
     }
+    // Loads are unconditional (clamped indices, values past the end masked
+    // afterwards): a load inside a branch gets its use scheduled inside the
+    // branch too, and that wait would hold back every load issued after it.
     constexpr int kHdrPT = 8;  // headers per thread per pass (2048 slots in one pass)
     uint32_t hv[kHdrPT];
 #pragma unroll
-    for (int j = 0; j < kHdrPT; ++j) {
-        const int s = tid + j * kSelThreads;
-        hv[j] = s < Ls.nslot ? Ls.hdr[s] : 0u;
-    }
+    for (int j = 0; j < kHdrPT; ++j) hv[j] = Ls.hdr[min(tid + j * kSelThreads, Ls.nslot - 1)];
     for (int s = tid + kHdrPT * kSelThreads; s < Ls.nslot; s += kSelThreads)  // not taken below 4M rows
         hv[0] = max(hv[0], Ls.hdr[s] & 0xffff0000u);
     u32x4 kq[kListEPT / 4], iq[kListEPT / 4];
@@ -624,7 +654,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     auto load_round = [&](int rd) {
         const int e0 = rd * kListEPT * kSelThreads + tid * kListEPT;
         const bool in = e0 < total;
-        own_hdr = in ? Ls.hdr[e0 >> Ls.cap_lg] : 0u;
+        own_hdr = Ls.hdr[min(e0 >> Ls.cap_lg, Ls.nslot - 1)];  // unconditional; masked by `in` below
         const int rb = rd * kListEPT * kSelThreads;
         const int t = in ? tid : 0;
 #pragma unroll
@@ -646,7 +676,8 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     const uint32_t nc = L.h[t1];
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kHdrPT; ++j) bad |= (int)(hv[j] >> 16) > t1;
+    for (int j = 0; j < kHdrPT; ++j)
+        bad |= tid + j * kSelThreads < Ls.nslot && (int)(hv[j] >> 16) > t1;
     if (tid == 0) L.misc[2] = 0;
     __syncthreads();  // L.h read by all, misc[2] cleared
     if (bad) L.misc[2] = 1;  // benign race: all write 1
@@ -670,7 +701,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     for (int rd = 0; rd < rounds; ++rd) {
         if (rd > 0) load_round(rd);
         const int e0 = rd * kListEPT * kSelThreads + tid * kListEPT;
-        const int cnt = e0 < total ? (int)(own_hdr & 0xffffu) - (e0 & (Ls.cap - 1)) : 0;  // valid entries here
+        const int cnt = e0 < total ? (int)(own_hdr & 0xffffu) - (e0 & (Ls.cap - 1)) : 0;  // valid entries here (own_hdr is a clamped slot's past the lists)
         uint32_t selm = 0, shm = 0;
 #pragma unroll
         for (int j = 0; j < kListEPT; ++j) {
