@@ -237,7 +237,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             if (hb != 0) return;
             const sel::SelResult R = sel::select_query_lists(
                 Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, a.k, SL, [] {});
-            sel::select_write_sorted(SL, R, a.topk_out + (size_t)b * a.k, a.k);
+            if (R.unordered)  // uniform
+                sel::select_write_sorted_any(SL, R, a.topk_out + (size_t)b * a.k, a.k, SL.ck);
+            else
+                sel::select_write_sorted(SL, R, a.topk_out + (size_t)b * a.k, a.k);
             return;
         }
     }

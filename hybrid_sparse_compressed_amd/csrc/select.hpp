@@ -160,6 +160,7 @@ struct SelResult {
     int nsel;    // selected-list length (<= take)
     int nch;     // chosen short-list entries (nsel + nch = take)
     int T_s;     // threads per segment in the gather / zero mapping
+    bool unordered;  // select_query_lists: the lists are not in index order (see there)
 };
 
 // The steps after the runs are placed.  L.h holds the second-digit
@@ -328,6 +329,7 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
     SelResult R;
     R.nseg = n_segments(S_max);
     R.take = min(k, n);
+    R.unordered = false;
 
     // 1. segment counts, the second-digit histogram and the first entries of
     //    every segment's runs, all loads in flight together: T_s threads per
@@ -494,11 +496,11 @@ __device__ inline Lists lists_of(const QWs& W, int S_max, int k) {
 }
 
 // f(i, key) for every candidate i < n (n >= 1) of a score row, all threads:
-// eight coalesced loads per thread in flight at once (clamped indices past
+// sixteen coalesced loads per thread in flight at once (clamped indices past
 // the row are loaded and skipped)
 template <typename F>
 __device__ __forceinline__ void for_each_key(const float* srow, int n, F&& f) {
-    constexpr int U = 8;
+    constexpr int U = 16;
     for (int i0 = (int)threadIdx.x; i0 < n; i0 += U * kSelThreads) {
         float v[U];
 #pragma unroll
@@ -514,9 +516,10 @@ __device__ __forceinline__ void for_each_key(const float* srow, int n, F&& f) {
 // Exact select by passes over the query's score row (the lists' fallback):
 // t1 / rem1 are the threshold bin and how many of it are taken (take < n).
 // Leaves the whole selection in L.sel[0..take), ascending (R.nch = 0).
-__device__ inline void select_scan(const float* srow, int n, int t1, int rem1, const SelLds& L,
-                                   SelResult& R) {
+__device__ inline void select_scan(const float* srow, int n, int S_max, int t1, int rem1,
+                                   const SelLds& L, SelResult& R) {
     const int tid = threadIdx.x;
+    (void)S_max;
     uint32_t* h = L.h;
     uint32_t pref = (uint32_t)t1 << 21, pmask = 0xffe00000u;
     int need = rem1, rem;
@@ -565,15 +568,20 @@ __device__ inline void select_scan(const float* srow, int n, int t1, int rem1, c
         }
         imax = ~pr;
     }
-    // every chosen candidate in index order, 16 consecutive per thread and round
+    // every chosen candidate in index order, 16 consecutive per thread and
+    // round; the next round's scores are loaded before this round's scan
     constexpr int E = 16;
     uint32_t base = 0;
+    float v[E];
+    auto load = [&](int r0) {
+        const int i0 = r0 + tid * E;
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = srow[min(i0 + j, n - 1)];  // clamped, unconditional
+    };
+    load(0);
 #pragma unroll 1
     for (int r0 = 0; r0 < n; r0 += E * kSelThreads) {
         const int i0 = r0 + tid * E;
-        float v[E];  // all loads in flight first (clamped indices past the row)
-#pragma unroll
-        for (int j = 0; j < E; ++j) v[j] = srow[min(i0 + j, n - 1)];
         uint32_t m = 0;
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -581,6 +589,7 @@ __device__ inline void select_scan(const float* srow, int n, int t1, int rem1, c
             const uint32_t kk = score_key(v[j]);
             if (i < n && (kk > T || (kk == T && (uint32_t)i <= imax))) m |= 1u << j;
         }
+        if (r0 + E * kSelThreads < n) load(r0 + E * kSelThreads);
         uint32_t all;
         uint32_t pos = base + block_excl_scan<kSelThreads>((uint32_t)__popc(m), L.tmp, &all);
         while (m) {
@@ -613,6 +622,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     SelResult R;
     R.nseg = 0;
     R.T_s = 1;
+    R.unordered = false;
     R.take = min(k, n);
     R.nc = 0;
     R.nsel = 0;
@@ -645,8 +655,8 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     uint32_t hv[kHdrPT];
 #pragma unroll
     for (int j = 0; j < kHdrPT; ++j) hv[j] = Ls.hdr[min(tid + j * kSelThreads, Ls.nslot - 1)];
-    for (int s = tid + kHdrPT * kSelThreads; s < Ls.nslot; s += kSelThreads)  // not taken below 4M rows
-        hv[0] = max(hv[0], Ls.hdr[s] & 0xffff0000u);
+    static_assert(kHdrPT * kSelThreads * kListRows >= kTopkMaxSegments * kFilterChunk,
+                  "every slot header is read in one pass");
     u32x4 kq[kListEPT / 4], iq[kListEPT / 4];
     uint32_t own_hdr;
     // a thread past the lists reads its round's first entries (in bounds:
@@ -674,18 +684,22 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     int rem1;
     const int t1 = find_crossing<kBins>(L.h, R.take, L.tmp, &rem1);
     const uint32_t nc = L.h[t1];
-    bool bad = false;
+    // slots whose list was cut above t1 ("short" slots: their lists may miss
+    // candidates of bin t1 or above), listed in L.mem in (thread, pass) order
+    uint32_t badm = 0;
 #pragma unroll
     for (int j = 0; j < kHdrPT; ++j)
-        bad |= tid + j * kSelThreads < Ls.nslot && (int)(hv[j] >> 16) > t1;
-    if (tid == 0) L.misc[2] = 0;
-    __syncthreads();  // L.h read by all, misc[2] cleared
-    if (bad) L.misc[2] = 1;  // benign race: all write 1
-    __syncthreads();
-    if (L.misc[2] != 0) {  // uniform
-        select_scan(srow, n, t1, rem1, L, R);
+        if (tid + j * kSelThreads < Ls.nslot && (int)(hv[j] >> 16) > t1) badm |= 1u << j;
+    uint32_t nbad;
+    uint32_t bpos = block_excl_scan<kSelThreads>((uint32_t)__popc(badm), L.tmp, &nbad);  // barriers: L.h read by all
+    if (nbad > (uint32_t)(3 * kSelThreads)) {  // uniform: too many to list, select from the score row
+        select_scan(srow, n, S_max, t1, rem1, L, R);
         return R;
     }
+#pragma unroll
+    for (int j = 0; j < kHdrPT; ++j)
+        if ((badm >> j) & 1u) L.mem[bpos++] = (uint32_t)(tid + j * kSelThreads);
+    R.unordered = nbad > 0;
     R.nc = (int)nc;
     R.nsel = R.take - rem1;
     const int need = rem1;
@@ -701,7 +715,10 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     for (int rd = 0; rd < rounds; ++rd) {
         if (rd > 0) load_round(rd);
         const int e0 = rd * kListEPT * kSelThreads + tid * kListEPT;
-        const int cnt = e0 < total ? (int)(own_hdr & 0xffffu) - (e0 & (Ls.cap - 1)) : 0;  // valid entries here (own_hdr is a clamped slot's past the lists)
+        // valid entries here (own_hdr is a clamped slot's past the lists); a
+        // short slot's list is skipped: its rows are read below
+        const int cnt = (e0 < total && (int)(own_hdr >> 16) <= t1)
+                            ? (int)(own_hdr & 0xffffu) - (e0 & (Ls.cap - 1)) : 0;
         uint32_t selm = 0, shm = 0;
 #pragma unroll
         for (int j = 0; j < kListEPT; ++j) {
@@ -752,10 +769,78 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
         bsel += ts;
         bsh += tc;
     }
+    // 4. short slots: their 2048 rows straight from the score row (8 per
+    //    thread), routed like the list entries and appended after them
+#pragma unroll 1
+    for (uint32_t qb = 0; qb < nbad; ++qb) {
+        const int r0 = (int)L.mem[qb] * kListRows + tid * 8;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = srow[min(r0 + j, n - 1)];  // clamped, unconditional
+        uint32_t selm = 0, shm = 0, kk8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            kk8[j] = score_key(v[j]);
+            const int bin = (int)(kk8[j] >> 21);
+            if (r0 + j < n && bin > t1) selm |= 1u << j;
+            if (r0 + j < n && bin == t1 && refine) shm |= 1u << j;
+        }
+        uint32_t ps, pc, ts, tc;
+        block_excl_scan2<kSelThreads>((uint32_t)__popc(selm), (uint32_t)__popc(shm), L.tmp, &ps, &pc,
+                                      &ts, &tc);
+        ps += bsel;
+        pc += bsh;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if ((selm >> j) & 1u) {
+                if (ps < (uint32_t)kTopkMaxK) L.sel[ps] = r0 + j;
+                ++ps;
+            }
+            if ((shm >> j) & 1u) {
+                if (small) {
+                    if (pc < (uint32_t)kCandCap) { L.ck[pc] = kk8[j]; L.ci[pc] = (uint32_t)(r0 + j); }
+                } else if (pc < (uint32_t)S_max) {
+                    W.flat_key[pc] = kk8[j];
+                    W.flat_idx[pc] = (uint32_t)(r0 + j);
+                }
+                atomicAdd(&L.h[(kk8[j] >> 10) & (kBins - 1)], 1u);
+                ++pc;
+            }
+        }
+        bsel += ts;
+        bsh += tc;
+    }
     __syncthreads();
     if (!refine) return R;
     select_finish(W, R, need, small, L);
     return R;
+}
+
+// The query's top-k in ascending index order when the two lists are not
+// (select_query_lists with short slots): both lists sorted together in LDS
+// (bitonic, in `buf`, at least 2048 words), -1 padded.
+__device__ inline void select_write_sorted_any(const SelLds& L, const SelResult& R, int32_t* o, int k,
+                                               uint32_t* buf) {
+    const int tid = threadIdx.x;
+    const int take = R.nsel + R.nch;
+    int P = 1;
+    while (P < take) P <<= 1;
+    for (int i = tid; i < P; i += kSelThreads)
+        buf[i] = i < R.nsel ? (uint32_t)L.sel[i] : (i < take ? (uint32_t)L.chs[i - R.nsel] : 0xffffffffu);
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < P / 2; t += kSelThreads) {
+                const int lo = 2 * t - (t & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const uint32_t a = buf[lo], b = buf[hi];
+                if ((a > b) == up) { buf[lo] = b; buf[hi] = a; }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = tid; i < k; i += kSelThreads) o[i] = i < take ? (int32_t)buf[i] : -1;
 }
 
 // The query's top-k in ascending index order: the merge of the two ascending

@@ -220,11 +220,12 @@ int hsa_attn_decode(int dtype, const void *q, const void *swa_kv, const int32_t 
  * also leaves, per 2048 candidates, a list of those whose top 11 key bits
  * reach that block's own cut (at most 64..256 of them), and the select is
  * finished inside the attention kernel from those lists and the completed
- * first-digit histogram; if some block's list cannot hold the top-k's
- * threshold bin, the attention kernel selects from the score row instead
- * (slower, same result).  The rows are then taken as the selected-above-
- * threshold list followed by the chosen threshold-bin entries, each in index
- * order.  Other shapes run the two calls above.
+ * first-digit histogram; the 2048 scores of a block whose list cannot hold
+ * the top-k's threshold bin are read from the score row instead (the whole
+ * row when more than 768 blocks are so), with the same result.  The rows are
+ * then taken as the selected-above-threshold list followed by the chosen
+ * threshold-bin entries, each in index order except that entries of such
+ * blocks follow the others.  Other shapes run the two calls above.
  *
  *   Arguments: as in hsa_index_topk (q_idx must not be NULL) and
  *              hsa_attn_decode (sparse mode), same layouts and limits.
