@@ -137,11 +137,12 @@ def test_all_candidates_tie():
     np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (B, 1)))
 
 
-def test_concentrated_top_rows_take_the_score_row_path(oracle):
+def test_concentrated_top_rows_read_their_slot_from_the_score_row(oracle):
     """Most of the top-k inside one scoring workgroup's 2048 rows: that
     workgroup's candidate list cannot hold the threshold bin, so the select
-    reads the score row itself; results stay exact (against the separate
-    calls and the oracle's top-k), with duplicated rows for ties."""
+    reads that slot's 2048 scores from the score row; results stay exact
+    (against the separate calls and the oracle's top-k), with duplicated rows
+    for ties, and the written top-k is sorted."""
     import hybrid_sparse_compressed_amd as hsa
 
     B, S, k = 2, 40000, 512
@@ -204,6 +205,29 @@ def test_fused_lists_fp32_and_large_k(oracle):
     ridx = oracle.topk(rs.astype(np.float32), nc, k)
     inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(idx.cpu().numpy(), ridx))
     assert inter / int((ridx >= 0).sum()) >= 0.999
+
+
+def test_every_slot_short_selects_from_the_score_row():
+    """1.6M candidates with equal keys: all 782 slots' lists are cut above the
+    threshold bin (more than the 768 the select reads one by one), so every
+    workgroup selects from the whole score row; the lowest k indices win."""
+    import hybrid_sparse_compressed_amd as hsa
+
+    B, S, H, W, k = 1, 1600000, 64, 128, 512
+    g = torch.Generator(device="cuda").manual_seed(17)
+    bf = torch.bfloat16
+    w = dict(q=torch.randn(B, H, 576, generator=g, device="cuda").to(bf),
+             swa_kv=torch.randn(B, W, 576, generator=g, device="cuda").to(bf),
+             comp_kv=torch.randn(B, S, 576, generator=g, device="cuda").to(bf),
+             q_idx=torch.randn(B, 64, 128, generator=g, device="cuda").to(bf),
+             scale=1.0 / 24.0)
+    w["k_idx"] = torch.randn(B, 1, 128, generator=g, device="cuda").to(bf).expand(B, S, 128).contiguous()
+    w["n_cand"] = torch.tensor([S], dtype=torch.int32, device="cuda")
+    w["swa_len"] = torch.tensor([128], dtype=torch.int32, device="cuda")
+    w["comp_len"] = torch.tensor([S], dtype=torch.int32, device="cuda")
+    note("decode_sparse every slot short")
+    idx, _, _ = _check_against_separate(hsa, w, k, "every-slot-short")
+    np.testing.assert_array_equal(idx.cpu().numpy(), np.arange(k, dtype=np.int32)[None, :])
 
 
 def test_small_pool_takes_the_separate_path():
