@@ -659,11 +659,14 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
         const int n4 = n / 4;
         constexpr int U = 8;
         for (int b0 = 0; b0 < n4; b0 += U * kThreads) {
+            // unconditional loads (clamped index; chunks past the row are
+            // skipped below): a load inside a branch is followed by a wait
+            // there, which made the eight loads eight round trips
             f32x4 v[U];
 #pragma unroll
             for (int j = 0; j < U; ++j) {
-                const int i4 = b0 + j * kThreads + tid;
-                if (i4 < n4) v[j] = *reinterpret_cast<const f32x4*>(src + 4 * i4);
+                const int i4 = min(b0 + j * kThreads + tid, n4 - 1);
+                v[j] = *reinterpret_cast<const f32x4*>(src + 4 * i4);
             }
 #pragma unroll
             for (int j = 0; j < U; ++j) {
@@ -682,10 +685,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     for (int b0 = i0; b0 < n; b0 += 8 * kThreads) {
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = b0 + j * kThreads + tid;
-            if (i < n) v[j] = src[i];
-        }
+        for (int j = 0; j < 8; ++j) v[j] = src[min(b0 + j * kThreads + tid, n - 1)];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = b0 + j * kThreads + tid;
