@@ -305,7 +305,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         const int grp = kThreads - 1 - tid;
         uint32_t hb[8], s8 = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { hb[j] = hist[grp * 8 + j]; s8 += hb[j]; }
+        for (int h4 = 0; h4 < 2; ++h4) {  // 16-byte LDS reads
+            const u32x4 v = reinterpret_cast<const u32x4*>(hist)[2 * grp + h4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) { hb[4 * h4 + c] = v[c]; s8 += v[c]; }
+        }
         if (tid == 0) cut_res = 0;
         uint32_t all;
         const uint32_t above = block_excl_scan<kThreads>(s8, scan_tmp, &all);
@@ -322,10 +326,15 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         // rows 8t .. 8t+7 of the workgroup at or above the cut, in index order
         static_assert(kScoreRowsMulti == 8 * kThreads && kScoreRowsMulti == kListRows, "8 rows per thread");
         uint32_t kk[8], m = 0;
+        {
+            const f32x4 s0 = reinterpret_cast<const f32x4*>(stage)[2 * tid];
+            const f32x4 s1 = reinterpret_cast<const f32x4*>(stage)[2 * tid + 1];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) { kk[c] = score_key(s0[c]); kk[4 + c] = score_key(s1[c]); }
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = tid * 8 + j;
-            kk[j] = score_key(stage[i]);
             if (i < nr && (kk[j] >> 21) >= a) m |= 1u << j;
         }
         uint32_t cnt;
