@@ -7,8 +7,9 @@ each, 64 heads over a 576-wide latent (value 512), window 128, indexer
 One step = one decode layer-step: indexer scores over every C4 key, exact
 radix top-512 select, and the SWA + selected-C4 attention with split-KV merge,
 together with the decode-time compression state update, all in one
-hsa_decode_step call (scoring; filter, with the compression-state append
-riding in the same launch; attention that finishes the select; merge): each
+hsa_decode_step call (scoring, which also leaves per-2048-candidate lists
+and carries the compression-state append as extra workgroups; attention that
+finishes the select from the lists; merge): each
 sequence's new token enters its 4-token ring and on every 4th step completes
 the block, whose C4 entry is written to the pool before the attention runs.
 Two copies of the

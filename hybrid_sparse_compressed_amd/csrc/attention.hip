@@ -31,13 +31,14 @@
 // latent-576 shape, prefill64_kernel instead gives a query's 64 heads one
 // 8-wave workgroup that gathers each tile once.
 //
-// Fused sparse decode (the whole C4 layer-step after the filter kernel): a
+// Fused sparse decode (the whole C4 layer-step after the scoring launch): a
 // workgroup with compressed rows first finishes its sequence's top-k select
-// itself (select.hpp, in the LDS its tiles use later) and takes its rows from
-// the selected list followed by the chosen short-list entries, both in index
-// order, so no separate select kernel, index round trip or sort sits on the
+// itself from the scoring workgroups' candidate lists and the first-digit
+// histogram (select.hpp, in the LDS its tiles use later) and takes its rows
+// from the selected list followed by the chosen short-list entries, so no
+// filter pass, separate select kernel, index round trip or sort sits on the
 // attention's critical path.  One extra workgroup per sequence writes the
-// ascending top-k indices and clears the first-digit histogram.
+// ascending top-k indices; the merge kernel clears the histogram.
 #include "hsa_common.hpp"
 #include "hsa_internal.hpp"
 #include "select.hpp"

@@ -253,7 +253,7 @@ int hsa_decode_sparse(int dtype, const void *q_idx, const void *k_idx, const int
  * [NK "DeepSeek V4 的新架构", five state classes]: SWA and C4 pools plus the
  * in-flight C4 block; [KD "Arquitectura del Sistema", Hierarchical
  * Multi-Stream Overlap]: attention preparation overlapped with other work --
- * here the append runs inside the launch that finishes the candidate filter.
+ * here the append runs as extra workgroups of the scoring launch.
  *
  * Results equal hsa_compress_append(dtype, x_tok, g_tok, bias, ring_x,
  * ring_g, pos, comp_kv, B, d_qk, 4, S_max) followed by hsa_decode_sparse(...)
