@@ -571,9 +571,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             for (int j = 0; j < NCH; ++j) {
                 const int c = lane + j * kWave;
                 const int row = c / CPRW, col = (c % CPRW) * 4;
-                if (h0 + row < a.H)
-                    *reinterpret_cast<f32x4*>(a.part_o + (prow0 + row) * DV + wave * DW + col) =
-                        *reinterpret_cast<const f32x4*>(ob + row * OS + col);
+                if (h0 + row < a.H)  // streamed past the L2: only the merge kernel reads it
+                    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ob + row * OS + col),
+                                                reinterpret_cast<f32x4*>(a.part_o + (prow0 + row) * DV + wave * DW + col));
             }
             return;
         }
