@@ -982,10 +982,15 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
             }
         }
     }
-    if (has_d) {
-        T* o = reinterpret_cast<T*>(out) + ((size_t)b * H + h) * DV;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Elem<T>::store(o, d + e, acc[e] * inv);
+    if (has_d) {  // the thread's 4 channels in one store
+        T* o = reinterpret_cast<T*>(out) + ((size_t)b * H + h) * DV + d;
+        if constexpr (sizeof(T) == 2) {
+            const uint2 pk{(uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16),
+                           (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16)};
+            *reinterpret_cast<uint2*>(o) = pk;
+        } else {
+            *reinterpret_cast<f32x4*>(o) = acc * inv;
+        }
     }
     if (lse && tid == 0) lse[(size_t)b * H + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
     // fused decode: every reader of the sequence's first-digit histogram (the
