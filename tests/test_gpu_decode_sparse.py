@@ -230,6 +230,26 @@ def test_every_slot_short_selects_from_the_score_row():
     np.testing.assert_array_equal(idx.cpu().numpy(), np.arange(k, dtype=np.int32)[None, :])
 
 
+@pytest.mark.parametrize("k", [1, 3, 100])
+def test_fused_lists_small_k(oracle, k):
+    """Small k on the list path (one or a few selected rows, list capacity at
+    its minimum), ragged candidate counts, against the separate calls and the
+    oracle's top-k."""
+    import hybrid_sparse_compressed_amd as hsa
+
+    B, S = 3, 25000
+    w = _small_case(18 + k, B, S, k=k, dup=True)
+    w["n_cand"] = torch.tensor([S, S - 999, 2], dtype=torch.int32, device="cuda")
+    w["swa_len"] = torch.tensor([128, 9, 128], dtype=torch.int32, device="cuda")
+    w["comp_len"] = torch.tensor([S, S, S], dtype=torch.int32, device="cuda")
+    note("decode_sparse small k=%d" % k)
+    idx, _, _ = _check_against_separate(hsa, w, k, "k%d" % k)
+    nc = w["n_cand"].cpu().numpy()
+    rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
+    ridx = oracle.topk(rs.astype(np.float32), nc, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+
+
 def test_small_pool_takes_the_separate_path():
     import hybrid_sparse_compressed_amd as hsa
 
