@@ -890,7 +890,8 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
                 *reinterpret_cast<float2*>(a.part_ml + prow * 2) = float2{m_run, l_run};
             float* po = a.part_o + prow * DV + half * DW;
 #pragma unroll
-            for (int t = 0; t < NMT; ++t) *reinterpret_cast<f32x4*>(po + t * 16 + quad * 4) = acc[t];
+            for (int t = 0; t < NMT; ++t)  // streamed past the L2: only the merge kernel reads it
+                __builtin_nontemporal_store(acc[t], reinterpret_cast<f32x4*>(po + t * 16 + quad * 4));
             return;
         }
     }
