@@ -173,7 +173,7 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
     hipStream_t st = as_stream(stream);
     uint8_t* ws_sel = static_cast<uint8_t*>(workspace);
     uint8_t* ws_attn = ws_sel + round256(hsa::topk_workspace_bytes(B, S_max, k));
-    if (S_max > hsa::kRowSelectCap && hsa::index_lists_apply(S_max, k) &&
+    if (S_max > hsa::kRowSelectCap && hsa::index_lists_apply(S_max, k, B) &&
         hsa::fused_decode_supported(B, H, W, k)) {
         // the append rides in the scoring launch, which ends before the attention
         // reads the pool; scoring never reads it

@@ -108,6 +108,7 @@ struct AttnArgs {
     int H, W, S_max, k, m, T_len, n_q, q_start;
     int rows_per_split, n_split, max_rows;
     int hblocks, n_queries;  // prefill: head blocks per query, queries in the grid
+    int list_rows_lg;     // fused decode: log2 of the candidate rows per list slot
     float scale_log2;     // scale * log2(e)
 };
 
@@ -130,7 +131,9 @@ template <typename T, int DQK, int DV> struct TileLds {
 // with 16-byte loads.
 static_assert(kTile == 64, "the fp32 PV map assumes 16 steps of 4 rows");
 
-constexpr int kModeDecode = 0, kModePrefill = 1, kModeFused = 2;
+// kModeFused: 2048-row list slots (constant slot arithmetic, the large-pool
+// case); kModeFusedVar: list slots of 256 .. 2048 rows (a.list_rows_lg)
+constexpr int kModeDecode = 0, kModePrefill = 1, kModeFused = 2, kModeFusedVar = 3;
 
 // LDS the select prologue of the fused mode carves out of the tile buffers
 constexpr size_t kSelLdsBytes = (size_t)sel::kBins * 4 + (2 * sel::kSelNW + 2) * 4 + 3 * (size_t)sel::kMaxSeg * 4 +
@@ -161,7 +164,8 @@ __device__ inline sel::SelLds sel_lds_at(unsigned char* base) {
 template <typename T, int DQK, int DV, int MODE>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     constexpr bool PREFILL = MODE == kModePrefill;
-    constexpr bool FUSED = MODE == kModeFused;
+    constexpr bool FUSED = MODE == kModeFused || MODE == kModeFusedVar;
+    const int list_rows_lg = MODE == kModeFusedVar ? a.list_rows_lg : 11;
     typedef TileLds<T, DQK, DV> L;
     typedef Mma<T> M;
     constexpr int V16 = Elem<T>::kPer16B;          // elements per 16-byte chunk
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         if ((int)blockIdx.x == a.n_split) {  // the sequence's ascending top-k output
             if (hb != 0) return;
             const sel::SelResult R = sel::select_query_lists(
-                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, a.k, SL, [] {});
+                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, list_rows_lg, a.k, SL, [] {});
             if (R.unordered)  // uniform
                 sel::select_write_sorted_any(SL, R, a.topk_out + (size_t)b * a.k, a.k, SL.ck);
             else
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             // Q goes out right behind the select's first loads: the select
             // never waits for it, and it arrives during the select
             const sel::SelResult R = sel::select_query_lists(
-                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, j1, SL, load_q);
+                Wq, a.scores + (size_t)b * a.S_max, n, a.S_max, a.k, list_rows_lg, j1, SL, load_q);
             f_jn = j1 - f_j0;
             for (int t = tid; t < f_jn; t += kAttnThreads) {
                 const int j = f_j0 + t;
@@ -1005,7 +1009,8 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
 template <typename T, int DQK, int DV, int MODE>
 hipError_t launch_attn_kernel(const AttnArgs& a, dim3 grid, hipStream_t st) {
     size_t lds = TileLds<T, DQK, DV>::kBytes;
-    if (MODE == kModeFused && lds < kSelStageOff + kSelStageBytes) lds = kSelStageOff + kSelStageBytes;
+    if ((MODE == kModeFused || MODE == kModeFusedVar) && lds < kSelStageOff + kSelStageBytes)
+        lds = kSelStageOff + kSelStageBytes;
     static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
@@ -1202,6 +1207,7 @@ hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv
     a.comp_len = comp_len;
     a.sel_ws = static_cast<uint8_t*>(sel_ws);
     a.scores = scores;
+    a.list_rows_lg = sel::list_rows_log2(S_max, B);
     a.n_cand = n_cand;
     a.topk_out = topk_out;
     a.out = out;
@@ -1222,7 +1228,8 @@ hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv
     a.scale_log2 = scale * kLog2e;
     // one more workgroup column per sequence writes the ascending top-k
     dim3 grid((unsigned)p.n_split + 1u, (unsigned)B, (unsigned)ceil_div(H, kHeadsPerWG));
-    hipError_t e = dispatch_attn<kModeFused>(dtype, d_qk, d_v, a, grid, st);
+    hipError_t e = a.list_rows_lg == 11 ? dispatch_attn<kModeFused>(dtype, d_qk, d_v, a, grid, st)
+                                        : dispatch_attn<kModeFusedVar>(dtype, d_qk, d_v, a, grid, st);
     if (e != hipSuccess) return e;
     return launch_merge(dtype, d_v, a, B, H, p.n_split, S_max, k, st);
 }

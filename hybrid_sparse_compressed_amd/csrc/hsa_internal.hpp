@@ -69,7 +69,7 @@ struct AppendJob {
 // candidate list, for S_max > kRowSelectCap where sel::lists_apply holds: the
 // select is finished by the fused decode attention.  job != nullptr: the
 // append runs as extra workgroups of the same launch.
-bool index_lists_apply(int S_max, int k);
+bool index_lists_apply(int S_max, int k, int Nq);
 hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
                               int S_max, int k, void* ws, const AppendJob* job, hipStream_t st);

@@ -109,8 +109,9 @@ __device__ __forceinline__ float reduce_scatter8(float (&v)[8], int sub) {
     return r;  // the row (sub >> (LB - 3)) of the batch
 }
 
-// SEL: 0 scores only; 1 also the first-digit histogram; 2 also the
-// workgroup's candidate list (select.hpp), and grid rows y >= Nq carry the
+// SEL: 0 scores only; 1 also the first-digit histogram; 2 (2048-row slots)
+// and 3 (256 .. 2048-row slots) also the workgroup's candidate list
+// (select.hpp), and grid rows y >= Nq carry the
 // decode-time C4 append of `job` (one (sequence, 256-chunk span) per
 // workgroup; it touches only the append's own buffers).
 template <typename T, int LPR, int SEL>
@@ -119,7 +120,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const int32_t* __restrict__ n_cand, float* __restrict__ scores, uint8_t* __restrict__ ws,
     int B, int H_I, int S_max, int k, int rows_per_wg, int Nq, AppendJob job) {
     constexpr bool HIST = SEL >= 1;
-    constexpr bool LIST = SEL == 2;
+    constexpr bool LIST = SEL >= 2;
+    // log2 of the rows per list slot: fixed at 2048 for SEL 2 (so that the
+    // large-pool path compiles with constant slot arithmetic), any of 256 ..
+    // 2048 for SEL 3
+    const int rows_lg = SEL == 3 ? (int)__builtin_ctz((unsigned)rows_per_wg) : 11;
     constexpr int V = Elem<T>::kPer16B;
     constexpr int DI = LPR * V;            // indexer width
     constexpr int RPL = kWave / LPR;       // rows covered by one wave-wide load
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     if (r0 >= r1) {  // uniform over the workgroup: no candidate rows here
         __builtin_amdgcn_s_waitcnt(0);  // retire the speculative loads first
         if constexpr (LIST) {  // an empty list that left nothing out, every call
-            if (tid == 0) lists_of(ws_of(ws, q, S_max, k), S_max, k).hdr[blockIdx.x] = 0u;
+            if (tid == 0) lists_of(ws_of(ws, q, S_max, k), S_max, k, rows_lg).hdr[blockIdx.x] = 0u;
         }
         return;
     }
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         // the cut a: the lowest bin with at most `cap` of this workgroup's
         // candidates at or above it (thread t sums the 8 bins of group
         // 255 - t, so the scan runs from the top bin down)
-        const Lists Ls = lists_of(ws_of(ws, q, S_max, k), S_max, k);
+        const Lists Ls = lists_of(ws_of(ws, q, S_max, k), S_max, k, rows_lg);
         const uint32_t cap = (uint32_t)Ls.cap;
         const int grp = kThreads - 1 - tid;
         uint32_t hb[8], s8 = 0;
@@ -323,19 +328,23 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         }
         __syncthreads();
         const uint32_t a = cut_res;
-        // rows 8t .. 8t+7 of the workgroup at or above the cut, in index order
-        static_assert(kScoreRowsMulti == 8 * kThreads && kScoreRowsMulti == kListRows, "8 rows per thread");
+        // rows rpt t .. rpt t + rpt - 1 of the workgroup (rpt = 1, 2, 4 or 8
+        // rows per thread) at or above the cut, in index order
+        const int rpt = (1 << rows_lg) / kThreads;
         uint32_t kk[8], m = 0;
-        {
+        if (rpt == 8) {
             const f32x4 s0 = reinterpret_cast<const f32x4*>(stage)[2 * tid];
             const f32x4 s1 = reinterpret_cast<const f32x4*>(stage)[2 * tid + 1];
 #pragma unroll
             for (int c = 0; c < 4; ++c) { kk[c] = score_key(s0[c]); kk[4 + c] = score_key(s1[c]); }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kk[j] = score_key(stage[min(tid * rpt + j, rows_per_wg - 1)]);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int i = tid * 8 + j;
-            if (i < nr && (kk[j] >> 21) >= a) m |= 1u << j;
+            const int i = tid * rpt + j;
+            if (j < rpt && i < nr && (kk[j] >> 21) >= a) m |= 1u << j;
         }
         uint32_t cnt;
         uint32_t pos = block_excl_scan<kThreads>((uint32_t)__popc(m), scan_tmp, &cnt);
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
             if ((m >> j) & 1u) {
                 const uint32_t at = list_pos(e0 + pos);
                 Ls.key[at] = kk[j];
-                Ls.idx[at] = (uint32_t)(r0 + tid * 8 + j);
+                Ls.idx[at] = (uint32_t)(r0 + tid * rpt + j);
                 ++pos;
             }
         }
@@ -872,9 +881,11 @@ template <typename T, int LPR>
 hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32_t* q_seq,
                         const int32_t* n_cand, float* scores, uint8_t* ws, int Nq, int H_I,
                         int S_max, int k, int sel, const AppendJob* job, hipStream_t st) {
-    const int rows = sel ? kScoreRowsMulti : min(S_max, 8192);
+    const int rows_lg = list_rows_log2(S_max, Nq);
+    if (sel == 2 && rows_lg != 11) sel = 3;  // smaller slots: the variable-slot instantiation
+    const int rows = sel >= 2 ? (1 << rows_lg) : sel ? kScoreRowsMulti : min(S_max, 8192);
     dim3 grid((unsigned)ceil_div(S_max, rows), (unsigned)Nq);
-    if (sel == 2 && job) {  // append rows after the query rows
+    if (sel >= 2 && job) {  // append rows after the query rows
         const int units = job->B * ((job->D / Elem<T>::kPer16B + kThreads - 1) / kThreads);
         grid.y += (unsigned)ceil_div(units, (int)grid.x);
     }
@@ -882,7 +893,11 @@ hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32
     const AppendJob& aj = job ? *job : none;
     const size_t lds = (size_t)rows * sizeof(float);  // staged scores
     ProfScope prof(kProfScore, st);
-    if (sel == 2)
+    if (sel == 3)
+        hipLaunchKernelGGL((score_kernel<T, LPR, 3>), grid, dim3(kThreads), lds, st,
+                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
+                           S_max, k, rows, Nq, aj);
+    else if (sel == 2)
         hipLaunchKernelGGL((score_kernel<T, LPR, 2>), grid, dim3(kThreads), lds, st,
                            (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
                            S_max, k, rows, Nq, aj);
@@ -920,7 +935,7 @@ size_t topk_workspace_bytes(int Nq, int S_max, int k) {
 // Scores, first-digit histogram and per-workgroup candidate lists (the fused
 // decode select reads them), with the decode-time C4 append of `job` (may be
 // null) in the same launch.
-bool index_lists_apply(int S_max, int k) { return lists_apply(S_max, k); }
+bool index_lists_apply(int S_max, int k, int Nq) { return lists_apply(S_max, k, Nq); }
 
 hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,

@@ -437,26 +437,44 @@ __device__ inline SelResult select_query(const QWs& W, int n, int S_max, int k, 
 // than `cap` candidates at or above t1: far more than its share on typical
 // rows, but possible for adversarial or tied scores) the select falls back to
 // passes over the score row itself, with the same result.
-constexpr int kListRows = 2048;   // rows per scoring workgroup
+constexpr int kListRows = 2048;   // most rows per scoring workgroup (slot)
 constexpr int kListEPT = 32;      // list entries per thread per read round
 
-__host__ __device__ inline int list_slots(int S_max) { return (S_max + kListRows - 1) >> 11; }
-static_assert(kListRows == 2048, "list_slots shifts by 11");
+// log2 of the rows per slot: 2048, halved while the Nq queries would give
+// fewer than 512 scoring workgroups (two per compute unit), down to 256
+__host__ __device__ inline int list_rows_log2(int S_max, int Nq) {
+    int lg = 11;
+    while (lg > 8 && (long long)Nq * ((S_max + (1 << lg) - 1) >> lg) < 512) --lg;
+    return lg;
+}
+__host__ __device__ inline int list_slots(int S_max, int rows_lg) {
+    return (S_max + (1 << rows_lg) - 1) >> rows_lg;
+}
 
-// log2 of the list capacity per workgroup: the smallest power of two in
-// [64, 256] that is at least four times a workgroup's even share of the
-// top-k, 4 k 2048 / S_max (compared by products: no division on the device)
-__host__ __device__ inline int list_cap_log2(int S_max, int k) {
-    const long long need = (long long)4 * k * kListRows;
+// log2 of the list capacity per slot: the smallest power of two in [64, 256]
+// that is at least four times a slot's even share of the top-k,
+// 4 k rows / S_max (compared by products: no division on the device)
+__host__ __device__ inline int list_cap_log2(int S_max, int k, int rows_lg) {
+    const long long need = ((long long)4 * k) << rows_lg;
     int lg = 6;
     while (lg < 8 && ((long long)S_max << lg) < need) ++lg;
     return lg;
 }
-__host__ __device__ inline int list_cap(int S_max, int k) { return 1 << list_cap_log2(S_max, k); }
 
-// the lists are used when that capacity covers four even shares
-__host__ __device__ inline bool lists_apply(int S_max, int k) {
-    return S_max > kRowSelectCap && (long long)4 * k * kListRows <= 256LL * S_max;
+// words of the list area: headers, alignment pad, keys and indices in whole
+// rounds of 8192
+__host__ __device__ inline long long list_words(int S_max, int k, int rows_lg) {
+    const long long slots = list_slots(S_max, rows_lg);
+    const long long ent = ((slots << list_cap_log2(S_max, k, rows_lg)) + 8191) & ~8191LL;
+    return slots + 3 + 2 * ent;
+}
+
+// the lists are used when that capacity covers four even shares, every
+// header is read in one pass and the lists fit the candidate area
+__host__ __device__ inline bool lists_apply(int S_max, int k, int Nq) {
+    const int rl = list_rows_log2(S_max, Nq);
+    return S_max > kRowSelectCap && (((long long)4 * k) << rl) <= 256LL * S_max &&
+           list_slots(S_max, rl) <= 2048 && list_words(S_max, k, rl) <= 2LL * S_max;
 }
 
 // Lists live in the query's candidate area (cand_key / cand_idx, 2 S_max
@@ -478,12 +496,14 @@ struct Lists {
     uint32_t* hdr;
     uint32_t* key;
     uint32_t* idx;
-    int nslot, cap, cap_lg;
+    int nslot, cap, cap_lg, rows_lg;
 };
-__device__ inline Lists lists_of(const QWs& W, int S_max, int k) {
+// rows_lg: list_rows_log2(S_max, Nq), which the host passes down
+__device__ inline Lists lists_of(const QWs& W, int S_max, int k, int rows_lg) {
     Lists l;
-    l.nslot = list_slots(S_max);
-    l.cap_lg = list_cap_log2(S_max, k);
+    l.rows_lg = rows_lg;
+    l.nslot = list_slots(S_max, l.rows_lg);
+    l.cap_lg = list_cap_log2(S_max, k, l.rows_lg);
     l.cap = 1 << l.cap_lg;
     l.hdr = W.cand_key;
     // 16-byte alignment by an index offset (a pointer rebuilt from an integer
@@ -617,7 +637,8 @@ __device__ inline void select_scan(const float* srow, int n, int S_max, int t1, 
 //   (the caller's own loads that the select does not wait for go there)
 template <typename F>
 __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, int n, int S_max,
-                                               int k, int j_need, const SelLds& L, F&& after_loads) {
+                                               int k, int rows_lg, int j_need, const SelLds& L,
+                                               F&& after_loads) {
     const int tid = threadIdx.x;
     SelResult R;
     R.nseg = 0;
@@ -634,7 +655,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
         R.nsel = n;
         return R;
     }
-    const Lists Ls = lists_of(W, S_max, k);
+    const Lists Ls = lists_of(W, S_max, k, rows_lg);
     const int total = Ls.nslot << Ls.cap_lg;
     const int rounds = (total + kListEPT * kSelThreads - 1) >> 13;
     static_assert(kListEPT * kSelThreads == 8192, "rounds of 8192 entries");
@@ -655,8 +676,7 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
     uint32_t hv[kHdrPT];
 #pragma unroll
     for (int j = 0; j < kHdrPT; ++j) hv[j] = Ls.hdr[min(tid + j * kSelThreads, Ls.nslot - 1)];
-    static_assert(kHdrPT * kSelThreads * kListRows >= kTopkMaxSegments * kFilterChunk,
-                  "every slot header is read in one pass");
+    // (lists_apply keeps nslot <= kHdrPT * kSelThreads = 2048)
     u32x4 kq[kListEPT / 4], iq[kListEPT / 4];
     uint32_t own_hdr;
     // a thread past the lists reads its round's first entries (in bounds:
@@ -769,21 +789,23 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
         bsel += ts;
         bsh += tc;
     }
-    // 4. short slots: their 2048 rows straight from the score row (8 per
+    // 4. short slots: their rows straight from the score row (up to 8 per
     //    thread), routed like the list entries and appended after them
+    const int rpt = (1 << Ls.rows_lg) / kSelThreads;  // rows per thread: 1, 2, 4 or 8
 #pragma unroll 1
     for (uint32_t qb = 0; qb < nbad; ++qb) {
-        const int r0 = (int)L.mem[qb] * kListRows + tid * 8;
+        const int r0 = ((int)L.mem[qb] << Ls.rows_lg) + tid * rpt;
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = srow[min(r0 + j, n - 1)];  // clamped, unconditional
+        for (int j = 0; j < 8; ++j) v[j] = srow[min(r0 + j, n - 1)];  // clamped, unconditional; j >= rpt unused
         uint32_t selm = 0, shm = 0, kk8[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             kk8[j] = score_key(v[j]);
             const int bin = (int)(kk8[j] >> 21);
-            if (r0 + j < n && bin > t1) selm |= 1u << j;
-            if (r0 + j < n && bin == t1 && refine) shm |= 1u << j;
+            const bool ok = j < rpt && r0 + j < n;
+            if (ok && bin > t1) selm |= 1u << j;
+            if (ok && bin == t1 && refine) shm |= 1u << j;
         }
         uint32_t ps, pc, ts, tc;
         block_excl_scan2<kSelThreads>((uint32_t)__popc(selm), (uint32_t)__popc(shm), L.tmp, &ps, &pc,
