@@ -217,10 +217,11 @@ int hsa_attn_decode(int dtype, const void *q, const void *swa_kv, const int32_t 
  * to rounding, since the attention may sum the selected rows in another
  * order.  For S_max > 12,288 and S_max >= 32 k (and B, H, W, k that split
  * the rows over at least two workgroups per sequence) the scoring launch
- * also leaves, per 2048 candidates, a list of those whose top 11 key bits
- * reach that block's own cut (at most 64..256 of them), and the select is
+ * also leaves, per block of 256..2048 candidates (one per scoring
+ * workgroup), a list of those whose top 11 key bits reach that block's own
+ * cut (at most 64..256 of them), and the select is
  * finished inside the attention kernel from those lists and the completed
- * first-digit histogram; the 2048 scores of a block whose list cannot hold
+ * first-digit histogram; the scores of a block whose list cannot hold
  * the top-k's threshold bin are read from the score row instead (the whole
  * row when more than 768 blocks are so), with the same result.  The rows are
  * then taken as the selected-above-threshold list followed by the chosen
