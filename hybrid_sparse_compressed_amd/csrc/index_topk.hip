@@ -725,28 +725,44 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     int nl = n;
     const uint16_t* li = nullptr;
     if (m <= kRowListCap) {
-        constexpr int RMAX = kRowSelectCap / kThreads;  // keys per thread at most (48)
-        const int E = 4 * ceil_div(n, 4 * kThreads);
-        const int s0 = min(n, tid * E), s1 = min(n, s0 + E);
-        uint32_t r[RMAX];
-        uint32_t cnt = 0;
+        // wave w takes keys [w P, w P + P) (P a multiple of 64), lane l the
+        // keys w P + 64 j + l: consecutive lanes read consecutive LDS words
+        // (no bank conflicts) and a ballot per 64 keys keeps index order.
+        // Every key is in registers before the barrier, so the compacted
+        // list can overwrite the keys in place afterwards.
+        constexpr int JMAX = kRowSelectCap / kThreads;  // 64-key chunks per wave at most (48)
+        const int lane = lane_id(), w = tid / kWave;
+        const int P = ceil_div(n, kThreads) * kWave;
+        const int wb = w * P;
+        uint32_t r[JMAX];
+        uint32_t cnt = 0;  // wave-uniform
 #pragma unroll
-        for (int j = 0; j < RMAX; ++j) {
-            const int s = s0 + j;
-            r[j] = s < s1 ? keys[s] : 0u;
-            cnt += (s < s1 && r[j] >= lo1) ? 1u : 0u;
+        for (int j = 0; j < JMAX; ++j) {
+            const int s = wb + kWave * j + lane;
+            const bool in = kWave * j < P && s < n;
+            r[j] = in ? keys[s] : 0u;
+            cnt += (uint32_t)__popcll(__ballot(in && r[j] >= lo1));
         }
-        uint32_t tot;
-        const uint32_t base = block_excl_scan<kThreads>(cnt, tmp, &tot);  // barriers: all reads done
-        uint32_t pos = base;
+        if (lane == 0) tmp[w] = cnt;
+        __syncthreads();  // every key read
+        uint32_t run = 0, tot = 0;
 #pragma unroll
-        for (int j = 0; j < RMAX; ++j) {
-            const int s = s0 + j;
-            if (s < s1 && r[j] >= lo1) {
-                keys[pos] = r[j];
-                lidx[pos] = (uint16_t)s;
-                ++pos;
+        for (int i = 0; i < kNW; ++i) {
+            run += i < w ? tmp[i] : 0u;
+            tot += tmp[i];
+        }
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+            const int s = wb + kWave * j + lane;
+            const bool take_it = kWave * j < P && s < n && r[j] >= lo1;
+            const unsigned long long mk = __ballot(take_it);
+            if (take_it) {
+                const uint32_t p = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+                keys[p] = r[j];
+                lidx[p] = (uint16_t)s;
             }
+            run += (uint32_t)__popcll(mk);
         }
         __syncthreads();
         nl = (int)tot;
