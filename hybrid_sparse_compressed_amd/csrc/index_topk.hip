@@ -725,25 +725,28 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     int nl = n;
     const uint16_t* li = nullptr;
     if (m <= kRowListCap) {
-        // wave w takes keys [w P, w P + P) (P a multiple of 64), lane l the
-        // keys w P + 64 j + l: consecutive lanes read consecutive LDS words
-        // (no bank conflicts) and a ballot per 64 keys keeps index order.
-        // Every key is in registers before the barrier, so the compacted
-        // list can overwrite the keys in place afterwards.
-        constexpr int JMAX = kRowSelectCap / kThreads;  // 64-key chunks per wave at most (48)
+        // wave w takes keys [w P, w P + P) (P a multiple of 256), and in chunk j
+        // lane l the four keys w P + 256 j + 4 l .. + 3: one 16-byte LDS read
+        // per lane covers 256 consecutive keys without bank conflicts, and a
+        // wave prefix sum of the per-lane counts keeps index order.  Every key
+        // is in registers before the barrier, so the compacted list can
+        // overwrite the keys in place afterwards.
+        constexpr int JMAX = kRowSelectCap / (4 * kThreads);  // chunks per wave at most (12)
         const int lane = lane_id(), w = tid / kWave;
-        const int P = ceil_div(n, kThreads) * kWave;
+        const int P = ceil_div(n, 4 * kThreads) * (4 * kWave);
         const int wb = w * P;
-        uint32_t r[JMAX];
-        uint32_t cnt = 0;  // wave-uniform
+        u32x4 r[JMAX];
+        uint32_t cnt = 0;
 #pragma unroll
         for (int j = 0; j < JMAX; ++j) {
-            const int s = wb + kWave * j + lane;
-            const bool in = kWave * j < P && s < n;
-            r[j] = in ? keys[s] : 0u;
-            cnt += (uint32_t)__popcll(__ballot(in && r[j] >= lo1));
+            const int s = wb + 4 * kWave * j + 4 * lane;
+            r[j] = (4 * kWave * j < P && s < n) ? *reinterpret_cast<const u32x4*>(keys + s)
+                                                : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cnt += (s + e < n && r[j][e] >= lo1) ? 1u : 0u;
         }
-        if (lane == 0) tmp[w] = cnt;
+        const uint32_t wcnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), kWave - 1);
+        if (lane == 0) tmp[w] = wcnt;
         __syncthreads();  // every key read
         uint32_t run = 0, tot = 0;
 #pragma unroll
@@ -753,16 +756,26 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
         }
 #pragma unroll
         for (int j = 0; j < JMAX; ++j) {
-            const int s = wb + kWave * j + lane;
-            const bool take_it = kWave * j < P && s < n && r[j] >= lo1;
-            const unsigned long long mk = __ballot(take_it);
-            if (take_it) {
-                const uint32_t p = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
-                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-                keys[p] = r[j];
-                lidx[p] = (uint16_t)s;
+            if (4 * kWave * j >= P) break;  // wave-uniform
+            const int s = wb + 4 * kWave * j + 4 * lane;
+            bool t[4];
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                t[e] = s + e < n && r[j][e] >= lo1;
+                c += t[e] ? 1u : 0u;
             }
-            run += (uint32_t)__popcll(mk);
+            const uint32_t inc = wave_incl_scan(c);
+            uint32_t p = run + inc - c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (t[e]) {
+                    keys[p] = r[j][e];
+                    lidx[p] = (uint16_t)(s + e);
+                    ++p;
+                }
+            }
+            run += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
         }
         __syncthreads();
         nl = (int)tot;
