@@ -739,11 +739,13 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
         uint32_t cnt = 0;
 #pragma unroll
         for (int j = 0; j < JMAX; ++j) {
+            // chunks past the wave's range count nothing (their zeros would
+            // pass the test below when lo1 is 0: a crossing at bin 0)
+            const bool in = 4 * kWave * j < P;
             const int s = wb + 4 * kWave * j + 4 * lane;
-            r[j] = (4 * kWave * j < P && s < n) ? *reinterpret_cast<const u32x4*>(keys + s)
-                                                : u32x4{0u, 0u, 0u, 0u};
+            r[j] = (in && s < n) ? *reinterpret_cast<const u32x4*>(keys + s) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cnt += (s + e < n && r[j][e] >= lo1) ? 1u : 0u;
+            for (int e = 0; e < 4; ++e) cnt += (in && s + e < n && r[j][e] >= lo1) ? 1u : 0u;
         }
         const uint32_t wcnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), kWave - 1);
         if (lane == 0) tmp[w] = wcnt;

@@ -84,6 +84,30 @@ def test_select_special_patterns(oracle, S):
     assert got[1].tolist() == list(range(S - k, S))
 
 
+@pytest.mark.parametrize("k", [64, 2048])
+def test_row_select_crowded_boundary_bins(oracle, k):
+    """Rows of the one-workgroup path (n <= 12288) whose boundary bin is crowded
+    however the first digit is placed: a row of two levels (the short list
+    exceeds 4096 entries at k = 2048), of 40 levels (hundreds of equal keys at
+    the boundary), a tight cluster with one huge outlier (the row's key range
+    is stretched so the cluster shares one first-digit bin) and a tight
+    cluster alone."""
+    S = 12000
+    rng = np.random.default_rng(11)
+    pats = [
+        rng.integers(0, 2, S).astype(np.float32),
+        rng.integers(0, 40, S).astype(np.float32),
+        (1000.0 + 1e-3 * rng.standard_normal(S)).astype(np.float32),
+        (1000.0 + 1e-3 * rng.standard_normal(S)).astype(np.float32),
+    ]
+    pats[2][rng.integers(0, S)] = 1e30
+    scores = np.stack(pats)
+    n_cand = np.array([S, S, S, S - 5], np.int32)
+    note("topk row select crowded bins S=%d k=%d" % (S, k))
+    got = _select(torch.from_numpy(scores), torch.from_numpy(n_cand), k)
+    np.testing.assert_array_equal(got, oracle.topk(scores, n_cand, k))
+
+
 def test_nan_ranks_below_numbers(oracle):
     S, k = 20000, 128
     rng = np.random.default_rng(4)
