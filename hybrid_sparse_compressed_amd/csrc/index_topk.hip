@@ -583,30 +583,108 @@ __global__ __launch_bounds__(kThreads) void score_gemm_kernel(
 }
 
 // ---- one workgroup per query, all keys in LDS ---------------------------------
+// The row histograms keep two 16-bit bin counts per LDS word (bin b in half
+// b & 1 of word b >> 1; a row has at most 12,288 keys, so no half carries
+// into the other): 4 KB instead of 8 for 2048 bins, which lets four
+// 8,192-key rows share a CU.
+__device__ __forceinline__ void hist16_add(uint32_t* hp, uint32_t b) {
+    atomicAdd(&hp[b >> 1], 1u << ((b & 1u) << 4));
+}
+
+// The bin d of packed counts hp[0..NB/2) such that (members in bins above d)
+// < need <= (members above d) + count(d).  Returns d; *rem = need minus the
+// members above d, *cnt = count(d), both read before the closing barrier so
+// the caller may reuse hp right away.  Every thread calls it.
+template <int NB>
+__device__ int row_crossing(const uint32_t* hp, int need, uint32_t* tmp, int* rem, int* cnt) {
+    constexpr int BPT = NB / kThreads;  // bins per thread
+    static_assert(BPT == 8 || BPT == 4, "one 16- or 8-byte LDS read of packed bins per thread");
+    __shared__ int res[3];
+    const int tid = threadIdx.x;
+    const int grp = kThreads - 1 - tid;  // thread 0 owns the top bins
+    if (tid == 0) {
+        res[0] = 0;
+        res[1] = 1;
+        res[2] = 0;
+    }
+    uint32_t c[BPT];
+    if constexpr (BPT == 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(hp + grp * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            c[2 * j] = v[j] & 0xffffu;
+            c[2 * j + 1] = v[j] >> 16;
+        }
+    } else {
+        const uint32_t v0 = hp[grp * 2], v1 = hp[grp * 2 + 1];
+        c[0] = v0 & 0xffffu;
+        c[1] = v0 >> 16;
+        c[2] = v1 & 0xffffu;
+        c[3] = v1 >> 16;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) sum += c[j];
+    uint32_t tot;
+    const uint32_t above = block_excl_scan<kThreads>(sum, tmp, &tot);
+    if (above < (uint32_t)need && (uint32_t)need <= above + sum) {
+        uint32_t cum = above;
+        bool found = false;
+#pragma unroll
+        for (int j = BPT - 1; j >= 0; --j) {
+            if (!found && cum + c[j] >= (uint32_t)need) {
+                res[0] = grp * BPT + j;
+                res[1] = need - (int)cum;
+                res[2] = (int)c[j];
+                found = true;
+            }
+            cum += c[j];
+        }
+    }
+    __syncthreads();
+    const int d = res[0];
+    *rem = res[1];
+    *cnt = res[2];
+    __syncthreads();
+    return d;
+}
+
 // Histogram of digit (key >> shift) & (NB-1) over the keys matching pref under
 // pmask, reading the LDS keys 16 bytes at a time; then the crossing bin.
 template <int NB>
 __device__ int row_digit(const uint32_t* keys, int n, uint32_t pmask, uint32_t pref, int shift,
-                         int need, uint32_t* h, uint32_t* tmp, int* rem) {
+                         int need, uint32_t* hp, uint32_t* tmp, int* rem) {
     const int tid = threadIdx.x;
-    for (int i = tid; i < NB; i += kThreads) h[i] = 0;
+    for (int i = tid; i < NB / 2; i += kThreads) hp[i] = 0;
     __syncthreads();
     const int n4 = n / 4;
     for (int i4 = tid; i4 < n4; i4 += kThreads) {
         const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + 4 * i4);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if ((kk[j] & pmask) == pref) atomicAdd(&h[(kk[j] >> shift) & (NB - 1)], 1u);
+            if ((kk[j] & pmask) == pref) hist16_add(hp, (kk[j] >> shift) & (NB - 1));
     }
     for (int i = 4 * n4 + tid; i < n; i += kThreads) {
         const uint32_t kk = keys[i];
-        if ((kk & pmask) == pref) atomicAdd(&h[(kk >> shift) & (NB - 1)], 1u);
+        if ((kk & pmask) == pref) hist16_add(hp, (kk >> shift) & (NB - 1));
     }
     __syncthreads();
-    return find_crossing<NB>(h, need, tmp, rem);
+    int cnt;
+    return row_crossing<NB>(hp, need, tmp, rem, &cnt);
 }
 
 constexpr int kRowListCap = 4096;  // short list of the row select (entries at or above bin d1)
+
+// Rows of at least 6,144 key words keep the short list's indices (kRowListCap
+// uint16) in key words [4096, 6144): the compacted list overwrites only words
+// below 4096, and every key is in registers before it is written.  Shorter
+// rows put them after the keys.
+__host__ __device__ constexpr bool row_lidx_in_keys(int S_max) {
+    return 4 * ((S_max + 3) / 4) >= kRowListCap + kRowListCap / 2;
+}
+__host__ __device__ constexpr size_t row_lds_bytes(int S_max) {
+    return (size_t)4 * (4 * ((S_max + 3) / 4)) + (row_lidx_in_keys(S_max) ? 0 : (size_t)kRowListCap * 2);
+}
 
 // Ordered compaction of the selected keys of list (lk, li?) of length n: the
 // first min(k, ...) under (key desc, index asc) given the k-th key T and the
@@ -652,11 +730,12 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
                                                             const int32_t* __restrict__ n_cand,
                                                             int32_t* __restrict__ out, int S_max,
                                                             int k) {
-    // dynamic LDS: the row's keys (S_max rounded up to 4), then the short
-    // list's indices (kRowListCap uint16)
+    // dynamic LDS: the row's keys (S_max rounded up to 4) and the short list's
+    // indices (kRowListCap uint16, inside the key words for long rows)
     extern __shared__ __align__(16) uint32_t keys[];
-    uint16_t* lidx = reinterpret_cast<uint16_t*>(keys + 4 * ceil_div(S_max, 4));
-    __shared__ uint32_t h[kBins];
+    uint16_t* lidx = reinterpret_cast<uint16_t*>(
+        keys + (row_lidx_in_keys(S_max) ? kRowListCap : 4 * ceil_div(S_max, 4)));
+    __shared__ __align__(16) uint32_t h[kBins / 2];  // packed 16-bit counts
     __shared__ uint32_t tmp[kNW + 2];
     const int q = blockIdx.x, tid = threadIdx.x;
     const int n = clamp_n(n_cand, q, S_max);
@@ -669,7 +748,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     // the row's scores -> keys in LDS (8 loads in flight per thread, 16-byte
     // loads when the row is 16-byte aligned) and the histogram of their top
     // 11 bits on the way
-    for (int i = tid; i < kBins; i += kThreads) h[i] = 0;
+    for (int i = tid; i < kBins / 2; i += kThreads) h[i] = 0;
     __syncthreads();
     const float* src = scores + (size_t)q * S_max;
     int i0 = 0;
@@ -694,7 +773,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
                                            score_key(v[j][3])};
                     *reinterpret_cast<u32x4*>(keys + 4 * i4) = kk;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) atomicAdd(&h[kk[e] >> 21], 1u);
+                    for (int e = 0; e < 4; ++e) hist16_add(h, kk[e] >> 21);
                 }
             }
         }
@@ -710,14 +789,14 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
             if (i < n) {
                 const uint32_t kk = score_key(v[j]);
                 keys[i] = kk;
-                atomicAdd(&h[kk >> 21], 1u);
+                hist16_add(h, kk >> 21);
             }
         }
     }
     __syncthreads();
-    int need = take, rem;
-    const int d1 = find_crossing<kBins>(h, need, tmp, &rem);
-    const int m = (take - rem) + (int)h[d1];  // entries with bin >= d1
+    int need = take, rem, hc;
+    const int d1 = row_crossing<kBins>(h, need, tmp, &rem, &hc);
+    const int m = (take - rem) + hc;  // entries with bin >= d1
     need = rem;
     const uint32_t lo1 = (uint32_t)d1 << 21;
     // short list: the entries at or above bin d1, compacted in index order in
@@ -1018,7 +1097,7 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     if (!multi) {
         // LDS for S_max keys (and the short list's indices) only, so that short
         // rows fit more workgroups per CU
-        const size_t lds = (size_t)ceil_div(S_max, 4) * 16 + (size_t)kRowListCap * 2;
+        const size_t lds = row_lds_bytes(S_max);
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)Nq), dim3(kThreads), lds, st, scores,
                            n_cand, topk_idx, S_max, k);
     } else {
