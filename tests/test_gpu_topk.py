@@ -43,8 +43,8 @@ def _plant_boundary_ties(oracle, s, n_cand, k, rng):
 
 @pytest.mark.parametrize(
     "Nq,S,k",
-    [(3, 1, 1), (4, 7, 3), (5, 64, 64), (6, 1000, 64), (4, 5000, 2048), (3, 12288, 512),
-     (3, 12289, 512), (4, 50000, 512), (2, 70000, 2048), (4, 262144, 512), (3, 300000, 1000)],
+    [(3, 1, 1), (4, 7, 3), (5, 64, 64), (6, 1000, 64), (4, 5000, 2048), (3, 6140, 2048),
+     (3, 6144, 2048), (3, 12288, 512), (3, 12289, 512), (4, 50000, 512), (2, 70000, 2048), (4, 262144, 512), (3, 300000, 1000)],
 )
 def test_select_bit_exact(oracle, Nq, S, k):
     from hybrid_sparse_compressed_amd import workloads
