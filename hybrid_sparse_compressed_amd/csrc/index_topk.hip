@@ -708,10 +708,12 @@ __device__ void row_write(const uint32_t* lk, const uint16_t* li, int n, uint32_
         gt += lk[s] > T;
         eq += lk[s] == T;
     }
-    uint32_t tot;
-    const uint32_t eq_base = block_excl_scan<kThreads>(eq, tmp, &tot);
+    // one paired scan: the equal keys taken before this thread's range are the
+    // first min(eq_base, need) of them (they are taken in index order)
+    uint32_t gt_base, eq_base, gt_tot, eq_tot;
+    block_excl_scan2<kThreads>(gt, eq, tmp, &gt_base, &eq_base, &gt_tot, &eq_tot);
     const int eq_take = max(0, min((int)eq, need - (int)eq_base));
-    const uint32_t pos0 = block_excl_scan<kThreads>(gt + (uint32_t)eq_take, tmp, &tot);
+    const uint32_t pos0 = gt_base + min(eq_base, (uint32_t)max(need, 0));
     if (gt + (uint32_t)eq_take == 0) return;
     int pos = (int)pos0, e = 0;
     for (s = s0; s < s1; ++s) {
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     uint16_t* lidx = reinterpret_cast<uint16_t*>(
         keys + (row_lidx_in_keys(S_max) ? kRowListCap : 4 * ceil_div(S_max, 4)));
     __shared__ __align__(16) uint32_t h[kBins / 2];  // packed 16-bit counts
-    __shared__ uint32_t tmp[kNW + 2];
+    __shared__ uint32_t tmp[2 * kNW + 2];
     const int q = blockIdx.x, tid = threadIdx.x;
     const int n = clamp_n(n_cand, q, S_max);
     const int take = min(k, n);
