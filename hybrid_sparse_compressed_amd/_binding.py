@@ -146,6 +146,22 @@ class Workspace:
             cls._cache[key] = buf
         return buf
 
+    @classmethod
+    def discard(cls, buf) -> None:
+        """Forget a cached buffer (after a failed call its contents are unknown, and
+        a zero-filled one is made on the next request)."""
+        for key, v in list(cls._cache.items()):
+            if v is buf:
+                del cls._cache[key]
+
+
+def _call_with_workspace(name, rc_fn, workspace, cached):
+    """Run one C call; if it fails and the workspace came from the cache, drop it."""
+    code = rc_fn()
+    if code != HSA_OK and cached:
+        Workspace.discard(workspace)
+    _check(name, code)
+
 
 def hsa_compress(x, gate, bias, m, out=None, stream=None):
     """out[b,i,:] = sum_j softmax_j(gate[b,m*i+j,:] + bias[j,:]) * x[b,m*i+j,:]."""
@@ -215,12 +231,14 @@ def hsa_index_topk(q_idx, k_idx, n_cand, k, q_seq=None, scores=None, topk_idx=No
         topk_idx = torch.empty((Nq, k), dtype=torch.int32, device=dev)
     st = torch.cuda.current_stream() if stream is None else stream
     need = lib.hsa_index_topk_workspace_size(Nq, S_max, k)
-    if workspace is None:
+    cached = workspace is None
+    if cached:
         workspace = Workspace.get("topk", need, dev, st)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("hsa_index_topk", lib.hsa_index_topk(
+    _call_with_workspace("hsa_index_topk", lambda: lib.hsa_index_topk(
         dt, _ptr(q_idx), _ptr(k_idx), B, _ptr(q_seq), _ptr(n_cand), _ptr(scores),
-        _ptr(topk_idx), Nq, H_I, d_I, S_max, k, 0, _ptr(workspace), wsz, _stream(st)))
+        _ptr(topk_idx), Nq, H_I, d_I, S_max, k, 0, _ptr(workspace), wsz, _stream(st)),
+        workspace, cached)
     return scores, topk_idx
 
 
@@ -277,16 +295,18 @@ def hsa_decode_sparse(q_idx, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     st = torch.cuda.current_stream() if stream is None else stream
     need = lib.hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k)
-    if workspace is None:
+    cached = workspace is None
+    if cached:
         # the select part sits at the front and must be zero-filled, so a
         # cached buffer serves one layout only
         workspace = Workspace.get("decode_sparse:%d:%d:%d:%d:%d" % (B, H, d_v, W, S_max * 4096 + k),
                                   need, dev, st)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("hsa_decode_sparse", lib.hsa_decode_sparse(
+    _call_with_workspace("hsa_decode_sparse", lambda: lib.hsa_decode_sparse(
         _dt(q), _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
         _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
-        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)))
+        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)),
+        workspace, cached)
     return scores, topk_idx, out, lse
 
 
@@ -324,15 +344,17 @@ def hsa_decode_step(x_tok, g_tok, bias, ring_x, ring_g, pos, q_idx, k_idx, n_can
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     st = torch.cuda.current_stream() if stream is None else stream
     need = lib.hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k)
-    if workspace is None:
+    cached = workspace is None
+    if cached:
         workspace = Workspace.get("decode_sparse:%d:%d:%d:%d:%d" % (B, H, d_v, W, S_max * 4096 + k),
                                   need, dev, st)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("hsa_decode_step", lib.hsa_decode_step(
+    _call_with_workspace("hsa_decode_step", lambda: lib.hsa_decode_step(
         _dt(q), _ptr(x_tok), _ptr(g_tok), _ptr(bias), _ptr(ring_x), _ptr(ring_g), _ptr(pos),
         _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
         _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
-        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)))
+        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)),
+        workspace, cached)
     return scores, topk_idx, out, lse
 
 

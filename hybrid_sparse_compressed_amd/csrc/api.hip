@@ -180,9 +180,13 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
         hipError_t e = hsa::launch_index_lists(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
                                                d_I, S_max, k, ws_sel, job, st);
         if (e != hipSuccess) return finish(e);
-        return finish(hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len,
-                                                    n_cand, ws_sel, scores, topk_idx, out, lse, B,
-                                                    H, d_qk, d_v, W, S_max, k, scale, ws_attn, st));
+        e = hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len, n_cand,
+                                          ws_sel, scores, topk_idx, out, lse, B, H, d_qk, d_v, W,
+                                          S_max, k, scale, ws_attn, st);
+        // the scoring launch counted into the histograms that the merge would have
+        // cleared: leave the workspace ready for the next call all the same
+        if (e != hipSuccess) hsa::launch_clear_select_hist(ws_sel, B, S_max, k, st);
+        return finish(e);
     }
     if (job) {
         hipError_t e = hsa::launch_compress_append(dtype, job->x_tok, job->g_tok, job->bias,

@@ -375,12 +375,13 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
 // top-11-bit histogram of given scores (select-only mode, multi-workgroup path)
 __global__ __launch_bounds__(kThreads) void hist_kernel(const float* __restrict__ scores,
                                                         const int32_t* __restrict__ n_cand,
+                                                        const int32_t* __restrict__ q_seq, int B,
                                                         uint8_t* __restrict__ ws, int S_max, int k,
                                                         int chunk) {
     __shared__ uint32_t hist[kBins];
     const int q = blockIdx.y, tid = threadIdx.x;
     clear_hist2_slice(ws, q, S_max, k);
-    const int n = clamp_n(n_cand, q, S_max);
+    const int n = query_n(n_cand, q_seq, B, q, S_max);
     const int s0 = blockIdx.x * chunk, s1 = min(n, s0 + chunk);
     if (s0 >= s1) return;
     for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
@@ -730,8 +731,9 @@ __device__ void row_write(const uint32_t* lk, const uint16_t* li, int n, uint32_
 
 __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restrict__ scores,
                                                             const int32_t* __restrict__ n_cand,
-                                                            int32_t* __restrict__ out, int S_max,
-                                                            int k) {
+                                                            const int32_t* __restrict__ q_seq,
+                                                            int B, int32_t* __restrict__ out,
+                                                            int S_max, int k) {
     // dynamic LDS: the row's keys (S_max rounded up to 4) and the short list's
     // indices (kRowListCap uint16, inside the key words for long rows)
     extern __shared__ __align__(16) uint32_t keys[];
@@ -740,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(const float* __restr
     __shared__ __align__(16) uint32_t h[kBins / 2];  // packed 16-bit counts
     __shared__ uint32_t tmp[2 * kNW + 2];
     const int q = blockIdx.x, tid = threadIdx.x;
-    const int n = clamp_n(n_cand, q, S_max);
+    const int n = query_n(n_cand, q_seq, B, q, S_max);
     const int take = min(k, n);
     int32_t* o = out + (size_t)q * k;
     if (take == n) {  // every candidate is selected
@@ -885,15 +887,16 @@ static_assert(kPerThread == 16, "per-thread masks and counts are 16 bits wide");
 // its selected indices right after it, and its two counts to seg[g].
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __restrict__ scores,
                                                                const int32_t* __restrict__ n_cand,
-                                                               uint8_t* __restrict__ ws, int S_max,
-                                                               int k) {
+                                                               const int32_t* __restrict__ q_seq,
+                                                               int B, uint8_t* __restrict__ ws,
+                                                               int S_max, int k) {
     __shared__ __align__(16) uint32_t h[kBins];
     __shared__ uint32_t tmp[kNW + 2];
     static_assert(kBins == 8 * kThreads, "two 16-byte histogram loads per thread");
 
     const int q = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
-    const int n = clamp_n(n_cand, q, S_max);
+    const int n = query_n(n_cand, q_seq, B, q, S_max);
     const int take = min(k, n);
     const int s0 = g * kFilterChunk;
     if (s0 >= n) {  // uniform: nothing here; the count is written every call
@@ -968,7 +971,8 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const float* __re
 // the two ascending lists into the output, and the zeroing of the query's
 // workspace.
 __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __restrict__ n_cand,
-                                                              int32_t* __restrict__ out,
+                                                              const int32_t* __restrict__ q_seq,
+                                                              int B, int32_t* __restrict__ out,
                                                               uint8_t* __restrict__ ws, int S_max,
                                                               int k) {
     __shared__ uint32_t h[kBins];
@@ -983,7 +987,7 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
     const int q = blockIdx.x;
     QWs W = ws_of(ws, q, S_max, k);
     const SelLds L = {h, tmp, segc, sbase, lbase, ck, ci, selv, chs, misc, mem, flag, nullptr};
-    const SelResult R = select_query(W, clamp_n(n_cand, q, S_max), S_max, k, k, L);
+    const SelResult R = select_query(W, query_n(n_cand, q_seq, B, q, S_max), S_max, k, k, L);
     select_write_sorted(L, R, out + (size_t)q * k, k);
     __syncthreads();
     select_zero<kThreads>(W, S_max, segc, tmp);
@@ -1037,7 +1041,21 @@ hipError_t launch_score_t(int d_I, const void* q_idx, const void* k_idx, int B,
     return launch_score<T, 32>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st);
 }
 
+// Zero the first-digit histogram of every query (a scoring launch whose select
+// never ran leaves it counted).
+__global__ __launch_bounds__(kThreads) void clear_hist_kernel(uint8_t* __restrict__ ws, int S_max,
+                                                              int k) {
+    uint32_t* h = ws_of(ws, (int)blockIdx.x, S_max, k).hist;
+    for (int i = (int)threadIdx.x; i < kBins; i += kThreads) h[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_clear_select_hist(void* ws, int Nq, int S_max, int k, hipStream_t st) {
+    hipLaunchKernelGGL(clear_hist_kernel, dim3((unsigned)Nq), dim3(kThreads), 0, st,
+                       static_cast<uint8_t*>(ws), S_max, k);
+    return hipGetLastError();
+}
 
 size_t topk_workspace_bytes(int Nq, int S_max, int k) {
     if (S_max <= kRowSelectCap) return 0;
@@ -1066,6 +1084,9 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     const bool multi = S_max > kRowSelectCap;
     uint8_t* w = static_cast<uint8_t*>(ws);
     hipError_t e = hipSuccess;
+    // the select treats a query routed outside [0, B) as one without candidates
+    // (select-only mode has no key sequences: q_seq is ignored there)
+    const int32_t* sel_seq = q_idx ? q_seq : nullptr;
     if (q_idx && !multi && dtype == kBF16 && Nq >= kGemmMinQueries &&
         (d_I == 64 || d_I == 128 || d_I == 256)) {
         ProfScope prof(kProfScore, st);
@@ -1091,8 +1112,8 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     } else if (multi) {
         dim3 grid((unsigned)ceil_div(S_max, kFilterChunk), (unsigned)Nq);
         ProfScope prof(kProfSelect, st);
-        hipLaunchKernelGGL(hist_kernel, grid, dim3(kThreads), 0, st, scores, n_cand, w, S_max, k,
-                           kFilterChunk);
+        hipLaunchKernelGGL(hist_kernel, grid, dim3(kThreads), 0, st, scores, n_cand, sel_seq, B, w,
+                           S_max, k, kFilterChunk);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     ProfScope prof(kProfSelect, st);
@@ -1101,14 +1122,14 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
         // rows fit more workgroups per CU
         const size_t lds = row_lds_bytes(S_max);
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)Nq), dim3(kThreads), lds, st, scores,
-                           n_cand, topk_idx, S_max, k);
+                           n_cand, sel_seq, B, topk_idx, S_max, k);
     } else {
         const int G = ceil_div(S_max, kFilterChunk);
         hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)G, (unsigned)Nq), dim3(kThreads), 0,
-                           st, scores, n_cand, w, S_max, k);
+                           st, scores, n_cand, sel_seq, B, w, S_max, k);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)Nq), dim3(kThreads), 0, st, n_cand,
-                           topk_idx, w, S_max, k);
+                           sel_seq, B, topk_idx, w, S_max, k);
     }
     return hipGetLastError();
 }

@@ -70,6 +70,16 @@ __device__ inline int clamp_n(const int32_t* n_cand, int q, int S_max) {
     return n < 0 ? 0 : (n > S_max ? S_max : n);
 }
 
+// Candidates of query q: n_cand[q] clamped to [0, S_max], or none when q_seq
+// (may be null) sends the query to a sequence outside [0, B).
+__device__ inline int query_n(const int32_t* n_cand, const int32_t* q_seq, int B, int q, int S_max) {
+    if (q_seq) {
+        const int b = q_seq[q];
+        if (b < 0 || b >= B) return 0;
+    }
+    return clamp_n(n_cand, q, S_max);
+}
+
 // ---- LDS radix machinery -------------------------------------------------------
 // Given bin counts h[0..NB), find the bin d such that (members in bins above d)
 // < need <= (members in bins above d) + h[d].  Returns d; *rem = need minus the
@@ -779,6 +789,9 @@ __device__ inline SelResult select_query_lists(const QWs& W, const float* srow, 
             if (small) {
                 if (pc < (uint32_t)kCandCap) { L.ck[pc] = kk; L.ci[pc] = ii; }
             } else if (pc < (uint32_t)S_max) {
+                // a short list too long for LDS goes to the query's flat area;
+                // every workgroup of the sequence computes the same list, so
+                // their concurrent writes to these words store identical values
                 W.flat_key[pc] = kk;
                 W.flat_idx[pc] = ii;
             }

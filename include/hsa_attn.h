@@ -34,6 +34,15 @@
  *  - Identical inputs give bitwise-identical outputs (no floating-point
  *    atomics; every reduction has a fixed order).
  *  - Re-entrant; calls that share one workspace must not overlap in time.
+ *
+ * Interface notes: every entry point returns an int holding an
+ * hsa_status_code (the ABI does not depend on the size of an enum type);
+ * the status-string call is hsa_strerror because the ROCm runtime already
+ * exports a symbol named hsa_status_string; hsa_index_topk takes B, the
+ * number of key sequences, so that q_seq can be checked against it;
+ * hsa_attn_prefill takes the block length m, which sets when a compressed
+ * row becomes visible; prefill attention needs no scratch memory, so its
+ * workspace size is 0.
  */
 #ifndef HSA_ATTN_H
 #define HSA_ATTN_H
@@ -143,7 +152,9 @@ int hsa_compress_append(int dtype, const void *x_tok, const void *g_tok, const v
  *              `scores` is an INPUT holding fp32 scores)
  *   k_idx    : [B, S_max, d_I] dtype (ignored in select-only mode, may be NULL)
  *   q_seq    : [Nq] int32 sequence of each query in [0, B), or NULL (query q
- *              reads sequence q; then Nq <= B)
+ *              reads sequence q; then Nq <= B).  A query whose entry lies
+ *              outside [0, B) has no candidates: its scores are not written
+ *              and its topk_idx row is all -1.  Ignored in select-only mode.
  *   n_cand   : [Nq] int32 candidate count per query, clamped to [0, S_max]
  *   scores   : [Nq, S_max] fp32, output (score mode) or input (select-only)
  *   topk_idx : [Nq, k] int32 output
@@ -235,7 +246,11 @@ int hsa_attn_decode(int dtype, const void *q, const void *swa_kv, const int32_t 
  *              completes leaves it ready for the next call with the same
  *              (B, H, d_v, W, S_max, k) (its histograms zero; other words it
  *              holds are rewritten before they are read), so a buffer reused
- *              with other sizes must be zero-filled again first.
+ *              with other sizes must be zero-filled again first.  A call that
+ *              returns HSA_ERR_HIP after its scoring launch still enqueues the
+ *              clearing of the histograms; a caller that cannot tell whether
+ *              the queued work ran (e.g. after a device error) zero-fills the
+ *              buffer again before reusing it.
  */
 size_t hsa_decode_sparse_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t W,
                                         int32_t S_max, int32_t k);

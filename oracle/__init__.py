@@ -20,18 +20,30 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# the same source built with AddressSanitizer and UndefinedBehaviorSanitizer; a
+# process that sets ORACLE_SANITIZED=1 (and preloads the two runtimes) loads it
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+if os.environ.get("ORACLE_SANITIZED") == "1":
+    _LIB = _LIB_SAN
 
 OR_F64, OR_F32, OR_BF16 = 0, 1, 2
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so next to it (gcc, -O2, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+def build(force: bool = True, sanitized: bool = False) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, -O2, OpenMP), or with
+    sanitized=True into liboracle_san.so with -fsanitize=address,undefined (every
+    report fatal)."""
+    lib = _LIB_SAN if sanitized else _LIB
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp%d" % os.getpid()
+        flags = ["-O2"]
+        if sanitized:
+            flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                     "-fno-sanitize-recover=all"]
+        cmd = ["gcc", *flags, "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 _lib = None

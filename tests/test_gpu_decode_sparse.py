@@ -52,7 +52,7 @@ def _check_against_separate(hsa, w, k, label):
     # the same workspace again gives the same results
     s3, i3, o3, l3 = _fused(hsa, w, k, workspace=ws)
     assert torch.equal(i2, i3) and torch.equal(o2, o3) and torch.equal(l2, l3), label + ": not repeatable"
-    return i2, o2, l2
+    return i2, o2, l2, s2
 
 
 def _small_case(seed, B, S, H=64, W=128, k=512, dup=False, equal_keys=False):
@@ -84,11 +84,14 @@ def test_full_size_against_separate_and_oracle(oracle, name):
     w = workloads.c4_decode(name, "cuda")
     k = w["cfg"]["k"]
     note("decode_sparse %s" % name)
-    idx, o, lse = _check_against_separate(hsa, w, k, name)
+    idx, o, lse, scores = _check_against_separate(hsa, w, k, name)
     nc = w["n_cand"].cpu().numpy()
+    got = idx.cpu().numpy()
+    # the fused select is bit-exact against the oracle's select on the GPU's own scores
+    np.testing.assert_array_equal(got, oracle.topk(scores.cpu().numpy(), nc, k),
+                                  err_msg=name + ": fused top-k vs oracle select on the same scores")
     rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
     ridx = oracle.topk(rs.astype(np.float32), nc, k)
-    got = idx.cpu().numpy()
     inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(got, ridx))
     assert inter / int((ridx >= 0).sum()) >= 0.999
     ro, rl = oracle.attn_decode(w["q"].cpu(), w["swa_kv"].cpu(), w["swa_len"].cpu().numpy(),
@@ -109,8 +112,9 @@ def test_ragged_lengths_and_ties(oracle):
     w["swa_len"] = torch.tensor([0, 5, 128, 128, 77], dtype=torch.int32, device="cuda")
     w["comp_len"] = torch.tensor([0, S, S, S - 1000, S], dtype=torch.int32, device="cuda")
     note("decode_sparse ragged")
-    idx, o, lse = _check_against_separate(hsa, w, k, "ragged")
+    idx, o, lse, scores = _check_against_separate(hsa, w, k, "ragged")
     nc = w["n_cand"].cpu().numpy()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(scores.cpu().numpy(), nc, k))
     rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
     ridx = oracle.topk(rs.astype(np.float32), nc, k)
     ro, rl = oracle.attn_decode(w["q"].cpu(), w["swa_kv"].cpu(), w["swa_len"].cpu().numpy(),
@@ -133,7 +137,7 @@ def test_all_candidates_tie():
     w["swa_len"] = torch.tensor([128, 64], dtype=torch.int32, device="cuda")
     w["comp_len"] = torch.tensor([S, S], dtype=torch.int32, device="cuda")
     note("decode_sparse all tie")
-    idx, _, _ = _check_against_separate(hsa, w, k, "all-tie")
+    idx, _, _, _ = _check_against_separate(hsa, w, k, "all-tie")
     np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (B, 1)))
 
 
@@ -154,8 +158,9 @@ def test_concentrated_top_rows_read_their_slot_from_the_score_row(oracle):
     w["swa_len"] = torch.tensor([128, 128], dtype=torch.int32, device="cuda")
     w["comp_len"] = torch.tensor([S, S], dtype=torch.int32, device="cuda")
     note("decode_sparse concentrated top rows")
-    idx, o, lse = _check_against_separate(hsa, w, k, "concentrated")
+    idx, o, lse, scores = _check_against_separate(hsa, w, k, "concentrated")
     nc = w["n_cand"].cpu().numpy()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(scores.cpu().numpy(), nc, k))
     rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
     ridx = oracle.topk(rs.astype(np.float32), nc, k)
     inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(idx.cpu().numpy(), ridx))
@@ -199,8 +204,9 @@ def test_fused_lists_fp32_and_large_k(oracle):
     w["swa_len"] = torch.tensor([128, 77], dtype=torch.int32, device="cuda")
     w["comp_len"] = torch.tensor([S, S], dtype=torch.int32, device="cuda")
     note("decode_sparse k=2048 lists")
-    idx, o, lse = _check_against_separate(hsa, w, k, "k2048")
+    idx, o, lse, scores = _check_against_separate(hsa, w, k, "k2048")
     nc = w["n_cand"].cpu().numpy()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(scores.cpu().numpy(), nc, k))
     rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
     ridx = oracle.topk(rs.astype(np.float32), nc, k)
     inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(idx.cpu().numpy(), ridx))
@@ -226,7 +232,7 @@ def test_every_slot_short_selects_from_the_score_row():
     w["swa_len"] = torch.tensor([128], dtype=torch.int32, device="cuda")
     w["comp_len"] = torch.tensor([S], dtype=torch.int32, device="cuda")
     note("decode_sparse every slot short")
-    idx, _, _ = _check_against_separate(hsa, w, k, "every-slot-short")
+    idx, _, _, _ = _check_against_separate(hsa, w, k, "every-slot-short")
     np.testing.assert_array_equal(idx.cpu().numpy(), np.arange(k, dtype=np.int32)[None, :])
 
 
@@ -243,7 +249,7 @@ def test_fused_lists_small_k(oracle, k):
     w["swa_len"] = torch.tensor([128, 9, 128], dtype=torch.int32, device="cuda")
     w["comp_len"] = torch.tensor([S, S, S], dtype=torch.int32, device="cuda")
     note("decode_sparse small k=%d" % k)
-    idx, _, _ = _check_against_separate(hsa, w, k, "k%d" % k)
+    idx, _, _, _ = _check_against_separate(hsa, w, k, "k%d" % k)
     nc = w["n_cand"].cpu().numpy()
     rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
     ridx = oracle.topk(rs.astype(np.float32), nc, k)

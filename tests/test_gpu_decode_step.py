@@ -47,7 +47,7 @@ def _step(hsa, d, k, pos, n_cand, swa_len, comp_len):
                                d["comp_kv"], comp_len, d["scale"], 512)
 
 
-@pytest.mark.parametrize("S,k", [(16384, 512), (4096, 256)])  # fused filter path / separate path
+@pytest.mark.parametrize("S,k", [(16384, 512), (4096, 256)])  # fused lists path / separate path
 def test_decode_step_against_oracle_and_separate(oracle, S, k):
     import hybrid_sparse_compressed_amd as hsa
 
@@ -196,3 +196,92 @@ def test_decode_step_replays_from_a_hip_graph(S, k):
             assert torch.equal(a, b), "replay %d: %s differs from the eager call" % (rep, name)
         for b, nb in enumerate(n_cand.tolist()):
             assert torch.equal(og[0][b, :nb], oe[0][b, :nb]), "replay %d: scores" % rep
+
+
+def test_decode_step_at_the_1m_workload(oracle):
+    """The call the bench times: hsa_decode_step at c4_decode_1m (4 sequences x
+    262,144 C4 entries: 2048-row list slots, the append as extra workgroups of the
+    scoring launch).  Sequence 0's token completes the block of a pool row the
+    oracle selects, so the attention must read the new entry; sequence 1 completes
+    a block near the pool's end, 2 leaves its block open, 3 is idle.  Checks: the
+    two separate calls bit for bit, rings bit for bit and new entries against the
+    oracle's append, top-k bit-exact against the oracle's select on the GPU's own
+    fp32 scores, overlap with the oracle's fp64 chain, and out / lse against the
+    oracle's attention over the updated pool."""
+    import hybrid_sparse_compressed_amd as hsa
+    from hybrid_sparse_compressed_amd import workloads
+
+    w = workloads.c4_decode("c4_decode_1m", "cuda")
+    B, S, k = w["cfg"]["B"], w["S"], w["cfg"]["k"]
+    D = w["cfg"]["d_qk"]
+    nc = w["n_cand"].cpu().numpy()
+    note("decode_step 1m: oracle scores")
+    rs = oracle.index_scores(w["q_idx"].cpu(), w["k_idx"].cpu(), nc)
+    ridx = oracle.topk(rs.astype(np.float32), nc, k)
+    r_sel = int(ridx[0][k // 2])  # a row the oracle selects for sequence 0
+    g = torch.Generator().manual_seed(404)
+    bf = torch.bfloat16
+    app = dict(x_tok=torch.randn(B, D, generator=g).to(bf), g_tok=torch.randn(B, D, generator=g).to(bf),
+               bias=(torch.randn(4, D, generator=g) * 0.1).to(bf),
+               ring_x=torch.randn(B, 4, D, generator=g).to(bf),
+               ring_g=torch.randn(B, 4, D, generator=g).to(bf))
+    pos = torch.tensor([4 * r_sel + 3, 4 * (S - 3) + 3, 4 * 5000 + 2, -1], dtype=torch.int32)
+    comp0 = w["comp_kv"].clone()
+    d1 = {kk: v.cuda() for kk, v in app.items()}
+    d2 = {kk: v.cuda() for kk, v in app.items()}
+    pd = pos.cuda()
+    note("decode_step 1m: fused step")
+    s1, i1, o1, l1 = hsa.hsa_decode_step(d1["x_tok"], d1["g_tok"], d1["bias"], d1["ring_x"],
+                                         d1["ring_g"], pd, w["q_idx"], w["k_idx"], w["n_cand"], k,
+                                         w["q"], w["swa_kv"], w["swa_len"], w["comp_kv"],
+                                         w["comp_len"], w["scale"], 512)
+    torch.cuda.synchronize()
+    pool1 = w["comp_kv"].clone()
+    w["comp_kv"].copy_(comp0)
+    note("decode_step 1m: separate calls")
+    hsa.hsa_compress_append(d2["x_tok"], d2["g_tok"], d2["bias"], d2["ring_x"], d2["ring_g"], pd,
+                            w["comp_kv"])
+    s2, i2, o2, l2 = hsa.hsa_decode_sparse(w["q_idx"], w["k_idx"], w["n_cand"], k, w["q"],
+                                           w["swa_kv"], w["swa_len"], w["comp_kv"], w["comp_len"],
+                                           w["scale"], 512)
+    torch.cuda.synchronize()
+    for name, a, b in (("ring_x", d1["ring_x"], d2["ring_x"]), ("ring_g", d1["ring_g"], d2["ring_g"]),
+                       ("pool", pool1, w["comp_kv"]), ("scores", s1, s2), ("topk", i1, i2),
+                       ("out", o1, o2), ("lse", l1, l2)):
+        assert torch.equal(a, b), "decode_step differs from the two separate calls: " + name
+
+    # top-k: bit-exact against the oracle's select on the GPU's own scores
+    got = i1.cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.topk(s1.cpu().numpy(), nc, k))
+    assert r_sel in set(got[0].tolist())
+    inter = sum(len(set(a[a >= 0].tolist()) & set(b[b >= 0].tolist())) for a, b in zip(got, ridx))
+    ov = inter / int((ridx >= 0).sum())
+    print("selected-set overlap %.6f" % ov)
+    assert ov >= 0.999
+
+    # the append: rings, new entries, untouched rows
+    rx, rg = app["ring_x"].clone(), app["ring_g"].clone()
+    new = np.zeros((B, S, D))
+    wrote = oracle.compress_append(app["x_tok"], app["g_tok"], app["bias"], rx, rg, pos.numpy(),
+                                   new, 4)
+    assert wrote == [(0, r_sel), (1, S - 3)]
+    assert torch.equal(d1["ring_x"].cpu().view(torch.int16), rx.view(torch.int16))
+    assert torch.equal(d1["ring_g"].cpu().view(torch.int16), rg.view(torch.int16))
+    comp = comp0.cpu()
+    for b, r in wrote:
+        compare(pool1[b, r].cpu(), new[b, r], TOL_BF16, "new entry %d" % b)
+        comp[b, r] = round_bf16(new[b, r])
+    changed = (pool1 != comp0).any(dim=2).nonzero().cpu().tolist()
+    assert all(tuple(x) in set(wrote) for x in changed)
+
+    ro, rl = oracle.attn_decode(w["q"].cpu(), w["swa_kv"].cpu(), w["swa_len"].cpu().numpy(), comp,
+                                w["comp_len"].cpu().numpy(), w["scale"], 512, comp_idx=got)
+    print(compare(o1, ro, TOL_BF16, "decode_step 1m out vs oracle"))
+    print(compare(l1, rl, TOL_BF16, "decode_step 1m lse vs oracle"))
+    # sequence 0 attended the new entry, not the row it replaced
+    ro_old, _ = oracle.attn_decode(w["q"][:1].cpu(), w["swa_kv"][:1].cpu(),
+                                   w["swa_len"][:1].cpu().numpy(), comp0[:1].cpu(),
+                                   w["comp_len"][:1].cpu().numpy(), w["scale"], 512, comp_idx=got[:1])
+    d_new = np.abs(o1[0].float().cpu().numpy() - ro[0]).max()
+    d_old = np.abs(o1[0].float().cpu().numpy() - ro_old[0]).max()
+    assert d_new < d_old, (d_new, d_old)

@@ -204,3 +204,31 @@ def test_prefill_32k_indexer_sampled(oracle):
     ov = _overlap(idx[sel].cpu().numpy(), want)
     print("score error / bound (worst) = %.3g, overlap = %.6f" % (worst, ov))
     assert ov >= 0.999
+
+
+@pytest.mark.parametrize("S_max,Nq", [(3000, 12), (20000, 12), (2048, 100)])
+def test_query_routed_outside_the_batch_has_no_candidates(oracle, S_max, Nq):
+    """A q_seq entry outside [0, B) (here -1 and B) gives that query no candidates:
+    its top-k row is all -1 on every select path (one workgroup per row, the
+    multi-workgroup select, and the matrix-product scoring with 100 queries), and
+    the other queries are unaffected (exact against the oracle's select on the
+    GPU's own scores)."""
+    import hybrid_sparse_compressed_amd as hsa
+
+    g = torch.Generator().manual_seed(S_max + Nq)
+    B, H_I, d_I, k = 3, 64, 128, 64
+    q_idx = torch.randn(Nq, H_I, d_I, generator=g).to(torch.bfloat16)
+    k_idx = torch.randn(B, S_max, d_I, generator=g).to(torch.bfloat16)
+    q_seq = torch.randint(0, B, (Nq,), generator=g, dtype=torch.int32)
+    q_seq[1], q_seq[5] = -1, B
+    n_cand = torch.full((Nq,), S_max, dtype=torch.int32)
+    note("index bad q_seq S_max=%d Nq=%d" % (S_max, Nq))
+    s, idx = hsa.hsa_index_topk(q_idx.cuda(), k_idx.cuda(), n_cand, k, q_seq=q_seq)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert (got[1] == -1).all() and (got[5] == -1).all()
+    ok = [i for i in range(Nq) if i not in (1, 5)]
+    nc = n_cand.numpy()[ok]
+    np.testing.assert_array_equal(got[ok], oracle.topk(s.cpu().numpy()[ok], nc, k))
+    ref = oracle.index_scores(q_idx[ok], k_idx, nc, q_seq=q_seq.numpy()[ok])
+    _check_scores(s[ok], ref, q_idx[ok], k_idx, q_seq.numpy()[ok], nc)
