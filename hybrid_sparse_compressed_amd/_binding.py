@@ -24,7 +24,8 @@ EXPORTED = (
     "hsa_index_topk_workspace_size",
     "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
     "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
-    "hsa_decode_sparse", "hsa_decode_step", "hsa_profile_enable", "hsa_profile_read",
+    "hsa_decode_sparse", "hsa_decode_step", "hsa_decode_step_noalloc", "hsa_profile_enable",
+    "hsa_profile_read",
 )
 HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
 
@@ -67,6 +68,8 @@ def _load():
     lib.hsa_decode_sparse.restype = I
     lib.hsa_decode_step.argtypes = [I] + [P] * 18 + [I32] * 9 + [F, P, SZ, P]
     lib.hsa_decode_step.restype = I
+    lib.hsa_decode_step_noalloc.argtypes = [I] + [P] * 18 + [I32] * 9 + [F, P]
+    lib.hsa_decode_step_noalloc.restype = I
     lib.hsa_attn_prefill_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.hsa_attn_prefill_workspace_size.restype = SZ
     lib.hsa_attn_prefill.argtypes = [I, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
@@ -355,6 +358,43 @@ def hsa_decode_step(x_tok, g_tok, bias, ring_x, ring_g, pos, q_idx, k_idx, n_can
         _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
         d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)),
         workspace, cached)
+    return scores, topk_idx, out, lse
+
+
+def hsa_decode_step_noalloc(x_tok, g_tok, bias, ring_x, ring_g, pos, q_idx, k_idx, n_cand, k, q,
+                            swa_kv, swa_len, comp_kv, comp_len, scale, d_v, scores, topk_idx,
+                            out, lse, stream=None):
+    """hsa_decode_step without a workspace (the library's own fixed scratch): for
+    callers that cannot allocate, so every output is passed in.  Arguments and
+    results as hsa_decode_step; n_cand, swa_len and comp_len must be int32 device
+    tensors already."""
+    B, H_I, d_I = q_idx.shape
+    _, S_max, _ = k_idx.shape
+    _, H, d_qk = q.shape
+    W = swa_kv.shape[1]
+    for name, t, shape, dt in (("scores", scores, (B, S_max), torch.float32),
+                               ("topk_idx", topk_idx, (B, k), torch.int32),
+                               ("out", out, (B, H, d_v), q.dtype), ("lse", lse, (B, H), torch.float32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("hsa_decode_step_noalloc: %s must be a contiguous %s %s" % (name, dt, shape))
+    for name, t in (("pos", pos), ("n_cand", n_cand), ("swa_len", swa_len), ("comp_len", comp_len)):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,) or t.device != q.device:
+            raise TypeError("hsa_decode_step_noalloc: %s must be int32 [B] on the query's device" % name)
+    if comp_kv.shape[1] != S_max or k_idx.dtype != q_idx.dtype or q.dtype != q_idx.dtype:
+        raise ValueError("hsa_decode_step_noalloc: shape or dtype mismatch")
+    for t in (x_tok, g_tok, bias, ring_x, ring_g, comp_kv):
+        if t.dtype != q.dtype:
+            raise TypeError("hsa_decode_step_noalloc: append tensors must have the query dtype")
+    if (tuple(x_tok.shape) != (B, d_qk) or tuple(g_tok.shape) != (B, d_qk)
+            or tuple(bias.shape) != (4, d_qk) or tuple(ring_x.shape) != (B, 4, d_qk)
+            or tuple(ring_g.shape) != (B, 4, d_qk)):
+        raise ValueError("hsa_decode_step_noalloc: append shape mismatch")
+    st = torch.cuda.current_stream() if stream is None else stream
+    _check("hsa_decode_step_noalloc", lib.hsa_decode_step_noalloc(
+        _dt(q), _ptr(x_tok), _ptr(g_tok), _ptr(bias), _ptr(ring_x), _ptr(ring_g), _ptr(pos),
+        _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
+        _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
+        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _stream(st)))
     return scores, topk_idx, out, lse
 
 

@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -144,14 +146,16 @@ size_t hsa_decode_sparse_workspace_size(int32_t B, int32_t H, int32_t d_v, int32
 namespace {
 
 // hsa_decode_sparse, preceded by the decode-time C4 append of `job` when it is
-// not null (its arguments already checked)
+// not null (its arguments already checked).  clear_ws: the workspace holds
+// unknown contents, so the words the chosen path needs at zero are cleared
+// first (by fill kernels on the stream, after every argument check).
 int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const int32_t* n_cand,
                        float* scores, int32_t* topk_idx, const void* q, const void* swa_kv,
                        const int32_t* swa_len, const void* comp_kv, const int32_t* comp_len,
                        void* out, float* lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
                        int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
                        float scale, void* workspace, size_t workspace_bytes, void* stream,
-                       const hsa::AppendJob* job) {
+                       const hsa::AppendJob* job, bool clear_ws = false) {
     // indexer + select arguments (as hsa_index_topk with Nq = B, no q_seq)
     if (!dtype_ok(dtype) || !q_idx || !k_idx || !n_cand || !scores || !topk_idx)
         return HSA_ERR_INVALID_ARG;
@@ -173,8 +177,20 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
     hipStream_t st = as_stream(stream);
     uint8_t* ws_sel = static_cast<uint8_t*>(workspace);
     uint8_t* ws_attn = ws_sel + round256(hsa::topk_workspace_bytes(B, S_max, k));
-    if (S_max > hsa::kRowSelectCap && hsa::index_lists_apply(S_max, k, B) &&
-        hsa::fused_decode_supported(B, H, W, k)) {
+    const bool fused = S_max > hsa::kRowSelectCap && hsa::index_lists_apply(S_max, k, B) &&
+                       hsa::fused_decode_supported(B, H, W, k);
+    if (clear_ws) {
+        // fused: only the first-digit histograms must start at zero (every other
+        // word is written before it is read); the separate multi-workgroup
+        // select needs its whole workspace zero; the LDS row select needs none
+        hipError_t e = hipSuccess;
+        if (fused)
+            e = hsa::launch_clear_select_hist(ws_sel, B, S_max, k, st);
+        else
+            e = hsa::launch_zero_words(ws_sel, hsa::topk_workspace_bytes(B, S_max, k) / 4, st);
+        if (e != hipSuccess) return finish(e);
+    }
+    if (fused) {
         // the append rides in the scoring launch, which ends before the attention
         // reads the pool; scoring never reads it
         hipError_t e = hsa::launch_index_lists(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
@@ -241,6 +257,85 @@ int hsa_decode_step(int dtype, const void* x_tok, const void* g_tok, const void*
         return decode_sparse_impl(dtype, q_idx, k_idx, n_cand, scores, topk_idx, q, swa_kv,
                                   swa_len, comp_kv, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
                                   W, S_max, k, scale, workspace, workspace_bytes, stream, &job);
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of hsa_decode_step_noalloc: device memory of the library itself, one
+// copy per GPU, held until the process ends.  In host code this name is only a
+// stand-in: the kernels get the per-device address that hipGetSymbolAddress
+// returns (scratch_addr below), never the name itself.
+static __device__ __align__(256) uint8_t scratch[HSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxScratchDevices];
+
+// The device address of `scratch` on device `dev`, looked up on the first call
+// for that device with that device current, then kept.
+hipError_t scratch_addr(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hsa_decode_step_noalloc(int dtype, const void* x_tok, const void* g_tok, const void* bias,
+                            void* ring_x, void* ring_g, const int32_t* pos, const void* q_idx,
+                            const void* k_idx, const int32_t* n_cand, float* scores,
+                            int32_t* topk_idx, const void* q, const void* swa_kv,
+                            const int32_t* swa_len, void* comp_kv, const int32_t* comp_len,
+                            void* out, float* lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
+                            int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
+                            float scale, void* stream) {
+    try {
+        // append arguments (as hsa_decode_step); the rest is checked by the step itself
+        if (!dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!x_tok || !g_tok || !bias || !ring_x || !ring_g || !pos || !comp_kv)
+            return HSA_ERR_INVALID_ARG;
+        if (!aligned16(x_tok) || !aligned16(g_tok) || !aligned16(bias) || !aligned16(ring_x) ||
+            !aligned16(ring_g) || !aligned16(comp_kv))
+            return HSA_ERR_INVALID_ARG;
+        if (B < 1 || d_qk < 1 || S_max < 1) return HSA_ERR_INVALID_ARG;
+        if ((d_qk * esize(dtype)) % 16 != 0) return HSA_ERR_UNSUPPORTED;
+        const size_t need = hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k);
+        if (need == 0) return HSA_ERR_INVALID_ARG;
+        if (need > (size_t)HSA_NOALLOC_SCRATCH_BYTES) return HSA_ERR_WORKSPACE;
+        hipStream_t st = as_stream(stream);
+        int dev = 0;
+        hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess) return HSA_ERR_HIP;
+        void* ws = nullptr;
+        if (scratch_addr(dev, &ws) != hipSuccess) return HSA_ERR_HIP;
+        const hsa::AppendJob job{x_tok, g_tok, bias, ring_x, ring_g, pos, comp_kv, B, d_qk, S_max};
+        return decode_sparse_impl(dtype, q_idx, k_idx, n_cand, scores, topk_idx, q, swa_kv,
+                                  swa_len, comp_kv, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
+                                  W, S_max, k, scale, ws, (size_t)HSA_NOALLOC_SCRATCH_BYTES,
+                                  stream, &job, true);
     } catch (...) {
         return HSA_ERR_HIP;
     }

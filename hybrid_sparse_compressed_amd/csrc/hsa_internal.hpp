@@ -73,6 +73,8 @@ bool index_lists_apply(int S_max, int k, int Nq);
 // Zero the first-digit histograms of Nq queries in a top-k workspace (after a
 // scoring launch whose select did not run).
 hipError_t launch_clear_select_hist(void* ws, int Nq, int S_max, int k, hipStream_t st);
+// Zero `words` 32-bit words at p (16-byte aligned) with a fill kernel.
+hipError_t launch_zero_words(void* p, size_t words, hipStream_t st);
 hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
                               int S_max, int k, void* ws, const AppendJob* job, hipStream_t st);

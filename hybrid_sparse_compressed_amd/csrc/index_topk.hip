@@ -1049,7 +1049,27 @@ __global__ __launch_bounds__(kThreads) void clear_hist_kernel(uint8_t* __restric
     for (int i = (int)threadIdx.x; i < kBins; i += kThreads) h[i] = 0;
 }
 
+// Zero `words` 32-bit words from p (16-byte aligned), grid-stride with 16-byte stores.
+__global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* __restrict__ p,
+                                                              size_t words) {
+    const size_t n4 = words / 4;
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride)
+        reinterpret_cast<u32x4*>(p)[i] = u32x4{0u, 0u, 0u, 0u};
+    for (size_t i = n4 * 4 + (size_t)blockIdx.x * kThreads + threadIdx.x; i < words; i += stride)
+        p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_words(void* p, size_t words, hipStream_t st) {
+    if (words == 0) return hipSuccess;
+    const size_t blocks = (words / 4 + kThreads - 1) / kThreads;
+    const unsigned grid = (unsigned)(blocks < 1024 ? (blocks < 1 ? 1 : blocks) : 1024);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(kThreads), 0, st,
+                       static_cast<uint32_t*>(p), words);
+    return hipGetLastError();
+}
 
 hipError_t launch_clear_select_hist(void* ws, int Nq, int S_max, int k, hipStream_t st) {
     hipLaunchKernelGGL(clear_hist_kernel, dim3((unsigned)Nq), dim3(kThreads), 0, st,

@@ -293,6 +293,34 @@ int hsa_decode_step(int dtype, const void *x_tok, const void *g_tok, const void 
                     void *stream);
 
 /*
+ * hsa_decode_step_noalloc -- hsa_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.
+ *
+ * Same arguments, results and limits as hsa_decode_step, without the
+ * workspace.  Its scratch is a device array of the library itself,
+ * HSA_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU it runs on, held until the
+ * process ends; the call allocates nothing (the array's address on a device
+ * is looked up once, on the first call that uses that device).  A call whose
+ * need, hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k), exceeds the
+ * array returns HSA_ERR_WORKSPACE and launches nothing (4 sequences x 262,144
+ * C4 entries with top-512 need about 22 MB).  Every call first clears, with
+ * fill kernels on `stream`, the words of the array that must start at zero,
+ * so calls of any sizes may follow one another.  All calls on one GPU share
+ * the array: calls that overlap in time on one GPU (for example on two
+ * streams) race and give wrong results; the caller orders them.
+ */
+#define HSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int hsa_decode_step_noalloc(int dtype, const void *x_tok, const void *g_tok, const void *bias,
+                            void *ring_x, void *ring_g, const int32_t *pos, const void *q_idx,
+                            const void *k_idx, const int32_t *n_cand, float *scores,
+                            int32_t *topk_idx, const void *q, const void *swa_kv,
+                            const int32_t *swa_len, void *comp_kv, const int32_t *comp_len,
+                            void *out, float *lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
+                            int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
+                            float scale, void *stream);
+
+/*
  * hsa_attn_prefill -- a chunk of n_q consecutive query positions per
  * sequence, each with its own causal SWA window and its own compressed rows.
  *

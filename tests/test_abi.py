@@ -134,3 +134,26 @@ def test_attn_prefill_rejects(hsa):
     assert call(m=0) == 1
     assert call(kv=None) == 1
     assert call(d_qk=64, d_v=64) == 2
+
+
+def test_decode_step_noalloc_rejects(hsa):
+    """The no-allocation decode step rejects sizes whose workspace need exceeds its
+    fixed scratch (HSA_ERR_WORKSPACE) and bad arguments, launching nothing."""
+    lib = hsa.lib
+
+    def call(**kw):
+        a = dict(dtype=1, B=4, H_I=64, d_I=128, H=64, d_qk=576, d_v=512, W=128, S_max=262144,
+                 k=512, x_tok=A, comp=A)
+        a.update(kw)
+        ptrs = [a["x_tok"], A, A, A, A, A, A, A, A, A, A, A, A, A, a["comp"], A, A, A]
+        return lib.hsa_decode_step_noalloc(a["dtype"], *ptrs, a["B"], a["H_I"], a["d_I"], a["H"],
+                                           a["d_qk"], a["d_v"], a["W"], a["S_max"], a["k"], 0.04,
+                                           None)
+
+    need = lib.hsa_decode_sparse_workspace_size(4, 64, 512, 128, 262144, 512)
+    assert 0 < need <= 32 << 20                      # the 1M-context step fits the scratch
+    assert call(B=8) == 3                             # twice that does not
+    assert call(S_max=4000000, B=1) == 3
+    assert call(x_tok=None) == 1
+    assert call(comp=MIS) == 1
+    assert call(k=0) == 1
