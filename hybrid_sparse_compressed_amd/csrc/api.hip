@@ -201,7 +201,7 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
                                           S_max, k, scale, ws_attn, st);
         // the scoring launch counted into the histograms that the merge would have
         // cleared: leave the workspace ready for the next call all the same
-        if (e != hipSuccess) hsa::launch_clear_select_hist(ws_sel, B, S_max, k, st);
+        if (e != hipSuccess) (void)hsa::launch_clear_select_hist(ws_sel, B, S_max, k, st);
         return finish(e);
     }
     if (job) {

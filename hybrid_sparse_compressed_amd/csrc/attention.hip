@@ -74,16 +74,9 @@ template <> struct Mma<float> {
     }
 };
 
-// Element x of a 16-byte chunk, and a store of the x-th elements of two rows
-// (consecutive in the transposed tile) as one 2-element write.
+// fp32 tiles: a store of the x-th elements of two rows (consecutive in the
+// transposed tile) as one 2-element write.
 template <typename T> struct Pair;
-template <> struct Pair<bf16_t> {
-    __device__ static __forceinline__ void put(bf16_t* dst, const u32x4& a, const u32x4& b, int x) {
-        const uint32_t lo = (a[x >> 1] >> (16 * (x & 1))) & 0xffffu;
-        const uint32_t hi = (b[x >> 1] >> (16 * (x & 1))) & 0xffffu;
-        *reinterpret_cast<uint32_t*>(dst) = lo | (hi << 16);
-    }
-};
 template <> struct Pair<float> {
     __device__ static __forceinline__ void put(float* dst, const u32x4& a, const u32x4& b, int x) {
         *reinterpret_cast<uint2*>(dst) = uint2{a[x], b[x]};
@@ -113,16 +106,29 @@ struct AttnArgs {
 };
 
 // LDS footprint of one tile, in elements of T: K row-major, V^T (one row per
-// value channel), P^T (one row per head).  Every row carries a 16-byte skew
-// so that the 16 rows one MFMA operand reads fall on distinct banks.
+// value channel; fp32 only), P^T (one row per head).  Every row carries a
+// 16-byte skew so that the 16 rows one MFMA operand reads fall on distinct
+// banks.  bf16 tiles keep no V^T: the PV product reads the value columns out
+// of the row-major K rows with transposing LDS loads (kTr).
 template <typename T, int DQK, int DV> struct TileLds {
+    static constexpr bool kTr = sizeof(T) == 2;
     static constexpr int kSkew = 16 / (int)sizeof(T);
     static constexpr int kStrideK = DQK + kSkew;
     static constexpr int kStrideT = kTile + kSkew;   // V^T and P^T rows
     static constexpr size_t kOffV = (size_t)kTile * kStrideK;
-    static constexpr size_t kOffP = kOffV + (size_t)DV * kStrideT;
+    static constexpr size_t kOffP = kOffV + (kTr ? (size_t)0 : (size_t)DV * kStrideT);
     static constexpr size_t kBytes = (kOffP + (size_t)kHeadsPerWG * kStrideT) * sizeof(T);
 };
+
+// bf16 PV operands.  Step ks of the PV product contracts tile rows 32 ks ..
+// 32 ks + 31; k-slot 8 q + j of lane group q stands for row
+// 32 ks + 4 q + j (j < 4) or 32 ks + 16 + 4 q + (j - 4) (j >= 4), so that each
+// half of a lane's V^T fragment is one transposing read of 4 consecutive rows,
+// and the 8 rows that two lane groups read together sit 36 banks apart.  P^T
+// is stored in the same order: tile row R goes to position p_pos(R).
+__device__ __forceinline__ int p_pos(int R) {
+    return (R & ~31) + 8 * ((R >> 2) & 3) + 4 * ((R >> 4) & 1) + (R & 3);
+}
 
 // Rows of the PV contraction.  bf16: step ks takes tile rows 32*ks..32*ks+31,
 // lane group q the 8 rows 32*ks + 8*q + j.  fp32: step ks takes 4 rows, lane
@@ -348,23 +354,42 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     const T* win = reinterpret_cast<const T*>(a.win);
     const T* comp = reinterpret_cast<const T*>(a.comp);
 
-    // gather registers: a thread moves chunk `ch` of the row pair (2rp, 2rp+1)
-    // of a tile; the next tile's rows are loaded while this one is computed
-    constexpr int kUnits = (kTile / 2) * CPR;
+    // gather registers; the next tile's rows are loaded while this one is
+    // computed.  bf16: thread t moves chunks (t & 7) + 8 i of rows t / 8 and
+    // t / 8 + 32 (one instruction of a wave covers eight 128-byte runs),
+    // stored row-major.  fp32: chunk `ch` of the row pair (2rp, 2rp+1),
+    // stored row-major and transposed.
+    constexpr bool TR = L::kTr;
+    static_assert(!TR || (CPR % 8 == 0 && kTile == 2 * (kAttnThreads / 8)), "bf16 gather map");
+    constexpr int kUnits = TR ? kTile * CPR : (kTile / 2) * CPR;
     constexpr int kIter = (kUnits + kAttnThreads - 1) / kAttnThreads;
-    u32x4 ga[kIter], gb[kIter];
+    u32x4 ga[kIter], gb[TR ? 1 : kIter];
     auto issue = [&](int tb) {
+        if constexpr (TR) {
+            constexpr int NC = CPR / 8;  // chunks per row and thread
 #pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-            const int u = tid + it * kAttnThreads;
-            const int rp = u % (kTile / 2), ch = u / (kTile / 2);
-            ga[it] = gb[it] = u32x4{0u, 0u, 0u, 0u};
-            if (u < kUnits) {
-                const long long oa = row_off[tb + 2 * rp], ob = row_off[tb + 2 * rp + 1];
-                if (oa >= 0)
-                    ga[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp] ? comp : win) + oa + (long long)ch * V16);
-                if (ob >= 0)
-                    gb[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp + 1] ? comp : win) + ob + (long long)ch * V16);
+            for (int h = 0; h < 2; ++h) {
+                const int row = (tid >> 3) + 32 * h;
+                const long long o = row_off[tb + row];
+                const T* src = (row_src[tb + row] ? comp : win) + (o >= 0 ? o : 0) + (tid & 7) * V16;
+#pragma unroll
+                for (int i = 0; i < NC; ++i)
+                    ga[h * NC + i] = o >= 0 ? *reinterpret_cast<const u32x4*>(src + 8 * i * V16)
+                                            : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < kIter; ++it) {
+                const int u = tid + it * kAttnThreads;
+                const int rp = u % (kTile / 2), ch = u / (kTile / 2);
+                ga[it] = gb[it] = u32x4{0u, 0u, 0u, 0u};
+                if (u < kUnits) {
+                    const long long oa = row_off[tb + 2 * rp], ob = row_off[tb + 2 * rp + 1];
+                    if (oa >= 0)
+                        ga[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp] ? comp : win) + oa + (long long)ch * V16);
+                    if (ob >= 0)
+                        gb[it] = *reinterpret_cast<const u32x4*>((row_src[tb + 2 * rp + 1] ? comp : win) + ob + (long long)ch * V16);
+                }
             }
         }
     };
@@ -394,14 +419,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int it = 0; it < kIter; ++it) {
             const int u = tid + it * kAttnThreads;
-            const int rp = u % (kTile / 2), ch = u / (kTile / 2);
-            if (u < kUnits) {
-                *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp) * L::kStrideK + ch * V16) = ga[it];
-                *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp + 1) * L::kStrideK + ch * V16) = gb[it];
-                if (ch * V16 < DV) {
+            if constexpr (TR) {
+                constexpr int NC = CPR / 8;
+                const int row = (tid >> 3) + 32 * (it / NC), ch = (tid & 7) + 8 * (it % NC);
+                *reinterpret_cast<u32x4*>(Ks + (size_t)row * L::kStrideK + ch * V16) = ga[it];
+            } else {
+                const int rp = u % (kTile / 2), ch = u / (kTile / 2);
+                if (u < kUnits) {
+                    *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp) * L::kStrideK + ch * V16) = ga[it];
+                    *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp + 1) * L::kStrideK + ch * V16) = gb[it];
+                    if (ch * V16 < DV) {
 #pragma unroll
-                    for (int x = 0; x < V16; ++x)
-                        Pair<T>::put(Vt + (size_t)(ch * V16 + x) * L::kStrideT + 2 * rp, ga[it], gb[it], x);
+                        for (int x = 0; x < V16; ++x)
+                            Pair<T>::put(Vt + (size_t)(ch * V16 + x) * L::kStrideT + 2 * rp, ga[it], gb[it], x);
+                    }
                 }
             }
         }
@@ -498,12 +529,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             if (mw != -INFINITY) tsum += red_s[w][hl] * exp2f(mw - m_new);
         }
         const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
-        // P^T rows of this wave (natural row order)
+        // P^T rows of this wave (bf16: in the PV k-slot order, p_pos; fp32: natural)
         if constexpr (sizeof(T) == 2) {
             uint2 pk;
             pk.x = (uint32_t)f32_to_bf16(p[0] * sc) | ((uint32_t)f32_to_bf16(p[1] * sc) << 16);
             pk.y = (uint32_t)f32_to_bf16(p[2] * sc) | ((uint32_t)f32_to_bf16(p[3] * sc) << 16);
-            *reinterpret_cast<uint2*>(Pt + (size_t)hl * L::kStrideT + wave * 16 + quad * 4) = pk;
+            *reinterpret_cast<uint2*>(Pt + (size_t)hl * L::kStrideT + p_pos(wave * 16 + quad * 4)) = pk;
         } else {
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Pt) + (size_t)hl * L::kStrideT + wave * 16 + quad * 4) =
                 f32x4{p[0] * sc, p[1] * sc, p[2] * sc, p[3] * sc};
@@ -517,22 +548,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         __syncthreads();
 
         // ---- O^T[wave's channels] += V^T * P^T
-        const T* vbase = Vt + (size_t)(wave * DW + hl) * L::kStrideT;
         const T* pbase = Pt + (size_t)hl * L::kStrideT;
         if constexpr (sizeof(T) == 2) {
+            // V^T fragment of channel block t: two transposing reads of the K
+            // rows (rows 4 quad + (lane & 15) / 4 and 16 more, channels
+            // 16 t + 4 (lane & 3) of the wave's range), in p_pos order
+            const T* vtr = Ks + (size_t)(4 * quad + ((lane & 15) >> 2)) * L::kStrideK + wave * DW + 4 * (lane & 3);
 #pragma unroll
             for (int ks = 0; ks < kTile / 32; ++ks) {
                 // the step's P^T and V^T fragments are all read before its MFMAs
                 const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pbase + ks * 32 + quad * 8));
                 u32x4 vv[NMT];
 #pragma unroll
-                for (int t = 0; t < NMT; ++t)
-                    vv[t] = *reinterpret_cast<const u32x4*>(vbase + (size_t)t * 16 * L::kStrideT + ks * 32 + quad * 8);
+                for (int t = 0; t < NMT; ++t) {
+                    const T* pa = vtr + (size_t)(32 * ks) * L::kStrideK + 16 * t;
+                    const uint2 lo = lds_read_tr16x4(pa);
+                    const uint2 hi = lds_read_tr16x4(pa + (size_t)16 * L::kStrideK);
+                    vv[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int t = 0; t < NMT; ++t) acc[t] = M::mma(__builtin_bit_cast(bf16x8, vv[t]), pf, acc[t]);
             }
         } else {
+            const T* vbase = Vt + (size_t)(wave * DW + hl) * L::kStrideT;
             // lane group q contracts rows 16q..16q+15 (one per step): 4 vector reads per operand
             const float* pf = reinterpret_cast<const float*>(pbase) + quad * 16;
 #pragma unroll
@@ -618,20 +657,15 @@ constexpr int kP64Heads = 64;
 constexpr int kP64Rows = 64;                    // rows per tile
 constexpr int kP64Chunk = kP64Threads;          // rows listed at once (one per thread)
 
+// K rows (row-major; the PV product reads the value columns out of them with
+// transposing LDS loads) and P^T (one row per head, in p_pos order).
 template <int DQK, int DV> struct P64Lds {
     static constexpr int kSkew = 8;             // 16 bytes of bf16
     static constexpr int kStrideK = DQK + kSkew;
     static constexpr int kStrideT = kP64Rows + kSkew;
-    static constexpr size_t kOffV = (size_t)kP64Rows * kStrideK;
-    static constexpr size_t kOffP = kOffV + (size_t)DV * kStrideT;
+    static constexpr size_t kOffP = (size_t)kP64Rows * kStrideK;
     static constexpr size_t kBytes = (kOffP + (size_t)kP64Heads * kStrideT) * sizeof(bf16_t);
 };
-
-// the two bf16 halves x of chunks a and b as one word (a low, b high)
-__device__ __forceinline__ uint32_t pair_word(const u32x4& a, const u32x4& b, int x) {
-    return (x & 1) ? __builtin_amdgcn_perm(b[x >> 1], a[x >> 1], 0x07060302u)
-                   : __builtin_amdgcn_perm(b[x >> 1], a[x >> 1], 0x05040100u);
-}
 
 template <int DQK, int DV, bool DEC>
 __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
@@ -648,7 +682,6 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
     T* Ks = reinterpret_cast<T*>(lds_raw);
-    T* Vt = Ks + L::kOffV;
     T* Pt = Ks + L::kOffP;
     __shared__ const T* row_ptr[kP64Chunk];        // row address, nullptr: no row
     __shared__ int tile_any[kP64Chunk / kP64Rows];
@@ -720,23 +753,17 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < NMT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // gather: thread moves chunk ch of the row pair (2rp, 2rp+1) of a tile
-    constexpr int kUnits = (kP64Rows / 2) * CPR;
-    constexpr int kIter = (kUnits + kP64Threads - 1) / kP64Threads;
-    u32x4 ga[kIter], gb[kIter];
+    // gather: thread t moves chunks (t & 7) + 8 i of row t / 8 of a tile (one
+    // instruction of a wave covers eight 128-byte runs), stored row-major
+    static_assert(CPR % 8 == 0 && kP64Rows * 8 == kP64Threads, "gather map");
+    constexpr int kIter = CPR / 8;
+    u32x4 ga[kIter];
     auto issue = [&](int tb) {
+        const T* pr = row_ptr[tb + (tid >> 3)];
+        const T* src = (pr ? pr : reinterpret_cast<const T*>(a.q)) + (tid & 7) * V16;
 #pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-            const int u = tid + it * kP64Threads;
-            const int rp = u % (kP64Rows / 2), ch = u / (kP64Rows / 2);
-            ga[it] = gb[it] = u32x4{0u, 0u, 0u, 0u};
-            if (u < kUnits) {
-                const T* pa = row_ptr[tb + 2 * rp];
-                const T* pb = row_ptr[tb + 2 * rp + 1];
-                if (pa) ga[it] = *reinterpret_cast<const u32x4*>(pa + ch * V16);
-                if (pb) gb[it] = *reinterpret_cast<const u32x4*>(pb + ch * V16);
-            }
-        }
+        for (int it = 0; it < kIter; ++it)
+            ga[it] = pr ? *reinterpret_cast<const u32x4*>(src + 8 * it * V16) : u32x4{0u, 0u, 0u, 0u};
     };
 
     for (int c0 = vr0; c0 < vr1; c0 += kP64Chunk) {
@@ -756,20 +783,8 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             if (!tile_any[tb / kP64Rows]) continue;  // uniform
             if (pre != tb) issue(tb);
 #pragma unroll
-            for (int it = 0; it < kIter; ++it) {
-                const int u = tid + it * kP64Threads;
-                const int rp = u % (kP64Rows / 2), ch = u / (kP64Rows / 2);
-                if (u < kUnits) {
-                    *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp) * L::kStrideK + ch * V16) = ga[it];
-                    *reinterpret_cast<u32x4*>(Ks + (size_t)(2 * rp + 1) * L::kStrideK + ch * V16) = gb[it];
-                    if (ch * V16 < DV) {
-#pragma unroll
-                        for (int x = 0; x < V16; ++x)
-                            *reinterpret_cast<uint32_t*>(Vt + (size_t)(ch * V16 + x) * L::kStrideT + 2 * rp) =
-                                pair_word(ga[it], gb[it], x);
-                    }
-                }
-            }
+            for (int it = 0; it < kIter; ++it)
+                *reinterpret_cast<u32x4*>(Ks + (size_t)(tid >> 3) * L::kStrideK + ((tid & 7) + 8 * it) * V16) = ga[it];
             __syncthreads();
             pre = -1;
             for (int nb = tb + kP64Rows; nb < c1 - c0; nb += kP64Rows) {
@@ -848,11 +863,11 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             }
             const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < 2; ++rb) {  // P^T in the PV k-slot order (p_pos)
                 uint2 pk;
                 pk.x = (uint32_t)f32_to_bf16(p[4 * rb] * sc) | ((uint32_t)f32_to_bf16(p[4 * rb + 1] * sc) << 16);
                 pk.y = (uint32_t)f32_to_bf16(p[4 * rb + 2] * sc) | ((uint32_t)f32_to_bf16(p[4 * rb + 3] * sc) << 16);
-                *reinterpret_cast<uint2*>(Pt + (size_t)head * L::kStrideT + 32 * half + 16 * rb + 4 * quad) = pk;
+                *reinterpret_cast<uint2*>(Pt + (size_t)head * L::kStrideT + p_pos(32 * half + 16 * rb + 4 * quad)) = pk;
             }
             if (__ballot(move && l_run > 0.f)) {
 #pragma unroll
@@ -862,8 +877,9 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             m_run = m_new;
             __syncthreads();
 
-            // ---- O^T[channels 256*half + 16t.., head] += V^T * P^T
-            const T* vbase = Vt + (size_t)(half * DW + hl) * L::kStrideT;
+            // ---- O^T[channels 256*half + 16t.., head] += V^T * P^T; V^T
+            // fragments by transposing reads of the K rows (as attn_kernel)
+            const T* vtr = Ks + (size_t)(4 * quad + ((lane & 15) >> 2)) * L::kStrideK + half * DW + 4 * (lane & 3);
             const T* pbase = Pt + (size_t)head * L::kStrideT;
 #pragma unroll
             for (int ks = 0; ks < kP64Rows / 32; ++ks) {
@@ -873,8 +889,12 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
                 for (int t0 = 0; t0 < NMT; t0 += VG) {
                     u32x4 vv[VG];
 #pragma unroll
-                    for (int j = 0; j < VG; ++j)
-                        vv[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(t0 + j) * 16 * L::kStrideT + ks * 32 + quad * 8);
+                    for (int j = 0; j < VG; ++j) {
+                        const T* pa = vtr + (size_t)(32 * ks) * L::kStrideK + 16 * (t0 + j);
+                        const uint2 lo = lds_read_tr16x4(pa);
+                        const uint2 hi = lds_read_tr16x4(pa + (size_t)16 * L::kStrideK);
+                        vv[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int j = 0; j < VG; ++j)

@@ -13,6 +13,19 @@ constexpr int kWave = 64;  // CDNA wavefront width
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane b passes the address of 4 consecutive 16-bit elements
+// B_b[0..3]; lane l of the group receives B_{4m + l/4}[l % 4] for m = 0..3.
+// Pointing lane b at M[r0 + b/4][c0 + 4 (b % 4)] of a row-major 16-bit matrix
+// M therefore hands lane l the column c0 + l % 16 over rows r0 .. r0 + 3.
+__device__ __forceinline__ uint2 lds_read_tr16x4(const void* p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(const __attribute__((address_space(3))) void*)p);
+    return __builtin_bit_cast(uint2, v);
+}
 
 // Storage tag for bf16 (raw 16-bit pattern); fp32 is stored as float.
 struct bf16_t {
