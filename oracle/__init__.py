@@ -232,3 +232,120 @@ def attn_prefill(q, kv, comp_kv, q_start, W, m, scale, d_v, comp_idx=None, sel=N
                                        n_seq, n_q, q_start, T, H, d_qk, d_v, W, S_max, k, m,
                                        float(scale), _p(sl), sl.shape[0]), "attn_prefill")
     return out, lse
+
+
+# ---- paged pools --------------------------------------------------------------
+# [KD "Arquitectura del Sistema", ShadowRadix paragraph] and [NK "推理侧优化",
+# shadow radix cache bullet]: every pool is addressed through its own index
+# map ("shadow") from a sequence's virtual rows to physical storage, so pools
+# live and die independently (SWA pages go once the window has passed them).
+# Reading (the pages give no layout): a pool is [pool_pages, P, D]; row r of
+# sequence b is pool[page_map[b, r // P], r % P]; a page past the map or a map
+# entry outside [0, pool_pages) is not resident.  SWA rows are indexed by
+# token position, C4 KV and indexer-key rows by entry; the compression state
+# of token t sits at t's SWA row in two state pools shaped like the SWA pool.
+# These functions only resolve the maps and then call the definitions above.
+
+def paged_rows(pool, page_map_b, n_rows, page_rows, fill=np.nan):
+    """Rows 0 .. n_rows-1 of one sequence of a paged pool.
+
+    pool: [pool_pages, P, D] (torch CPU or numpy); page_map_b: the sequence's
+    map entries.  Returns (rows float64 [n_rows, D], resident bool [n_rows]);
+    rows that are not resident hold `fill`."""
+    pa = np.asarray(pool.float() if hasattr(pool, "float") else pool, dtype=np.float64)
+    pm = np.asarray(page_map_b, dtype=np.int64).reshape(-1)
+    r = np.arange(n_rows)
+    j = r // page_rows
+    page = np.where(j < pm.shape[0], pm[np.minimum(j, max(pm.shape[0] - 1, 0))], -1)
+    resident = (page >= 0) & (page < pa.shape[0])
+    rows = np.full((n_rows, pa.shape[2]), fill, dtype=np.float64)
+    rows[resident] = pa[page[resident], (r % page_rows)[resident]]
+    return rows, resident
+
+
+def physical_row(page_map_b, r, page_rows, pool_pages):
+    """(page, offset) of row r of one sequence, or None when it is not resident."""
+    pm = np.asarray(page_map_b).reshape(-1)
+    j = r // page_rows
+    if r < 0 or j >= pm.shape[0] or not (0 <= int(pm[j]) < pool_pages):
+        return None
+    return int(pm[j]), r % page_rows
+
+
+def compress_append_paged(x_tok, g_tok, bias, state_x, state_g, pos, swa_map, c4_map,
+                          swa_page_rows, c4_page_rows, c4_pool_pages, S_max, m=4):
+    """Decode-time compression state on paged pools (m = 4).
+
+    The token of sequence b at p = pos[b] >= 0 is stored at its SWA row of the
+    state pools (state_x, state_g: [swa_pool_pages, P, D], updated in place);
+    when p mod m == m-1 and i = p div m < S_max, the entry of tokens p-m+1 .. p
+    (compress() of their state rows) is due at C4 row i.  A token whose SWA
+    row is not resident is not stored; an entry whose C4 row (or a state row of
+    its block) is not resident is not formed.
+    Returns [(b, i, (page, offset), entry float64 [D])] for the entries formed."""
+    written = []
+    n_pages = state_x.shape[0]
+    for b in range(x_tok.shape[0]):
+        p = int(pos[b])
+        if p < 0:
+            continue
+        at = physical_row(swa_map[b], p, swa_page_rows, n_pages)
+        if at is None:
+            continue
+        state_x[at[0], at[1]] = x_tok[b]
+        state_g[at[0], at[1]] = g_tok[b]
+        i = p // m
+        if p % m != m - 1 or i >= S_max:
+            continue
+        dest = physical_row(c4_map[b], i, c4_page_rows, c4_pool_pages)
+        rows = [physical_row(swa_map[b], t, swa_page_rows, n_pages) for t in range(p - m + 1, p + 1)]
+        if dest is None or any(a is None for a in rows):
+            continue
+        rx = state_x[[a[0] for a in rows], [a[1] for a in rows]][None, None]
+        rg = state_g[[a[0] for a in rows], [a[1] for a in rows]][None, None]
+        # one block of m tokens: [1, m, D]
+        entry = compress(rx.reshape(1, m, -1), rg.reshape(1, m, -1), bias, m)[0, 0]
+        written.append((b, i, dest, entry))
+    return written
+
+
+def index_scores_paged(q_idx, kI_pool, kI_map, c4_page_rows, n_cand, S_max):
+    """index_scores over indexer-key rows reached through the kI shadow; a row
+    that is not resident is all-NaN, so its score is NaN."""
+    B = q_idx.shape[0]
+    keys = np.stack([paged_rows(kI_pool, kI_map[b], S_max, c4_page_rows)[0] for b in range(B)])
+    return index_scores(q_idx.double() if hasattr(q_idx, "double") else np.asarray(q_idx, np.float64),
+                        keys, n_cand)
+
+
+def attn_decode_paged(q, swa_pool, swa_map, swa_page_rows, swa_len, pos, W, c4_pool, c4_map,
+                      c4_page_rows, comp_len, comp_idx, S_max, scale, d_v):
+    """attn_decode (sparse) with the window = the n = clamp(swa_len[b], 0, W)
+    tokens pos[b]-n+1 .. pos[b] (none when pos[b] < 0) and the listed C4 rows
+    (i < comp_len[b]), each read through its shadow; rows that are not resident
+    are left out."""
+    qa = np.asarray(q.double() if hasattr(q, "double") else q, dtype=np.float64)
+    B, H, d_qk = qa.shape
+    sp = np.asarray(swa_pool.float() if hasattr(swa_pool, "float") else swa_pool, dtype=np.float64)
+    win = np.zeros((B, W, d_qk))
+    n_win = np.zeros(B, dtype=np.int32)
+    comp = np.zeros((B, S_max, d_qk))
+    ci = np.array(comp_idx, dtype=np.int32, copy=True)
+    for b in range(B):
+        p = int(pos[b])
+        n = min(max(int(swa_len[b]), 0), W) if p >= 0 else 0
+        kept = []
+        for t in range(p - n + 1, p + 1):
+            at = physical_row(swa_map[b], t, swa_page_rows, sp.shape[0])
+            if at is not None:
+                kept.append(sp[at[0], at[1]])
+        for j, row in enumerate(kept):
+            win[b, j] = row
+        n_win[b] = len(kept)
+        crow, cres = paged_rows(c4_pool, c4_map[b], S_max, c4_page_rows, fill=0.0)
+        comp[b] = crow
+        for j in range(ci.shape[1]):
+            if 0 <= ci[b, j] < S_max and not cres[ci[b, j]]:
+                ci[b, j] = -1
+    return attn_decode(qa, win, n_win, comp, np.asarray(comp_len, dtype=np.int32), scale, d_v,
+                       comp_idx=ci)
