@@ -372,7 +372,61 @@ def other_rows(hsa, workloads):
     del e
     rows.update(append_rows(hsa, torch))
     torch.cuda.empty_cache()
+    rows.update(paged_step_rows(hsa, workloads, torch))
+    torch.cuda.empty_cache()
     return rows
+
+
+def paged_step_rows(hsa, workloads, torch):
+    """The metric's layer-step on paged pools: c4_decode_1m with the indexer keys and
+    the C4 pool on shuffled 256-row pages and the window and compression state on
+    64-token SWA pages (only the pages the window and the open block use resident),
+    timed next to the same step on the flat pools (same inputs, same bytes)."""
+    w = workloads.c4_decode("c4_decode_1m", "cuda")
+    c = w["cfg"]
+    B, S, k, H, D, W = c["B"], w["S"], c["k"], c["H"], c["d_qk"], c["W"]
+    g = torch.Generator().manual_seed(11)
+    bf = torch.bfloat16
+
+    def paged(flat, P):
+        n = flat.shape[1] // P
+        perm = torch.randperm(B * n, generator=g).cuda()
+        pool = torch.empty((B * n, P, flat.shape[2]), dtype=bf, device="cuda")
+        pool[perm] = flat.reshape(B * n, P, flat.shape[2])
+        return pool, perm.reshape(B, n).to(torch.int32)
+
+    kI, kmap = paged(w["k_idx"], 256)
+    c4, cmap = paged(w["comp_kv"], 256)
+    P = 64
+    pos = torch.full((B,), 4 * (S - 1) + 3, dtype=torch.int32, device="cuda")
+    last = (4 * (S - 1) + 3) // P
+    smap = torch.full((B, last + 1), -1, dtype=torch.int32)
+    for b in range(B):  # the window (128 tokens) and the open block: the last three pages
+        for j in range(3):
+            smap[b, last - j] = 3 * b + j
+    smap = smap.cuda()
+    swa = torch.randn((3 * B, P, D), device="cuda").to(bf)
+    sx, sg = torch.randn_like(swa, dtype=torch.float32).to(bf), torch.randn_like(swa, dtype=torch.float32).to(bf)
+    xt = torch.randn((B, D), device="cuda").to(bf)
+    gt = torch.randn((B, D), device="cuda").to(bf)
+    bias = (torch.randn((4, D), device="cuda") * 0.1).to(bf)
+    rx, rg = torch.randn((B, 4, D), device="cuda").to(bf), torch.randn((B, 4, D), device="cuda").to(bf)
+    sc = torch.empty((B, S), dtype=torch.float32, device="cuda")
+    ix = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    o = torch.empty((B, H, 512), dtype=bf, device="cuda")
+    l = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    us = _median_us(torch, lambda: hsa.hsa_decode_step_paged(
+        xt, gt, bias, sx, sg, pos, w["q_idx"], kI, kmap, w["n_cand"], k, w["q"], swa, smap,
+        w["swa_len"], c4, cmap, w["comp_len"], w["scale"], 512, W, S, scores=sc, topk_idx=ix,
+        out=o, lse=l), 7, 20)
+    flat_us = _median_us(torch, lambda: hsa.hsa_decode_step(
+        xt, gt, bias, rx, rg, pos, w["q_idx"], w["k_idx"], w["n_cand"], k, w["q"], w["swa_kv"],
+        w["swa_len"], w["comp_kv"], w["comp_len"], w["scale"], 512, scores=sc, topk_idx=ix,
+        out=o, lse=l), 7, 20)
+    alg = (B * S * 128 * 2 + B * (W + k) * D * 2 + B * H * D * 2 + B * H * 512 * 2
+           + B * 64 * 128 * 2 + B * k * 4)
+    return {"f2_decode_step_paged_c4_1m": _row("c4_decode_1m", us, "hbm", alg, "GB/s", HBM_PEAK_GBPS,
+                                               flat_us=round(flat_us, 2), page_rows={"swa": P, "c4": 256})}
 
 
 def append_rows(hsa, torch):

@@ -24,10 +24,19 @@ EXPORTED = (
     "hsa_index_topk_workspace_size",
     "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
     "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
-    "hsa_decode_sparse", "hsa_decode_step", "hsa_decode_step_noalloc", "hsa_profile_enable",
-    "hsa_profile_read",
+    "hsa_decode_sparse", "hsa_decode_step", "hsa_decode_step_noalloc", "hsa_decode_step_paged",
+    "hsa_profile_enable", "hsa_profile_read",
 )
 HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
+
+
+class PageMaps(ctypes.Structure):
+    """hsa_page_maps: the shadows of one paged decode call (device map pointers)."""
+    _fields_ = [("swa_map", ctypes.c_void_p), ("swa_map_pages", ctypes.c_int32),
+                ("swa_page_rows", ctypes.c_int32), ("swa_pool_pages", ctypes.c_int32),
+                ("c4_map", ctypes.c_void_p), ("kI_map", ctypes.c_void_p),
+                ("c4_map_pages", ctypes.c_int32), ("c4_page_rows", ctypes.c_int32),
+                ("c4_pool_pages", ctypes.c_int32), ("kI_pool_pages", ctypes.c_int32)]
 
 
 class HsaError(RuntimeError):
@@ -70,6 +79,9 @@ def _load():
     lib.hsa_decode_step.restype = I
     lib.hsa_decode_step_noalloc.argtypes = [I] + [P] * 18 + [I32] * 9 + [F, P]
     lib.hsa_decode_step_noalloc.restype = I
+    lib.hsa_decode_step_paged.argtypes = [I] + [P] * 16 + [ctypes.POINTER(PageMaps), P, P] + \
+        [I32] * 9 + [F, P, SZ, P]
+    lib.hsa_decode_step_paged.restype = I
     lib.hsa_attn_prefill_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.hsa_attn_prefill_workspace_size.restype = SZ
     lib.hsa_attn_prefill.argtypes = [I, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
@@ -358,6 +370,66 @@ def hsa_decode_step(x_tok, g_tok, bias, ring_x, ring_g, pos, q_idx, k_idx, n_can
         _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
         d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)),
         workspace, cached)
+    return scores, topk_idx, out, lse
+
+
+def hsa_decode_step_paged(x_tok, g_tok, bias, state_x, state_g, pos, q_idx, kI_pool, kI_map,
+                          n_cand, k, q, swa_pool, swa_map, swa_len, c4_pool, c4_map, comp_len,
+                          scale, d_v, W, S_max, scores=None, topk_idx=None, out=None, lse=None,
+                          workspace=None, stream=None):
+    """hsa_decode_step on paged pools (x_tok None: no append, as hsa_decode_sparse).
+
+    Pools: swa_pool, state_x, state_g [swa_pool_pages, P_swa, d_qk]; c4_pool
+    [c4_pool_pages, P_c4, d_qk]; kI_pool [kI_pool_pages, P_c4, d_I].  Shadows
+    (int32 device tensors): swa_map [B, swa_map_pages], c4_map and kI_map
+    [B, c4_map_pages].  pos: [B] int32, the query token positions.  Window: the
+    swa_len[b] (<= W) tokens ending at pos[b].  Returns (scores, topk_idx, out, lse)."""
+    B, H_I, d_I = q_idx.shape
+    _, H, d_qk = q.shape
+    if kI_pool.dtype != q_idx.dtype or q.dtype != q_idx.dtype or swa_pool.dtype != q.dtype \
+            or c4_pool.dtype != q.dtype:
+        raise TypeError("hsa_decode_step_paged: pools must have the query dtype")
+    if swa_pool.dim() != 3 or c4_pool.dim() != 3 or kI_pool.dim() != 3:
+        raise ValueError("hsa_decode_step_paged: pools are [pages, rows, D]")
+    if kI_pool.shape[1] != c4_pool.shape[1] or kI_map.shape != c4_map.shape:
+        raise ValueError("hsa_decode_step_paged: kI and C4 shadows must share the page size")
+    for t in (pos, swa_map, c4_map, kI_map):
+        if t.dtype != torch.int32:
+            raise TypeError("hsa_decode_step_paged: pos and maps must be int32")
+    if x_tok is not None:
+        for t in (x_tok, g_tok, bias, state_x, state_g):
+            if t.dtype != q.dtype:
+                raise TypeError("hsa_decode_step_paged: append tensors must have the query dtype")
+        if (tuple(x_tok.shape) != (B, d_qk) or tuple(g_tok.shape) != (B, d_qk)
+                or tuple(bias.shape) != (4, d_qk) or tuple(state_x.shape) != tuple(swa_pool.shape)
+                or tuple(state_g.shape) != tuple(swa_pool.shape)):
+            raise ValueError("hsa_decode_step_paged: append shape mismatch")
+    maps = PageMaps(_ptr(swa_map).value, swa_map.shape[1], swa_pool.shape[1], swa_pool.shape[0],
+                    _ptr(c4_map).value, _ptr(kI_map).value, c4_map.shape[1], c4_pool.shape[1],
+                    c4_pool.shape[0], kI_pool.shape[0])
+    dev = q.device
+    n_cand, swa_len, comp_len = _i32(n_cand, dev), _i32(swa_len, dev), _i32(comp_len, dev)
+    if scores is None:
+        scores = torch.empty((B, S_max), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream() if stream is None else stream
+    need = lib.hsa_decode_sparse_workspace_size(B, H, d_v, W, S_max, k)
+    cached = workspace is None
+    if cached:
+        workspace = Workspace.get("decode_sparse:%d:%d:%d:%d:%d" % (B, H, d_v, W, S_max * 4096 + k),
+                                  need, dev, st)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call_with_workspace("hsa_decode_step_paged", lambda: lib.hsa_decode_step_paged(
+        _dt(q), _ptr(x_tok), _ptr(g_tok), _ptr(bias), _ptr(state_x), _ptr(state_g), _ptr(pos),
+        _ptr(q_idx), _ptr(kI_pool), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
+        _ptr(swa_pool), _ptr(swa_len), _ptr(c4_pool), _ptr(comp_len), ctypes.byref(maps),
+        _ptr(out), _ptr(lse), B, H_I, d_I, H, d_qk, d_v, W, S_max, k, float(scale),
+        _ptr(workspace), wsz, _stream(st)), workspace, cached)
     return scores, topk_idx, out, lse
 
 

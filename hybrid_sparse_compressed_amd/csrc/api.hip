@@ -155,7 +155,8 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
                        void* out, float* lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
                        int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
                        float scale, void* workspace, size_t workspace_bytes, void* stream,
-                       const hsa::AppendJob* job, bool clear_ws = false) {
+                       const hsa::AppendJob* job, bool clear_ws = false,
+                       const hsa::Paging* pg = nullptr) {
     // indexer + select arguments (as hsa_index_topk with Nq = B, no q_seq)
     if (!dtype_ok(dtype) || !q_idx || !k_idx || !n_cand || !scores || !topk_idx)
         return HSA_ERR_INVALID_ARG;
@@ -194,28 +195,32 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
         // the append rides in the scoring launch, which ends before the attention
         // reads the pool; scoring never reads it
         hipError_t e = hsa::launch_index_lists(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
-                                               d_I, S_max, k, ws_sel, job, st);
+                                               d_I, S_max, k, ws_sel, job, st,
+                                               pg ? &pg->kI : nullptr);
         if (e != hipSuccess) return finish(e);
         e = hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len, n_cand,
                                           ws_sel, scores, topk_idx, out, lse, B, H, d_qk, d_v, W,
-                                          S_max, k, scale, ws_attn, st);
+                                          S_max, k, scale, ws_attn, st, pg);
         // the scoring launch counted into the histograms that the merge would have
         // cleared: leave the workspace ready for the next call all the same
         if (e != hipSuccess) (void)hsa::launch_clear_select_hist(ws_sel, B, S_max, k, st);
         return finish(e);
     }
     if (job) {
-        hipError_t e = hsa::launch_compress_append(dtype, job->x_tok, job->g_tok, job->bias,
-                                                   job->ring_x, job->ring_g, job->pos, job->pool,
-                                                   job->B, job->D, 4, job->S_max, st);
+        hipError_t e = job->swa.map
+                           ? hsa::launch_compress_append_paged(dtype, *job, st)
+                           : hsa::launch_compress_append(dtype, job->x_tok, job->g_tok, job->bias,
+                                                         job->ring_x, job->ring_g, job->pos,
+                                                         job->pool, job->B, job->D, 4, job->S_max, st);
         if (e != hipSuccess) return finish(e);
     }
     hipError_t e = hsa::launch_index_topk(dtype, q_idx, k_idx, B, nullptr, n_cand, scores,
-                                          topk_idx, B, H_I, d_I, S_max, k, ws_sel, st);
+                                          topk_idx, B, H_I, d_I, S_max, k, ws_sel, st,
+                                          pg ? &pg->kI : nullptr);
     if (e != hipSuccess) return finish(e);
     return finish(hsa::launch_attn_decode(dtype, q, swa_kv, swa_len, comp_kv, topk_idx,
                                           comp_len, out, lse, B, H, d_qk, d_v, W, S_max, k,
-                                          scale, ws_attn, st));
+                                          scale, ws_attn, st, pg));
 }
 
 }  // namespace
@@ -257,6 +262,51 @@ int hsa_decode_step(int dtype, const void* x_tok, const void* g_tok, const void*
         return decode_sparse_impl(dtype, q_idx, k_idx, n_cand, scores, topk_idx, q, swa_kv,
                                   swa_len, comp_kv, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
                                   W, S_max, k, scale, workspace, workspace_bytes, stream, &job);
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+int hsa_decode_step_paged(int dtype, const void* x_tok, const void* g_tok, const void* bias,
+                          void* state_x, void* state_g, const int32_t* pos, const void* q_idx,
+                          const void* kI_pool, const int32_t* n_cand, float* scores,
+                          int32_t* topk_idx, const void* q, const void* swa_pool,
+                          const int32_t* swa_len, void* c4_pool, const int32_t* comp_len,
+                          const hsa_page_maps* maps, void* out, float* lse, int32_t B,
+                          int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v,
+                          int32_t W, int32_t S_max, int32_t k, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    try {
+        if (!dtype_ok(dtype) || !maps || !pos) return HSA_ERR_INVALID_ARG;
+        const hsa_page_maps& m = *maps;
+        auto page_rows_ok = [](int32_t v) { return v >= 16 && v <= 4096 && (v & (v - 1)) == 0; };
+        if (!m.swa_map || !m.c4_map || !m.kI_map) return HSA_ERR_INVALID_ARG;
+        if (!page_rows_ok(m.swa_page_rows) || !page_rows_ok(m.c4_page_rows)) return HSA_ERR_INVALID_ARG;
+        if (m.swa_map_pages < 1 || m.c4_map_pages < 1 || m.swa_pool_pages < 1 ||
+            m.c4_pool_pages < 1 || m.kI_pool_pages < 1)
+            return HSA_ERR_INVALID_ARG;
+        if (B < 1 || S_max < 1 || d_qk < 1) return HSA_ERR_INVALID_ARG;
+        if ((long long)m.c4_map_pages * m.c4_page_rows < S_max) return HSA_ERR_INVALID_ARG;
+        hsa::Paging pg;
+        pg.swa = {m.swa_map, m.swa_map_pages, __builtin_ctz((unsigned)m.swa_page_rows), m.swa_pool_pages};
+        pg.c4 = {m.c4_map, m.c4_map_pages, __builtin_ctz((unsigned)m.c4_page_rows), m.c4_pool_pages};
+        pg.kI = {m.kI_map, m.c4_map_pages, __builtin_ctz((unsigned)m.c4_page_rows), m.kI_pool_pages};
+        pg.pos = pos;
+        hsa::AppendJob job{};
+        if (x_tok) {
+            // append arguments (as hsa_decode_step, the rings replaced by the state pools)
+            if (!g_tok || !bias || !state_x || !state_g || !c4_pool) return HSA_ERR_INVALID_ARG;
+            if (!aligned16(x_tok) || !aligned16(g_tok) || !aligned16(bias) || !aligned16(state_x) ||
+                !aligned16(state_g) || !aligned16(c4_pool))
+                return HSA_ERR_INVALID_ARG;
+            if ((d_qk * esize(dtype)) % 16 != 0) return HSA_ERR_UNSUPPORTED;
+            job = hsa::AppendJob{x_tok, g_tok, bias, state_x, state_g, pos, c4_pool, B, d_qk, S_max,
+                                 pg.swa, pg.c4};
+        }
+        return decode_sparse_impl(dtype, q_idx, kI_pool, n_cand, scores, topk_idx, q, swa_pool,
+                                  swa_len, c4_pool, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
+                                  W, S_max, k, scale, workspace, workspace_bytes, stream,
+                                  x_tok ? &job : nullptr, false, &pg);
     } catch (...) {
         return HSA_ERR_HIP;
     }

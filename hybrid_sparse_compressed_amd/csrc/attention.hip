@@ -103,6 +103,10 @@ struct AttnArgs {
     int hblocks, n_queries;  // prefill: head blocks per query, queries in the grid
     int list_rows_lg;     // fused decode: log2 of the candidate rows per list slot
     float scale_log2;     // scale * log2(e)
+    // paged decode (pg_swa.map != nullptr): win and comp are the paged SWA and
+    // C4 pools; window row vr of sequence b is token pos[b] - n_swa + 1 + vr
+    PoolMap pg_swa, pg_c4;
+    const int32_t* pos;
 };
 
 // LDS footprint of one tile, in elements of T: K row-major, V^T (one row per
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     } else {
         n_swa = a.swa_len[b];
         n_swa = n_swa < 0 ? 0 : (n_swa > a.W ? a.W : n_swa);
+        if (a.pg_swa.map && a.pos[b] < 0) n_swa = 0;  // paged: no query token, no window
         n_comp = a.comp_len[b];
         n_comp = n_comp < 0 ? 0 : (n_comp > a.S_max ? a.S_max : n_comp);
     }
@@ -266,8 +271,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             if constexpr (PREFILL) {
                 const int tok = qpos - a.W + 1 + vr;
                 if (tok >= 0) off = ((long long)b * a.T_len + tok) * DQK;
-            } else {
-                if (vr < n_swa) off = ((long long)b * a.W + vr) * DQK;
+            } else if (vr < n_swa) {
+                if (a.pg_swa.map) {
+                    const long long pr = paged_row(a.pg_swa, b, (long long)a.pos[b] - n_swa + 1 + vr);
+                    if (pr >= 0) off = pr * DQK;
+                } else {
+                    off = ((long long)b * a.W + vr) * DQK;
+                }
             }
         } else {
             const int j = vr - a.W;
@@ -284,8 +294,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
                 ci = j;
             }
             if (ci >= 0 && ci < n_comp) {
-                off = ((long long)b * a.S_max + ci) * DQK;
-                src = 1;
+                if (!PREFILL && a.pg_c4.map) {
+                    const long long pr = paged_row(a.pg_c4, b, ci);
+                    if (pr >= 0) {
+                        off = pr * DQK;
+                        src = 1;
+                    }
+                } else {
+                    off = ((long long)b * a.S_max + ci) * DQK;
+                    src = 1;
+                }
             }
         }
     };
@@ -1166,8 +1184,14 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
                               const int32_t* swa_len, const void* comp_kv,
                               const int32_t* comp_idx, const int32_t* comp_len, void* out,
                               float* lse, int B, int H, int d_qk, int d_v, int W, int S_max,
-                              int k, float scale, void* ws, hipStream_t st) {
+                              int k, float scale, void* ws, hipStream_t st, const Paging* pg) {
     AttnArgs a = {};
+    if (pg) {
+        if (!comp_idx) return hipErrorInvalidValue;  // paged: sparse mode only
+        a.pg_swa = pg->swa;
+        a.pg_c4 = pg->c4;
+        a.pos = pg->pos;
+    }
     a.q = q;
     a.win = swa_kv;
     a.swa_len = swa_len;
@@ -1217,8 +1241,13 @@ hipError_t launch_attn_decode_fused(int dtype, const void* q, const void* swa_kv
                                     const int32_t* comp_len, const int32_t* n_cand, void* sel_ws,
                                     const float* scores, int32_t* topk_out, void* out, float* lse, int B, int H,
                                     int d_qk, int d_v, int W, int S_max, int k, float scale,
-                                    void* ws, hipStream_t st) {
+                                    void* ws, hipStream_t st, const Paging* pg) {
     AttnArgs a = {};
+    if (pg) {
+        a.pg_swa = pg->swa;
+        a.pg_c4 = pg->c4;
+        a.pos = pg->pos;
+    }
     a.q = q;
     a.win = swa_kv;
     a.swa_len = swa_len;

@@ -472,6 +472,16 @@ hipError_t launch_append_short(const void* x_tok, const void* g_tok, const void*
     return hipGetLastError();
 }
 
+// the paged C4 append (append_short_chunk_paged), one thread per chunk
+template <typename T>
+__global__ __launch_bounds__(kAppendThreads) void compress_append_paged_kernel(AppendJob job) {
+    append_short_chunk_paged<T, 4>(
+        static_cast<const T*>(job.x_tok), static_cast<const T*>(job.g_tok),
+        static_cast<const T*>(job.bias), static_cast<T*>(job.ring_x), static_cast<T*>(job.ring_g),
+        job.pos, static_cast<T*>(job.pool), job.D, job.S_max, job.swa, job.c4, blockIdx.x,
+        blockIdx.y * kAppendThreads + threadIdx.x);
+}
+
 // rows folded per thread: enough parts that each holds about kAppendRows rows
 int append_parts(int m) {
     int want = std::min(32, (m + kAppendRows - 1) / kAppendRows);
@@ -513,6 +523,17 @@ hipError_t launch_compress_append(int dtype, const void* x_tok, const void* g_to
                                                D, m, S_max, st);
     return launch_compress_append_t<bf16_t>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D,
                                             m, S_max, st);
+}
+
+hipError_t launch_compress_append_paged(int dtype, const AppendJob& job, hipStream_t st) {
+    const int nchunk = job.D * (dtype == kF32 ? 4 : 2) / 16;
+    const dim3 grid((unsigned)job.B, (unsigned)((nchunk + kAppendThreads - 1) / kAppendThreads));
+    ProfScope prof(kProfCompress, st);
+    if (dtype == kF32)
+        hipLaunchKernelGGL(compress_append_paged_kernel<float>, grid, dim3(kAppendThreads), 0, st, job);
+    else
+        hipLaunchKernelGGL(compress_append_paged_kernel<bf16_t>, grid, dim3(kAppendThreads), 0, st, job);
+    return hipGetLastError();
 }
 
 hipError_t launch_compress(int dtype, const void* x, const void* g, const void* bias, void* out,

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "hsa_common.hpp"
+#include "hsa_internal.hpp"
 
 namespace hsa {
 
@@ -95,6 +96,66 @@ __device__ __forceinline__ void append_short_chunk(const T* x_tok, const T* g_to
     }
     *reinterpret_cast<u32x4*>(pool + ((size_t)b * S_max + blk) * D + (size_t)c * V) =
         pack16<T>(res);
+}
+
+// The same append on paged pools ([KD "Arquitectura del Sistema",
+// ShadowRadix]: the compression-state rings form a pool of their own, reached
+// from the SWA page by an arithmetic second-level map).  Token t's latent and
+// gate logits are state rows of the SWA row of t (physical row of t in the SWA
+// shadow `swa`); since 4 divides the page size a block's M <= 4 tokens share
+// one page.  The token at position p = pos[b] is stored at its row; when it
+// completes block i = p div M, the entry formed from the rows of tokens
+// p-M+1 .. p goes to row i of the C4 shadow `c4` if i < S_max.  Rows that are
+// not resident are neither read nor written (the token or entry is dropped).
+template <typename T, int M>
+__device__ __forceinline__ void append_short_chunk_paged(const T* x_tok, const T* g_tok,
+                                                         const T* bias, T* state_x, T* state_g,
+                                                         const int32_t* pos, T* pool, int D,
+                                                         int S_max, const PoolMap& swa,
+                                                         const PoolMap& c4, int b, int c) {
+    constexpr int V = Elem<T>::kPer16B;
+    if (c >= D / V) return;  // a chunk past the row
+    const size_t tok = (size_t)b * D + (size_t)c * V;
+    const u32x4 xt = *reinterpret_cast<const u32x4*>(x_tok + tok);
+    const u32x4 gt = *reinterpret_cast<const u32x4*>(g_tok + tok);
+    const int p = pos[b];
+    if (p < 0) return;  // idle sequence
+    const long long sr = paged_row(swa, b, p);
+    if (sr < 0) return;
+    *reinterpret_cast<u32x4*>(state_x + (size_t)sr * D + (size_t)c * V) = xt;
+    *reinterpret_cast<u32x4*>(state_g + (size_t)sr * D + (size_t)c * V) = gt;
+    const int blk = p / M;
+    if (p % M != M - 1 || blk >= S_max) return;
+    const long long er = paged_row(c4, b, blk);
+    if (er < 0) return;
+    u32x4 xw[M], gw[M], bw[M];  // row M-1 is the token; rows before it are sr-M+1 .. sr-1
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        const size_t row = (size_t)(sr - (M - 1) + r) * D + (size_t)c * V;
+        gw[r] = r == M - 1 ? gt : *reinterpret_cast<const u32x4*>(state_g + row);
+        xw[r] = r == M - 1 ? xt : *reinterpret_cast<const u32x4*>(state_x + row);
+        bw[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)r * D + (size_t)c * V);
+    }
+    float res[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float z[M];
+#pragma unroll
+        for (int r = 0; r < M; ++r)
+            z[r] = (chunk_elem<T>(gw[r], e) + chunk_elem<T>(bw[r], e)) * kLog2e;
+        float gm = z[0];
+#pragma unroll
+        for (int r = 1; r < M; ++r) gm = fmaxf(gm, z[r]);
+        float sm = 0.f, acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+            const float w = exp2f(z[r] - gm);
+            sm += w;
+            acc = fmaf(w, chunk_elem<T>(xw[r], e), acc);
+        }
+        res[e] = acc / sm;
+    }
+    *reinterpret_cast<u32x4*>(pool + (size_t)er * D + (size_t)c * V) = pack16<T>(res);
 }
 
 }  // namespace hsa

@@ -114,11 +114,14 @@ __device__ __forceinline__ float reduce_scatter8(float (&v)[8], int sub) {
 // (select.hpp), and grid rows y >= Nq carry the
 // decode-time C4 append of `job` (one (sequence, 256-chunk span) per
 // workgroup; it touches only the append's own buffers).
-template <typename T, int LPR, int SEL>
+// PAGED: k_idx is the paged indexer-key pool of shadow kp (row s of sequence
+// b at its physical row; a row that is not resident scores NaN).
+constexpr int kScorePagesMax = 8192 / 16 + 1;  // logical pages a scoring workgroup spans
+template <typename T, int LPR, int SEL, bool PAGED>
 __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ n_cand, float* __restrict__ scores, uint8_t* __restrict__ ws,
-    int B, int H_I, int S_max, int k, int rows_per_wg, int Nq, AppendJob job) {
+    int B, int H_I, int S_max, int k, int rows_per_wg, int Nq, AppendJob job, PoolMap kp) {
     constexpr bool HIST = SEL >= 1;
     constexpr bool LIST = SEL >= 2;
     // log2 of the rows per list slot: fixed at 2048 for SEL 2 (so that the
@@ -138,18 +141,27 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     __shared__ uint32_t hist[HIST ? kBins : 1];
     __shared__ uint32_t scan_tmp[LIST ? kNW + 2 : 1];
     __shared__ uint32_t cut_res;
+    __shared__ int spg[PAGED ? kScorePagesMax : 1];  // physical page of each logical page, -1 absent
     extern __shared__ __align__(16) float stage[];  // this workgroup's scores (rows_per_wg)
 
     if constexpr (LIST) {
         if ((int)blockIdx.y >= Nq) {
             const int spans = (job.D / Elem<T>::kPer16B + kThreads - 1) / kThreads;
             const int j = ((int)blockIdx.y - Nq) * (int)gridDim.x + (int)blockIdx.x;
-            if (j < job.B * spans)
-                append_short_chunk<T, 4>(
-                    static_cast<const T*>(job.x_tok), static_cast<const T*>(job.g_tok),
-                    static_cast<const T*>(job.bias), static_cast<T*>(job.ring_x),
-                    static_cast<T*>(job.ring_g), job.pos, static_cast<T*>(job.pool), job.D,
-                    job.S_max, j / spans, (j % spans) * kThreads + threadIdx.x);
+            if (j < job.B * spans) {
+                if (job.swa.map)  // uniform: the paged state pools
+                    append_short_chunk_paged<T, 4>(
+                        static_cast<const T*>(job.x_tok), static_cast<const T*>(job.g_tok),
+                        static_cast<const T*>(job.bias), static_cast<T*>(job.ring_x),
+                        static_cast<T*>(job.ring_g), job.pos, static_cast<T*>(job.pool), job.D,
+                        job.S_max, job.swa, job.c4, j / spans, (j % spans) * kThreads + threadIdx.x);
+                else
+                    append_short_chunk<T, 4>(
+                        static_cast<const T*>(job.x_tok), static_cast<const T*>(job.g_tok),
+                        static_cast<const T*>(job.bias), static_cast<T*>(job.ring_x),
+                        static_cast<T*>(job.ring_g), job.pos, static_cast<T*>(job.pool), job.D,
+                        job.S_max, j / spans, (j % spans) * kThreads + threadIdx.x);
+            }
             return;
         }
     }
@@ -161,13 +173,40 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)sub * V;
     const int r0 = blockIdx.x * rows_per_wg;
     const int r1m = min(S_max, r0 + rows_per_wg);  // rows that are valid memory
+    // paged: the shadow entries of this workgroup's rows (logical pages j0 ..)
+    const int j0 = PAGED ? r0 >> kp.lg : 0;
+    if constexpr (PAGED) {
+        const int np = ((r1m - 1) >> kp.lg) - j0 + 1;
+        for (int i = tid; i < np; i += kThreads) {
+            const int j = j0 + i;
+            const int pg = j < kp.pages ? kp.map[(size_t)bseq * kp.pages + j] : -1;
+            spg[i] = (pg >= 0 && pg < kp.pool_pages) ? pg : -1;
+        }
+        __syncthreads();
+    }
+    // this lane's chunk of key row r (r < r1m); a row that is not resident reads
+    // physical row 0 (its score is replaced by NaN)
+    auto krow = [&](int r) -> const T* {
+        if constexpr (PAGED) {
+            const int pg = spg[(r >> kp.lg) - j0];
+            const size_t pr = pg < 0 ? 0 : (((size_t)pg << kp.lg) | (size_t)(r & ((1 << kp.lg) - 1)));
+            return k_idx + pr * DI + (size_t)sub * V;
+        } else {
+            return kbase + (size_t)r * DI;
+        }
+    };
 
     // Key rows are read once: nontemporal loads keep them from displacing
     // reusable lines.  Load u of batch bi: the 256 lanes read RPU consecutive
     // rows (4 KB), wave w the w-th quarter.  Full batches need no clamp.
     auto load_batch = [&](u32x4 (&buf)[U], int bi, int rlim) {
         const int rb = r0 + bi * RPB;
-        if (rb + RPB <= rlim) {
+        if (PAGED && rb + RPB <= rlim) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                buf[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(krow(rb + u * RPU + w * RPL + rs)));
+        } else if (rb + RPB <= rlim) {
             const T* p = kbase + (size_t)(rb + w * RPL + rs) * DI;
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -177,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
             for (int u = 0; u < U; ++u) {
                 const int r = rb + u * RPU + w * RPL + rs;
                 const int rc = r < rlim ? r : rlim - 1;  // stay inside the valid rows
-                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)rc * DI));
+                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc)));
             }
         }
     };
@@ -201,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * RPU + w * RPL + rs;
             const int rc = r < r1m ? r : r1m - 1;
-            cur[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (size_t)rc * DI));
+            cur[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc)));
         }
     }
     if constexpr (HIST) clear_hist2_slice(ws, q, S_max, k);
@@ -283,8 +322,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
             for (int e = 0; e < V; ++e) acc = fmaf(qv[e], kv[e], acc);
             d[u] = acc;
         }
-        const float sc = reduce_scatter8<LPR>(d, sub);
+        float sc = reduce_scatter8<LPR>(d, sub);
         const int r = r0 + bi * RPB + my_u * RPU + w * RPL + rs;
+        if constexpr (PAGED) {
+            if (r < r1 && spg[(r >> kp.lg) - j0] < 0) sc = __builtin_nanf("");
+        }
         if (writer && r < r1) {
             stage[r - r0] = sc;
             if constexpr (HIST) atomicAdd(&hist[score_key(sc) >> 21], 1u);
@@ -993,10 +1035,26 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
     select_zero<kThreads>(W, S_max, segc, tmp);
 }
 
+template <typename T, int LPR, int SEL>
+void launch_score_sel(dim3 grid, size_t lds, hipStream_t st, const void* q_idx, const void* k_idx,
+                      const int32_t* q_seq, const int32_t* n_cand, float* scores, uint8_t* ws,
+                      int B, int H_I, int S_max, int k, int rows, int Nq, const AppendJob& aj,
+                      const PoolMap* kp) {
+    if (kp && kp->map)
+        hipLaunchKernelGGL((score_kernel<T, LPR, SEL, true>), grid, dim3(kThreads), lds, st,
+                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
+                           S_max, k, rows, Nq, aj, *kp);
+    else
+        hipLaunchKernelGGL((score_kernel<T, LPR, SEL, false>), grid, dim3(kThreads), lds, st,
+                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
+                           S_max, k, rows, Nq, aj, PoolMap{});
+}
+
 template <typename T, int LPR>
 hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32_t* q_seq,
                         const int32_t* n_cand, float* scores, uint8_t* ws, int Nq, int H_I,
-                        int S_max, int k, int sel, const AppendJob* job, hipStream_t st) {
+                        int S_max, int k, int sel, const AppendJob* job, hipStream_t st,
+                        const PoolMap* kp) {
     const int rows_lg = list_rows_log2(S_max, Nq);
     if (sel == 2 && rows_lg != 11) sel = 3;  // smaller slots: the variable-slot instantiation
     const int rows = sel >= 2 ? (1 << rows_lg) : sel ? kScoreRowsMulti : min(S_max, 8192);
@@ -1010,21 +1068,13 @@ hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32
     const size_t lds = (size_t)rows * sizeof(float);  // staged scores
     ProfScope prof(kProfScore, st);
     if (sel == 3)
-        hipLaunchKernelGGL((score_kernel<T, LPR, 3>), grid, dim3(kThreads), lds, st,
-                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows, Nq, aj);
+        launch_score_sel<T, LPR, 3>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
     else if (sel == 2)
-        hipLaunchKernelGGL((score_kernel<T, LPR, 2>), grid, dim3(kThreads), lds, st,
-                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows, Nq, aj);
+        launch_score_sel<T, LPR, 2>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
     else if (sel == 1)
-        hipLaunchKernelGGL((score_kernel<T, LPR, 1>), grid, dim3(kThreads), lds, st,
-                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows, Nq, aj);
+        launch_score_sel<T, LPR, 1>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
     else
-        hipLaunchKernelGGL((score_kernel<T, LPR, 0>), grid, dim3(kThreads), lds, st,
-                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows, Nq, aj);
+        launch_score_sel<T, LPR, 0>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
     return hipGetLastError();
 }
 
@@ -1032,13 +1082,13 @@ template <typename T>
 hipError_t launch_score_t(int d_I, const void* q_idx, const void* k_idx, int B,
                           const int32_t* q_seq, const int32_t* n_cand, float* scores, uint8_t* ws,
                           int Nq, int H_I, int S_max, int k, int sel, const AppendJob* job,
-                          hipStream_t st) {
+                          hipStream_t st, const PoolMap* kp) {
     const int lpr = d_I * (int)sizeof(T) / 16;
     if (lpr == 8)
-        return launch_score<T, 8>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st);
+        return launch_score<T, 8>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp);
     if (lpr == 16)
-        return launch_score<T, 16>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st);
-    return launch_score<T, 32>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st);
+        return launch_score<T, 16>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp);
+    return launch_score<T, 32>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp);
 }
 
 // Zero the first-digit histogram of every query (a scoring launch whose select
@@ -1089,25 +1139,27 @@ bool index_lists_apply(int S_max, int k, int Nq) { return lists_apply(S_max, k, 
 
 hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
-                              int S_max, int k, void* ws, const AppendJob* job, hipStream_t st) {
+                              int S_max, int k, void* ws, const AppendJob* job, hipStream_t st,
+                              const PoolMap* kI) {
     uint8_t* w = static_cast<uint8_t*>(ws);
     return dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
-                                                  Nq, H_I, S_max, k, 2, job, st)
+                                                  Nq, H_I, S_max, k, 2, job, st, kI)
                          : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
-                                                   Nq, H_I, S_max, k, 2, job, st);
+                                                   Nq, H_I, S_max, k, 2, job, st, kI);
 }
 
 hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, int B,
                              const int32_t* q_seq, const int32_t* n_cand, float* scores,
                              int32_t* topk_idx, int Nq, int H_I, int d_I, int S_max, int k,
-                             void* ws, hipStream_t st) {
+                             void* ws, hipStream_t st, const PoolMap* kI) {
+    const bool paged = kI && kI->map;
     const bool multi = S_max > kRowSelectCap;
     uint8_t* w = static_cast<uint8_t*>(ws);
     hipError_t e = hipSuccess;
     // the select treats a query routed outside [0, B) as one without candidates
     // (select-only mode has no key sequences: q_seq is ignored there)
     const int32_t* sel_seq = q_idx ? q_seq : nullptr;
-    if (q_idx && !multi && dtype == kBF16 && Nq >= kGemmMinQueries &&
+    if (q_idx && !multi && !paged && dtype == kBF16 && Nq >= kGemmMinQueries &&
         (d_I == 64 || d_I == 128 || d_I == 256)) {
         ProfScope prof(kProfScore, st);
         const dim3 grid((unsigned)ceil_div(Nq, kGemmQ));
@@ -1125,9 +1177,9 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (q_idx) {
         e = dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores, w,
-                                                   Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st)
+                                                   Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st, kI)
                           : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores,
-                                                   w, Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st);
+                                                   w, Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st, kI);
         if (e != hipSuccess) return e;
     } else if (multi) {
         dim3 grid((unsigned)ceil_div(S_max, kFilterChunk), (unsigned)Nq);

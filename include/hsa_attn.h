@@ -321,6 +321,92 @@ int hsa_decode_step_noalloc(int dtype, const void *x_tok, const void *g_tok, con
                             float scale, void *stream);
 
 /*
+ * Paged pools: the shadows of one decode call.
+ *
+ * [KD "Arquitectura del Sistema", ShadowRadix]: virtual full-token slots are
+ * projected onto the physical KV pools (SWA, C4, C128) through one index map
+ * per pool, so each pool's lifetime is its own (SWA pages are freed once the
+ * window has passed them while the C4 rows stay); the compression-state rings
+ * form a pool of their own, reached from the SWA page index by arithmetic.
+ * [NK "推理侧优化", shadow radix cache bullet]: one list of virtual addresses
+ * per state class; the part of the SWA no longer used is deleted from physical
+ * memory and only its index is kept.
+ *
+ * A paged pool is an array of physical pages of P rows ([pool_pages, P, D]).
+ * Row r of sequence b lives at physical page map[b * map_pages + r / P], row
+ * r mod P.  A logical page at or past map_pages, or a map entry outside
+ * [0, pool_pages) (for example -1 for a freed page), is not resident: its rows
+ * do not exist.  SWA rows are indexed by token position; C4 KV and indexer-key
+ * rows by C4 entry.  The compression state of token t (its latent and gate
+ * logits, while its block is open) is kept in two state pools shaped like the
+ * SWA pool, at the physical row of t in the SWA shadow.
+ *
+ *   swa_map      : [B, swa_map_pages] int32 device memory
+ *   swa_page_rows: P of the SWA and state pools, a power of two in [16, 4096]
+ *   swa_pool_pages: physical pages of the SWA pool (and of each state pool)
+ *   c4_map       : [B, c4_map_pages] int32, shadow of the C4 KV pool
+ *   kI_map       : [B, c4_map_pages] int32, shadow of the indexer-key pool (it
+ *                  may be the same array as c4_map)
+ *   c4_page_rows : P of the C4 KV and indexer-key pools, a power of two in
+ *                  [16, 4096]; c4_map_pages * c4_page_rows >= S_max
+ *   c4_pool_pages, kI_pool_pages: physical pages of those two pools
+ * The struct is read on the host during the call; the maps it points to are
+ * read by the kernels.
+ */
+typedef struct {
+    const int32_t *swa_map;
+    int32_t swa_map_pages, swa_page_rows, swa_pool_pages;
+    const int32_t *c4_map;
+    const int32_t *kI_map;
+    int32_t c4_map_pages, c4_page_rows, c4_pool_pages, kI_pool_pages;
+} hsa_page_maps;
+
+/*
+ * hsa_decode_step_paged -- hsa_decode_step (or, with x_tok == NULL,
+ * hsa_decode_sparse) on paged pools: the same computation with every row
+ * reached through its shadow.
+ *
+ * For sequence b with p = pos[b] (the position of its query token; p < 0: no
+ * token this step):
+ *   1. append (x_tok != NULL, p >= 0): the token's latent and gate logits are
+ *      stored at its state rows; if p mod 4 == 3 and i = p div 4 < S_max, C4
+ *      entry i = sum_j softmax_j(g_j + bias_j) * x_j over tokens p-3 .. p
+ *      (their state rows) is written to row i of the C4 pool.  A token whose
+ *      SWA row is not resident is not stored; an entry whose C4 row is not
+ *      resident is not written.
+ *   2. scores[b, s] for s < n_cand[b]: as hsa_index_topk on indexer-key row s
+ *      of the kI shadow; a row that is not resident scores NaN (ranks last).
+ *   3. top-k select: as hsa_index_topk.
+ *   4. attention: as hsa_attn_decode (sparse mode) over the window -- the
+ *      n = clamp(swa_len[b], 0, W) tokens p-n+1 .. p, none when p < 0 -- and
+ *      the selected C4 rows i < comp_len[b]; rows that are not resident are
+ *      skipped.
+ * With identity shadows over pools holding the flat layout (and the window
+ * ring holding token p-n+1+j in slot j) the results equal hsa_decode_step's
+ * bit for bit: only the row addresses differ.
+ *
+ *   state_x, state_g : [swa_pool_pages, swa_page_rows, d_qk] dtype in/out
+ *                      (ignored when x_tok is NULL)
+ *   kI_pool  : [kI_pool_pages, c4_page_rows, d_I] dtype
+ *   swa_pool : [swa_pool_pages, swa_page_rows, d_qk] dtype (the caller stores
+ *              each token's KV latent at its SWA row before the call)
+ *   c4_pool  : [c4_pool_pages, c4_page_rows, d_qk] dtype (in/out)
+ *   pos      : [B] int32, required
+ *   maps     : host pointer to the shadows (above)
+ *   Other arguments, limits and workspace: as hsa_decode_step;
+ *   HSA_ERR_INVALID_ARG for a bad map description.
+ */
+int hsa_decode_step_paged(int dtype, const void *x_tok, const void *g_tok, const void *bias,
+                          void *state_x, void *state_g, const int32_t *pos, const void *q_idx,
+                          const void *kI_pool, const int32_t *n_cand, float *scores,
+                          int32_t *topk_idx, const void *q, const void *swa_pool,
+                          const int32_t *swa_len, void *c4_pool, const int32_t *comp_len,
+                          const hsa_page_maps *maps, void *out, float *lse, int32_t B,
+                          int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v,
+                          int32_t W, int32_t S_max, int32_t k, float scale, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * hsa_attn_prefill -- a chunk of n_q consecutive query positions per
  * sequence, each with its own causal SWA window and its own compressed rows.
  *

@@ -157,3 +157,33 @@ def test_decode_step_noalloc_rejects(hsa):
     assert call(x_tok=None) == 1
     assert call(comp=MIS) == 1
     assert call(k=0) == 1
+
+
+def test_decode_step_paged_rejects_bad_shadows(hsa):
+    """The paged step checks its map description on the host: page sizes that
+    are not powers of two in [16, 4096], empty maps or pools, a C4 shadow too
+    short for S_max, missing maps or positions (HSA_ERR_INVALID_ARG, nothing
+    launched)."""
+    lib = hsa.lib
+    from hybrid_sparse_compressed_amd._binding import PageMaps
+
+    def call(maps=True, pos=A, **kw):
+        m = dict(swa_map=A.value, swa_map_pages=8, swa_page_rows=16, swa_pool_pages=4, c4_map=A.value,
+                 kI_map=A.value, c4_map_pages=64, c4_page_rows=256, c4_pool_pages=300,
+                 kI_pool_pages=300)
+        m.update(kw)
+        pm = PageMaps(**m)
+        ptrs = [A, A, A, A, A, pos, A, A, A, A, A, A, A, A, A, A]
+        return lib.hsa_decode_step_paged(1, *ptrs, ctypes.byref(pm) if maps else None, A, A, 4, 64,
+                                         128, 64, 576, 512, 128, 16384, 512, 0.04, None, 0, None)
+
+    assert call(swa_page_rows=24) == 1
+    assert call(swa_page_rows=8) == 1
+    assert call(c4_page_rows=8192) == 1
+    assert call(c4_map_pages=63) == 1      # 63 * 256 rows < S_max = 16384
+    assert call(swa_map_pages=0) == 1
+    assert call(kI_pool_pages=0) == 1
+    assert call(c4_map=None) == 1
+    assert call(maps=False) == 1
+    assert call(pos=None) == 1
+    assert call() == 3                     # well-formed: only the workspace is missing
