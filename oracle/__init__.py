@@ -58,11 +58,13 @@ def _load():
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.oracle_compress.argtypes = [I, P, P, P, P, I, I, I, I]
         lib.oracle_index_scores.argtypes = [I, P, P, P, P, P, I, I, I, I, I]
+        lib.oracle_index_scores_weighted.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I]
         lib.oracle_topk.argtypes = [P, P, P, I, I, I]
         lib.oracle_attn_decode.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D]
         lib.oracle_attn_prefill.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I,
                                             I, D, P, I]
-        for f in (lib.oracle_compress, lib.oracle_index_scores, lib.oracle_topk,
+        for f in (lib.oracle_compress, lib.oracle_index_scores, lib.oracle_index_scores_weighted,
+                  lib.oracle_topk,
                   lib.oracle_attn_decode, lib.oracle_attn_prefill):
             f.restype = I
         _lib = lib
@@ -174,6 +176,26 @@ def index_scores(q_idx, k_idx, n_cand, q_seq=None):
     out = np.empty((Nq, S_max), dtype=np.float64)
     _check(_load().oracle_index_scores(et, _p(qa), _p(ka), _p(qs), _p(nc), _p(out), Nq, B, H_I,
                                        d_I, S_max), "index_scores")
+    return out
+
+
+def index_scores_weighted(q_idx, w, k_idx, n_cand, q_seq=None):
+    """Weighted, activated indexer heads (method variant):
+    sum_h w[q,h] * max(0, q_idx[q,h,:] . k_idx[seq(q),s,:]).
+
+    q_idx: [Nq, H_I, d_I]; w: [Nq, H_I] (taken as fp32); k_idx: [B, S_max, d_I];
+    n_cand: [Nq] -> float64 [Nq, S_max], NaN where s >= n_cand[q]."""
+    et, (qa, ka) = _same_et(q_idx, k_idx)
+    Nq, H_I, d_I = qa.shape
+    B, S_max, d2 = ka.shape
+    wa = np.ascontiguousarray(np.asarray(w.float() if hasattr(w, "float") else w, dtype=np.float32))
+    if d2 != d_I or wa.shape != (Nq, H_I):
+        raise ValueError("index_scores_weighted: shape mismatch")
+    nc, qs = _i32(n_cand), _i32(q_seq)
+    out = np.empty((Nq, S_max), dtype=np.float64)
+    _check(_load().oracle_index_scores_weighted(et, _p(qa), _p(wa), _p(ka), _p(qs), _p(nc),
+                                                _p(out), Nq, B, H_I, d_I, S_max),
+           "index_scores_weighted")
     return out
 
 

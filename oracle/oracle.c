@@ -153,6 +153,53 @@ int oracle_index_scores(int et, const void *q_idx, const void *k_idx,
 }
 
 /* ------------------------------------------------------------------------ *
+ * Indexer scores, weighted and activated heads (method variant).
+ *
+ * [KD "Arquitectura del Sistema"] names a DSA indexer; [NK "RL 训练侧"]
+ * likens the attention indexer to an MoE router, whose gate weighs each of
+ * its experts.  The pages define no head combination.  Reading for this
+ * variant (the DSA indexer as published with DeepSeek-V3.2): every head's dot
+ * product passes a ReLU, and the heads are summed with per-query weights:
+ *   score[q, s] = sum_h w[q, h] * max(0, sum_e q_idx[q, h, e] * k_idx[seq(q), s, e])
+ * for s < n_cand[q]; other entries NaN.
+ *
+ * w: [Nq, H_I] fp32; the rest as oracle_index_scores.
+ * ------------------------------------------------------------------------ */
+int oracle_index_scores_weighted(int et, const void *q_idx, const float *w,
+                                 const void *k_idx, const int32_t *q_seq,
+                                 const int32_t *n_cand, double *scores, int Nq, int B,
+                                 int H_I, int d_I, int S_max)
+{
+    if (bad_et(et) || !q_idx || !w || !k_idx || !n_cand || !scores) return 1;
+    if (Nq < 0 || B < 1 || H_I < 1 || d_I < 1 || S_max < 0) return 1;
+    for (int q = 0; q < Nq; ++q) {
+        int b = q_seq ? q_seq[q] : q;
+        if (b < 0 || b >= B) return 2;
+        if (n_cand[q] < 0 || n_cand[q] > S_max) return 2;
+    }
+    long units = (long)Nq * S_max;
+#pragma omp parallel for schedule(static)
+    for (long u = 0; u < units; ++u) {
+        const int q = (int)(u / (S_max ? S_max : 1)), s = (int)(u % (S_max ? S_max : 1));
+        const int b = q_seq ? q_seq[q] : q;
+        if (s >= n_cand[q]) {
+            scores[u] = NAN;
+            continue;
+        }
+        double acc = 0.0;
+        for (int h = 0; h < H_I; ++h) {
+            double dot = 0.0;
+            for (int e = 0; e < d_I; ++e)
+                dot += ld(q_idx, et, ((size_t)q * H_I + h) * d_I + e) *
+                       ld(k_idx, et, ((size_t)b * S_max + s) * d_I + e);
+            acc += (double)w[(size_t)q * H_I + h] * (dot > 0.0 ? dot : 0.0);
+        }
+        scores[u] = acc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ *
  * Top-k selection.
  *
  * [KD "Arquitectura del Sistema"] top-k in the indexer picks candidates
