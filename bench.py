@@ -425,8 +425,21 @@ def paged_step_rows(hsa, workloads, torch):
         out=o, lse=l), 7, 20)
     alg = (B * S * 128 * 2 + B * (W + k) * D * 2 + B * H * D * 2 + B * H * 512 * 2
            + B * 64 * 128 * 2 + B * k * 4)
-    return {"f2_decode_step_paged_c4_1m": _row("c4_decode_1m", us, "hbm", alg, "GB/s", HBM_PEAK_GBPS,
+    rows = {"f2_decode_step_paged_c4_1m": _row("c4_decode_1m", us, "hbm", alg, "GB/s", HBM_PEAK_GBPS,
                                                flat_us=round(flat_us, 2), page_rows={"swa": P, "c4": 256})}
+    # the weighted, activated indexer heads (MFMA per head) on the same workload,
+    # without the append, next to the unit-weight call
+    hw = (torch.rand((B, 64), generator=g) * 2.0 - 0.3).float().cuda()
+    wus = _median_us(torch, lambda: hsa.hsa_decode_sparse_weighted(
+        w["q_idx"], hw, w["k_idx"], w["n_cand"], k, w["q"], w["swa_kv"], w["swa_len"], w["comp_kv"],
+        w["comp_len"], w["scale"], 512, scores=sc, topk_idx=ix, out=o, lse=l), 7, 20)
+    uus = _median_us(torch, lambda: hsa.hsa_decode_sparse(
+        w["q_idx"], w["k_idx"], w["n_cand"], k, w["q"], w["swa_kv"], w["swa_len"], w["comp_kv"],
+        w["comp_len"], w["scale"], 512, scores=sc, topk_idx=ix, out=o, lse=l), 7, 20)
+    rows["f3_decode_sparse_weighted_heads_c4_1m"] = _row(
+        "c4_decode_1m", wus, "hbm", alg, "GB/s", HBM_PEAK_GBPS, unit_weight_us=round(uus, 2),
+        mfma_tflop=round(B * S * 64 * 128 * 2 / 1e12, 4))
+    return rows
 
 
 def append_rows(hsa, torch):

@@ -25,7 +25,8 @@ EXPORTED = (
     "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
     "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
     "hsa_decode_sparse", "hsa_decode_step", "hsa_decode_step_noalloc", "hsa_decode_step_paged",
-    "hsa_profile_enable", "hsa_profile_read",
+    "hsa_index_topk_weighted", "hsa_decode_sparse_weighted", "hsa_profile_enable",
+    "hsa_profile_read",
 )
 HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
 
@@ -82,6 +83,11 @@ def _load():
     lib.hsa_decode_step_paged.argtypes = [I] + [P] * 16 + [ctypes.POINTER(PageMaps), P, P] + \
         [I32] * 9 + [F, P, SZ, P]
     lib.hsa_decode_step_paged.restype = I
+    lib.hsa_index_topk_weighted.argtypes = [I, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, P,
+                                            SZ, P]
+    lib.hsa_index_topk_weighted.restype = I
+    lib.hsa_decode_sparse_weighted.argtypes = [I] + [P] * 13 + [I32] * 9 + [F, P, SZ, P]
+    lib.hsa_decode_sparse_weighted.restype = I
     lib.hsa_attn_prefill_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.hsa_attn_prefill_workspace_size.restype = SZ
     lib.hsa_attn_prefill.argtypes = [I, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
@@ -224,6 +230,19 @@ def hsa_index_topk(q_idx, k_idx, n_cand, k, q_seq=None, scores=None, topk_idx=No
 
     q_idx: [Nq, H_I, d_I]; k_idx: [B, S_max, d_I]; n_cand: [Nq] int32.
     Returns (scores [Nq, S_max] fp32, topk_idx [Nq, k] int32)."""
+    return _index_topk(q_idx, None, k_idx, n_cand, k, q_seq, scores, topk_idx, workspace, stream)
+
+
+def hsa_index_topk_weighted(q_idx, head_w, k_idx, n_cand, k, q_seq=None, scores=None,
+                            topk_idx=None, workspace=None, stream=None):
+    """hsa_index_topk with weighted, activated heads: head_w [Nq, H_I] fp32 (device),
+    score = sum_h head_w[q, h] * max(0, q_idx[q, h] . k).  bf16, d_I = 128."""
+    if head_w is None or head_w.dtype != torch.float32 or tuple(head_w.shape) != tuple(q_idx.shape[:2]):
+        raise ValueError("hsa_index_topk_weighted: head_w must be fp32 [Nq, H_I]")
+    return _index_topk(q_idx, head_w, k_idx, n_cand, k, q_seq, scores, topk_idx, workspace, stream)
+
+
+def _index_topk(q_idx, head_w, k_idx, n_cand, k, q_seq, scores, topk_idx, workspace, stream):
     if q_idx is not None:
         Nq, H_I, d_I = q_idx.shape
         B, S_max, d2 = k_idx.shape
@@ -250,10 +269,16 @@ def hsa_index_topk(q_idx, k_idx, n_cand, k, q_seq=None, scores=None, topk_idx=No
     if cached:
         workspace = Workspace.get("topk", need, dev, st)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call_with_workspace("hsa_index_topk", lambda: lib.hsa_index_topk(
-        dt, _ptr(q_idx), _ptr(k_idx), B, _ptr(q_seq), _ptr(n_cand), _ptr(scores),
-        _ptr(topk_idx), Nq, H_I, d_I, S_max, k, 0, _ptr(workspace), wsz, _stream(st)),
-        workspace, cached)
+    if head_w is None:
+        _call_with_workspace("hsa_index_topk", lambda: lib.hsa_index_topk(
+            dt, _ptr(q_idx), _ptr(k_idx), B, _ptr(q_seq), _ptr(n_cand), _ptr(scores),
+            _ptr(topk_idx), Nq, H_I, d_I, S_max, k, 0, _ptr(workspace), wsz, _stream(st)),
+            workspace, cached)
+    else:
+        _call_with_workspace("hsa_index_topk_weighted", lambda: lib.hsa_index_topk_weighted(
+            dt, _ptr(q_idx), _ptr(head_w), _ptr(k_idx), B, _ptr(q_seq), _ptr(n_cand),
+            _ptr(scores), _ptr(topk_idx), Nq, H_I, d_I, S_max, k, _ptr(workspace), wsz,
+            _stream(st)), workspace, cached)
     return scores, topk_idx
 
 
@@ -292,6 +317,23 @@ def hsa_decode_sparse(q_idx, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp
 
     q_idx: [B, H_I, d_I]; k_idx: [B, S_max, d_I]; q: [B, H, d_qk]; swa_kv: [B, W, d_qk];
     comp_kv: [B, S_max, d_qk].  Returns (scores, topk_idx, out, lse)."""
+    return _decode_sparse(q_idx, None, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp_len,
+                          scale, d_v, scores, topk_idx, out, lse, workspace, stream)
+
+
+def hsa_decode_sparse_weighted(q_idx, head_w, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv,
+                               comp_len, scale, d_v, scores=None, topk_idx=None, out=None,
+                               lse=None, workspace=None, stream=None):
+    """hsa_decode_sparse with the weighted, activated indexer heads of
+    hsa_index_topk_weighted (head_w [B, H_I] fp32)."""
+    if head_w is None or head_w.dtype != torch.float32 or tuple(head_w.shape) != tuple(q_idx.shape[:2]):
+        raise ValueError("hsa_decode_sparse_weighted: head_w must be fp32 [B, H_I]")
+    return _decode_sparse(q_idx, head_w, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp_len,
+                          scale, d_v, scores, topk_idx, out, lse, workspace, stream)
+
+
+def _decode_sparse(q_idx, head_w, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp_len, scale,
+                   d_v, scores, topk_idx, out, lse, workspace, stream):
     B, H_I, d_I = q_idx.shape
     _, S_max, _ = k_idx.shape
     _, H, d_qk = q.shape
@@ -317,11 +359,18 @@ def hsa_decode_sparse(q_idx, k_idx, n_cand, k, q, swa_kv, swa_len, comp_kv, comp
         workspace = Workspace.get("decode_sparse:%d:%d:%d:%d:%d" % (B, H, d_v, W, S_max * 4096 + k),
                                   need, dev, st)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call_with_workspace("hsa_decode_sparse", lambda: lib.hsa_decode_sparse(
-        _dt(q), _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
-        _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B, H_I,
-        d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)),
-        workspace, cached)
+    if head_w is None:
+        _call_with_workspace("hsa_decode_sparse", lambda: lib.hsa_decode_sparse(
+            _dt(q), _ptr(q_idx), _ptr(k_idx), _ptr(n_cand), _ptr(scores), _ptr(topk_idx), _ptr(q),
+            _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len), _ptr(out), _ptr(lse), B,
+            H_I, d_I, H, d_qk, d_v, W, S_max, k, float(scale), _ptr(workspace), wsz, _stream(st)),
+            workspace, cached)
+    else:
+        _call_with_workspace("hsa_decode_sparse_weighted", lambda: lib.hsa_decode_sparse_weighted(
+            _dt(q), _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _ptr(n_cand), _ptr(scores),
+            _ptr(topk_idx), _ptr(q), _ptr(swa_kv), _ptr(swa_len), _ptr(comp_kv), _ptr(comp_len),
+            _ptr(out), _ptr(lse), B, H_I, d_I, H, d_qk, d_v, W, S_max, k, float(scale),
+            _ptr(workspace), wsz, _stream(st)), workspace, cached)
     return scores, topk_idx, out, lse
 
 

@@ -102,6 +102,46 @@ int hsa_index_topk(int dtype, const void* q_idx, const void* k_idx, int32_t B,
     }
 }
 
+}  // extern "C"
+
+namespace {
+// Shape of the weighted, activated indexer heads: bf16, 128-wide keys, H_I a
+// multiple of 16 up to 64, fp32 weights 4-byte aligned.
+int weighted_heads_ok(int dtype, int32_t H_I, int32_t d_I, const float* head_w) {
+    if (!head_w || (reinterpret_cast<uintptr_t>(head_w) & 3u) != 0) return HSA_ERR_INVALID_ARG;
+    if (dtype != HSA_BF16 || d_I != 128 || H_I < 16 || H_I % 16 != 0 || H_I > 64)
+        return HSA_ERR_UNSUPPORTED;
+    return HSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int hsa_index_topk_weighted(int dtype, const void* q_idx, const float* head_w, const void* k_idx,
+                            int32_t B, const int32_t* q_seq, const int32_t* n_cand, float* scores,
+                            int32_t* topk_idx, int32_t Nq, int32_t H_I, int32_t d_I,
+                            int32_t S_max, int32_t k, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    try {
+        if (!q_idx || !dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!n_cand || !scores || !topk_idx || !k_idx) return HSA_ERR_INVALID_ARG;
+        if (Nq < 1 || B < 1 || H_I < 1 || d_I < 1 || S_max < 1 || k < 1 || k > hsa::kTopkMaxK)
+            return HSA_ERR_INVALID_ARG;
+        if (!aligned16(q_idx) || !aligned16(k_idx)) return HSA_ERR_INVALID_ARG;
+        if (!q_seq && Nq > B) return HSA_ERR_INVALID_ARG;
+        const int wok = weighted_heads_ok(dtype, H_I, d_I, head_w);
+        if (wok != HSA_OK) return wok;
+        if (S_max > hsa::kTopkMaxSegments * 4096) return HSA_ERR_UNSUPPORTED;
+        const size_t need = hsa::topk_workspace_bytes(Nq, S_max, k);
+        if (need > 0 && (!workspace || workspace_bytes < need)) return HSA_ERR_WORKSPACE;
+        return finish(hsa::launch_index_topk(dtype, q_idx, k_idx, B, q_seq, n_cand, scores,
+                                             topk_idx, Nq, H_I, d_I, S_max, k, workspace,
+                                             as_stream(stream), nullptr, head_w));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
 size_t hsa_attn_decode_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t max_rows) {
     if (B < 1 || H < 1 || d_v < 1 || max_rows < 1) return 0;
     return hsa::decode_workspace_bytes(B, H, d_v, max_rows);
@@ -156,7 +196,7 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
                        int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
                        float scale, void* workspace, size_t workspace_bytes, void* stream,
                        const hsa::AppendJob* job, bool clear_ws = false,
-                       const hsa::Paging* pg = nullptr) {
+                       const hsa::Paging* pg = nullptr, const float* head_w = nullptr) {
     // indexer + select arguments (as hsa_index_topk with Nq = B, no q_seq)
     if (!dtype_ok(dtype) || !q_idx || !k_idx || !n_cand || !scores || !topk_idx)
         return HSA_ERR_INVALID_ARG;
@@ -166,6 +206,10 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
     if (!aligned16(q_idx) || !aligned16(k_idx)) return HSA_ERR_INVALID_ARG;
     const int row_bytes = d_I * esize(dtype);
     if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512) return HSA_ERR_UNSUPPORTED;
+    if (head_w) {
+        const int wok = weighted_heads_ok(dtype, H_I, d_I, head_w);
+        if (wok != HSA_OK) return wok;
+    }
     // attention arguments (as hsa_attn_decode, sparse mode)
     if (!q || !swa_kv || !swa_len || !comp_kv || !comp_len || !out) return HSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(swa_kv) || !aligned16(out) || !aligned16(comp_kv))
@@ -196,7 +240,7 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
         // reads the pool; scoring never reads it
         hipError_t e = hsa::launch_index_lists(dtype, q_idx, k_idx, B, n_cand, scores, B, H_I,
                                                d_I, S_max, k, ws_sel, job, st,
-                                               pg ? &pg->kI : nullptr);
+                                               pg ? &pg->kI : nullptr, head_w);
         if (e != hipSuccess) return finish(e);
         e = hsa::launch_attn_decode_fused(dtype, q, swa_kv, swa_len, comp_kv, comp_len, n_cand,
                                           ws_sel, scores, topk_idx, out, lse, B, H, d_qk, d_v, W,
@@ -216,7 +260,7 @@ int decode_sparse_impl(int dtype, const void* q_idx, const void* k_idx, const in
     }
     hipError_t e = hsa::launch_index_topk(dtype, q_idx, k_idx, B, nullptr, n_cand, scores,
                                           topk_idx, B, H_I, d_I, S_max, k, ws_sel, st,
-                                          pg ? &pg->kI : nullptr);
+                                          pg ? &pg->kI : nullptr, head_w);
     if (e != hipSuccess) return finish(e);
     return finish(hsa::launch_attn_decode(dtype, q, swa_kv, swa_len, comp_kv, topk_idx,
                                           comp_len, out, lse, B, H, d_qk, d_v, W, S_max, k,
@@ -235,6 +279,25 @@ int hsa_decode_sparse(int dtype, const void* q_idx, const void* k_idx, const int
         return decode_sparse_impl(dtype, q_idx, k_idx, n_cand, scores, topk_idx, q, swa_kv,
                                   swa_len, comp_kv, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
                                   W, S_max, k, scale, workspace, workspace_bytes, stream, nullptr);
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+int hsa_decode_sparse_weighted(int dtype, const void* q_idx, const float* head_w,
+                               const void* k_idx, const int32_t* n_cand, float* scores,
+                               int32_t* topk_idx, const void* q, const void* swa_kv,
+                               const int32_t* swa_len, const void* comp_kv,
+                               const int32_t* comp_len, void* out, float* lse, int32_t B,
+                               int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v,
+                               int32_t W, int32_t S_max, int32_t k, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    try {
+        if (!head_w) return HSA_ERR_INVALID_ARG;
+        return decode_sparse_impl(dtype, q_idx, k_idx, n_cand, scores, topk_idx, q, swa_kv,
+                                  swa_len, comp_kv, comp_len, out, lse, B, H_I, d_I, H, d_qk, d_v,
+                                  W, S_max, k, scale, workspace, workspace_bytes, stream, nullptr,
+                                  false, nullptr, head_w);
     } catch (...) {
         return HSA_ERR_HIP;
     }

@@ -78,11 +78,14 @@ constexpr int kTopkMaxK = 2048;
 constexpr int kTopkMaxSegments = 1024;  // multi-workgroup select: S_max <= 1024 * 4096
 size_t topk_workspace_bytes(int Nq, int S_max, int k);
 // kI != nullptr with kI->map set: k_idx is the paged indexer-key pool (a row
-// that is not resident scores NaN).
+// that is not resident scores NaN).  head_w != nullptr: weighted, activated
+// heads, sum_h head_w[q, h] * max(0, q_h . k) (bf16, d_I = 128, H_I a multiple
+// of 16 up to 64; the caller checks the shape).
 hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, int B,
                              const int32_t* q_seq, const int32_t* n_cand, float* scores,
                              int32_t* topk_idx, int Nq, int H_I, int d_I, int S_max, int k,
-                             void* ws, hipStream_t st, const PoolMap* kI = nullptr);
+                             void* ws, hipStream_t st, const PoolMap* kI = nullptr,
+                             const float* head_w = nullptr);
 // A decode-time C4 append (block length 4) handed to a decode layer-step:
 // the arguments of launch_compress_append with m = 4.
 // Paged (swa.map != nullptr): ring_x / ring_g are the compression-state pools,
@@ -113,7 +116,7 @@ hipError_t launch_zero_words(void* p, size_t words, hipStream_t st);
 hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
                               int S_max, int k, void* ws, const AppendJob* job, hipStream_t st,
-                              const PoolMap* kI = nullptr);
+                              const PoolMap* kI = nullptr, const float* head_w = nullptr);
 
 // ---- attention ----
 struct DecodePlan {

@@ -116,12 +116,35 @@ __device__ __forceinline__ float reduce_scatter8(float (&v)[8], int sub) {
 // workgroup; it touches only the append's own buffers).
 // PAGED: k_idx is the paged indexer-key pool of shadow kp (row s of sequence
 // b at its physical row; a row that is not resident scores NaN).
+// WM = 1: weighted, activated heads, score = sum_h head_w[q, h] * max(0, q_h . k)
+// (bf16, 128-wide keys, H_I a multiple of 16 up to 64): per batch each wave
+// takes two blocks of 16 key rows as MFMA A operands (lane: row lane % 16,
+// channels 8 (lane / 16) + 32 ks), the query's heads are the B operands
+// (16 per MFMA column block) held in registers, and v_mfma_f32_16x16x32_bf16
+// gives each lane 4 rows x 1 head; the weighted ReLU terms of a lane's heads
+// are added in head-block order, then across the 16 lanes of the row group by
+// a xor butterfly (quad swaps, half-row and row mirrors), which hands every
+// lane the same sum: every row gets one fixed tree, so equal rows score the same.
 constexpr int kScorePagesMax = 8192 / 16 + 1;  // logical pages a scoring workgroup spans
-template <typename T, int LPR, int SEL, bool PAGED>
+constexpr int kWeightedMaxHeads = 64;
+
+// sum over the 16 lanes of a DPP row (xor 1, xor 2, half-row mirror, row
+// mirror): every lane of the row receives the bitwise-same value
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));
+    return v;
+}
+
+template <typename T, int LPR, int SEL, bool PAGED, int WM>
 __global__ __launch_bounds__(kThreads) void score_kernel(
     const T* __restrict__ q_idx, const T* __restrict__ k_idx, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ n_cand, float* __restrict__ scores, uint8_t* __restrict__ ws,
-    int B, int H_I, int S_max, int k, int rows_per_wg, int Nq, AppendJob job, PoolMap kp) {
+    int B, int H_I, int S_max, int k, int rows_per_wg, int Nq, AppendJob job, PoolMap kp,
+    const float* __restrict__ head_w) {
+    static_assert(WM == 0 || (LPR == 16 && sizeof(T) == 2), "weighted heads: bf16, 128-wide keys");
     constexpr bool HIST = SEL >= 1;
     constexpr bool LIST = SEL >= 2;
     // log2 of the rows per list slot: fixed at 2048 for SEL 2 (so that the
@@ -136,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     constexpr int RPB = RPU * U;           // rows per workgroup batch
     constexpr int NG = kThreads / LPR;     // partial head sums per channel
     constexpr int LB = (LPR == 8) ? 3 : (LPR == 16 ? 4 : 5);
-    __shared__ float qpart[NG][DI];
-    __shared__ float qsum[DI];
+    __shared__ float qpart[WM ? 1 : NG][WM ? 1 : DI];
+    __shared__ float qsum[WM ? 1 : DI];
     __shared__ uint32_t hist[HIST ? kBins : 1];
     __shared__ uint32_t scan_tmp[LIST ? kNW + 2 : 1];
     __shared__ uint32_t cut_res;
@@ -170,7 +193,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const int sub = lane % LPR, rs = lane / LPR;
     const int bseq_raw = q_seq ? q_seq[q] : q;
     const int bseq = (bseq_raw < 0 || bseq_raw >= B) ? 0 : bseq_raw;
-    const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)sub * V;
+    // the lane's first channel of a key row: chunk `sub` (unit weights) or the
+    // MFMA A-operand chunk 8 (lane / 16) (+ 32 ks per load, weighted)
+    const int lane_e = WM ? 8 * (lane >> 4) : sub * V;
+    const T* kbase = k_idx + (size_t)bseq * S_max * DI + (size_t)lane_e;
     const int r0 = blockIdx.x * rows_per_wg;
     const int r1m = min(S_max, r0 + rows_per_wg);  // rows that are valid memory
     // paged: the shadow entries of this workgroup's rows (logical pages j0 ..)
@@ -190,33 +216,34 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         if constexpr (PAGED) {
             const int pg = spg[(r >> kp.lg) - j0];
             const size_t pr = pg < 0 ? 0 : (((size_t)pg << kp.lg) | (size_t)(r & ((1 << kp.lg) - 1)));
-            return k_idx + pr * DI + (size_t)sub * V;
+            return k_idx + pr * DI + (size_t)lane_e;
         } else {
             return kbase + (size_t)r * DI;
         }
     };
 
     // Key rows are read once: nontemporal loads keep them from displacing
-    // reusable lines.  Load u of batch bi: the 256 lanes read RPU consecutive
-    // rows (4 KB), wave w the w-th quarter.  Full batches need no clamp.
+    // reusable lines.  Load u of batch bi: unit weights, the 256 lanes read RPU
+    // consecutive rows (4 KB), wave w the w-th quarter; weighted, wave w reads
+    // rows 32 w .. 32 w + 31 of the batch, load u the 16-row block u / 4 at
+    // channels 32 (u % 4) + 8 (lane / 16).  Full batches need no clamp.
+    auto urow = [&](int u) {
+        return WM ? w * 32 + 16 * (u >> 2) + (lane & 15) : u * RPU + w * RPL + rs;
+    };
+    auto uoff = [&](int u) { return WM ? 32 * (u & 3) : 0; };
     auto load_batch = [&](u32x4 (&buf)[U], int bi, int rlim) {
         const int rb = r0 + bi * RPB;
-        if (PAGED && rb + RPB <= rlim) {
+        if (rb + RPB <= rlim) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 buf[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(krow(rb + u * RPU + w * RPL + rs)));
-        } else if (rb + RPB <= rlim) {
-            const T* p = kbase + (size_t)(rb + w * RPL + rs) * DI;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (size_t)u * RPU * DI));
+                    reinterpret_cast<const u32x4*>(krow(rb + urow(u)) + uoff(u)));
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int r = rb + u * RPU + w * RPL + rs;
+                const int r = rb + urow(u);
                 const int rc = r < rlim ? r : rlim - 1;  // stay inside the valid rows
-                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc)));
+                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc) + uoff(u)));
             }
         }
     };
@@ -228,19 +255,38 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     const int nchunks = H_I * LPR;
     const T* qb = q_idx + (size_t)q * H_I * DI;
     u32x4 f4[4];
+    // weighted: the B operands (head 16 hb + lane % 16, channels 32 ks +
+    // 8 (lane / 16)) and the lane's head weights; head blocks past H_I are
+    // loaded from head block 0 and skipped
+    constexpr int NHB = WM ? kWeightedMaxHeads / 16 : 1;
+    bf16x8 qf[NHB][4];
+    float wl[NHB];
+    const int nhb = WM ? H_I / 16 : 0;
+    if constexpr (WM == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = tid + j * kThreads;
-        f4[j] = *reinterpret_cast<const u32x4*>(qb + (size_t)min(c, nchunks - 1) * V);
+        for (int j = 0; j < 4; ++j) {
+            const int c = tid + j * kThreads;
+            f4[j] = *reinterpret_cast<const u32x4*>(qb + (size_t)min(c, nchunks - 1) * V);
+        }
+    } else {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            const int h = (hb < nhb ? 16 * hb : 0) + (lane & 15);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qf[hb][ks] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(qb + (size_t)h * DI + 32 * ks + 8 * (lane >> 4)));
+            wl[hb] = head_w[(size_t)q * H_I + h];
+        }
     }
     u32x4 cur[U];
     {   // the first batch in the clamped form: no branch, so the loads above
         // keep an exact place in the in-order count
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * RPU + w * RPL + rs;
+            const int r = r0 + urow(u);
             const int rc = r < r1m ? r : r1m - 1;
-            cur[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc)));
+            cur[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc) + uoff(u)));
         }
     }
     if constexpr (HIST) clear_hist2_slice(ws, q, S_max, k);
@@ -260,7 +306,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     // fold the heads: thread t sums the chunks t, t+256, ... of q_idx[q] (all
     // loads issued together), then the NG partials of each channel are added
     // in a fixed order
-    {
+    if constexpr (WM != 0) {
+        if constexpr (HIST)
+            for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+        __syncthreads();
+    } else {
         const int ec = tid % LPR, grp = tid / LPR;
         float part[V];
 #pragma unroll
@@ -304,26 +354,60 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         __syncthreads();
     }
     float qv[V];
+    if constexpr (WM == 0) {
 #pragma unroll
-    for (int e = 0; e < V; ++e) qv[e] = qsum[sub * V + e];
-    const bool writer = (sub & ((1 << (LB - 3)) - 1)) == 0;
+        for (int e = 0; e < V; ++e) qv[e] = qsum[sub * V + e];
+    }
     const int my_u = sub >> (LB - 3);
 
     for (int bi = 0; bi < nb; ++bi) {
         u32x4 nxt[U];
         if (bi + 1 < nb) load_batch(nxt, bi + 1, r1);  // next batch in flight while this one is reduced
-        float d[U];
+        float sc;
+        int r;
+        bool writer;
+        if constexpr (WM == 0) {
+            float d[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kv[V];
-            Elem<T>::unpack(cur[u], kv);
-            float acc = 0.f;
+            for (int u = 0; u < U; ++u) {
+                float kv[V];
+                Elem<T>::unpack(cur[u], kv);
+                float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < V; ++e) acc = fmaf(qv[e], kv[e], acc);
-            d[u] = acc;
+                for (int e = 0; e < V; ++e) acc = fmaf(qv[e], kv[e], acc);
+                d[u] = acc;
+            }
+            sc = reduce_scatter8<LPR>(d, sub);
+            r = r0 + bi * RPB + my_u * RPU + w * RPL + rs;
+            writer = (sub & ((1 << (LB - 3)) - 1)) == 0;
+        } else {
+            f32x4 tot[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4 sj = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int hb = 0; hb < NHB; ++hb) {
+                    if (hb < nhb) {  // uniform
+                        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks)
+                            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, cur[4 * j + ks]), qf[hb][ks], c, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sj[i] = fmaf(wl[hb], fmaxf(c[i], 0.f), sj[i]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sj[i] = row16_sum(sj[i]);
+                tot[j] = sj;
+            }
+            // lane t < 8 of row group g writes row 16 (t / 4) + 4 g + t % 4 of the wave's 32
+            const int t = lane & 15, i = t & 3;
+            const f32x4 tj = (t >> 2) & 1 ? tot[1] : tot[0];
+            sc = i == 0 ? tj[0] : (i == 1 ? tj[1] : (i == 2 ? tj[2] : tj[3]));
+            r = r0 + bi * RPB + w * 32 + 16 * ((t >> 2) & 1) + 4 * (lane >> 4) + i;
+            writer = t < 8;
         }
-        float sc = reduce_scatter8<LPR>(d, sub);
-        const int r = r0 + bi * RPB + my_u * RPU + w * RPL + rs;
         if constexpr (PAGED) {
             if (r < r1 && spg[(r >> kp.lg) - j0] < 0) sc = __builtin_nanf("");
         }
@@ -1035,26 +1119,42 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const int32_t* __r
     select_zero<kThreads>(W, S_max, segc, tmp);
 }
 
+template <typename T, int LPR, int SEL, int WM>
+void launch_score_wm(dim3 grid, size_t lds, hipStream_t st, const void* q_idx, const void* k_idx,
+                     const int32_t* q_seq, const int32_t* n_cand, float* scores, uint8_t* ws,
+                     int B, int H_I, int S_max, int k, int rows, int Nq, const AppendJob& aj,
+                     const PoolMap* kp, const float* head_w) {
+    if (kp && kp->map)
+        hipLaunchKernelGGL((score_kernel<T, LPR, SEL, true, WM>), grid, dim3(kThreads), lds, st,
+                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
+                           S_max, k, rows, Nq, aj, *kp, head_w);
+    else
+        hipLaunchKernelGGL((score_kernel<T, LPR, SEL, false, WM>), grid, dim3(kThreads), lds, st,
+                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
+                           S_max, k, rows, Nq, aj, PoolMap{}, head_w);
+}
+
 template <typename T, int LPR, int SEL>
 void launch_score_sel(dim3 grid, size_t lds, hipStream_t st, const void* q_idx, const void* k_idx,
                       const int32_t* q_seq, const int32_t* n_cand, float* scores, uint8_t* ws,
                       int B, int H_I, int S_max, int k, int rows, int Nq, const AppendJob& aj,
-                      const PoolMap* kp) {
-    if (kp && kp->map)
-        hipLaunchKernelGGL((score_kernel<T, LPR, SEL, true>), grid, dim3(kThreads), lds, st,
-                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows, Nq, aj, *kp);
-    else
-        hipLaunchKernelGGL((score_kernel<T, LPR, SEL, false>), grid, dim3(kThreads), lds, st,
-                           (const T*)q_idx, (const T*)k_idx, q_seq, n_cand, scores, ws, B, H_I,
-                           S_max, k, rows, Nq, aj, PoolMap{});
+                      const PoolMap* kp, const float* head_w) {
+    if constexpr (std::is_same<T, bf16_t>::value && LPR == 16) {
+        if (head_w) {  // the caller checked the weighted shape (bf16, 128-wide, H_I % 16 == 0, <= 64)
+            launch_score_wm<T, LPR, SEL, 1>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B,
+                                            H_I, S_max, k, rows, Nq, aj, kp, head_w);
+            return;
+        }
+    }
+    launch_score_wm<T, LPR, SEL, 0>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I,
+                                    S_max, k, rows, Nq, aj, kp, nullptr);
 }
 
 template <typename T, int LPR>
 hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32_t* q_seq,
                         const int32_t* n_cand, float* scores, uint8_t* ws, int Nq, int H_I,
                         int S_max, int k, int sel, const AppendJob* job, hipStream_t st,
-                        const PoolMap* kp) {
+                        const PoolMap* kp, const float* head_w) {
     const int rows_lg = list_rows_log2(S_max, Nq);
     if (sel == 2 && rows_lg != 11) sel = 3;  // smaller slots: the variable-slot instantiation
     const int rows = sel >= 2 ? (1 << rows_lg) : sel ? kScoreRowsMulti : min(S_max, 8192);
@@ -1068,13 +1168,13 @@ hipError_t launch_score(const void* q_idx, const void* k_idx, int B, const int32
     const size_t lds = (size_t)rows * sizeof(float);  // staged scores
     ProfScope prof(kProfScore, st);
     if (sel == 3)
-        launch_score_sel<T, LPR, 3>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
+        launch_score_sel<T, LPR, 3>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp, head_w);
     else if (sel == 2)
-        launch_score_sel<T, LPR, 2>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
+        launch_score_sel<T, LPR, 2>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp, head_w);
     else if (sel == 1)
-        launch_score_sel<T, LPR, 1>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
+        launch_score_sel<T, LPR, 1>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp, head_w);
     else
-        launch_score_sel<T, LPR, 0>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp);
+        launch_score_sel<T, LPR, 0>(grid, lds, st, q_idx, k_idx, q_seq, n_cand, scores, ws, B, H_I, S_max, k, rows, Nq, aj, kp, head_w);
     return hipGetLastError();
 }
 
@@ -1082,13 +1182,13 @@ template <typename T>
 hipError_t launch_score_t(int d_I, const void* q_idx, const void* k_idx, int B,
                           const int32_t* q_seq, const int32_t* n_cand, float* scores, uint8_t* ws,
                           int Nq, int H_I, int S_max, int k, int sel, const AppendJob* job,
-                          hipStream_t st, const PoolMap* kp) {
+                          hipStream_t st, const PoolMap* kp, const float* head_w) {
     const int lpr = d_I * (int)sizeof(T) / 16;
     if (lpr == 8)
-        return launch_score<T, 8>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp);
+        return launch_score<T, 8>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp, head_w);
     if (lpr == 16)
-        return launch_score<T, 16>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp);
-    return launch_score<T, 32>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp);
+        return launch_score<T, 16>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp, head_w);
+    return launch_score<T, 32>(q_idx, k_idx, B, q_seq, n_cand, scores, ws, Nq, H_I, S_max, k, sel, job, st, kp, head_w);
 }
 
 // Zero the first-digit histogram of every query (a scoring launch whose select
@@ -1140,18 +1240,18 @@ bool index_lists_apply(int S_max, int k, int Nq) { return lists_apply(S_max, k, 
 hipError_t launch_index_lists(int dtype, const void* q_idx, const void* k_idx, int B,
                               const int32_t* n_cand, float* scores, int Nq, int H_I, int d_I,
                               int S_max, int k, void* ws, const AppendJob* job, hipStream_t st,
-                              const PoolMap* kI) {
+                              const PoolMap* kI, const float* head_w) {
     uint8_t* w = static_cast<uint8_t*>(ws);
     return dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
-                                                  Nq, H_I, S_max, k, 2, job, st, kI)
+                                                  Nq, H_I, S_max, k, 2, job, st, kI, head_w)
                          : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, nullptr, n_cand, scores, w,
-                                                   Nq, H_I, S_max, k, 2, job, st, kI);
+                                                   Nq, H_I, S_max, k, 2, job, st, kI, head_w);
 }
 
 hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, int B,
                              const int32_t* q_seq, const int32_t* n_cand, float* scores,
                              int32_t* topk_idx, int Nq, int H_I, int d_I, int S_max, int k,
-                             void* ws, hipStream_t st, const PoolMap* kI) {
+                             void* ws, hipStream_t st, const PoolMap* kI, const float* head_w) {
     const bool paged = kI && kI->map;
     const bool multi = S_max > kRowSelectCap;
     uint8_t* w = static_cast<uint8_t*>(ws);
@@ -1159,7 +1259,7 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
     // the select treats a query routed outside [0, B) as one without candidates
     // (select-only mode has no key sequences: q_seq is ignored there)
     const int32_t* sel_seq = q_idx ? q_seq : nullptr;
-    if (q_idx && !multi && !paged && dtype == kBF16 && Nq >= kGemmMinQueries &&
+    if (q_idx && !multi && !paged && !head_w && dtype == kBF16 && Nq >= kGemmMinQueries &&
         (d_I == 64 || d_I == 128 || d_I == 256)) {
         ProfScope prof(kProfScore, st);
         const dim3 grid((unsigned)ceil_div(Nq, kGemmQ));
@@ -1177,9 +1277,9 @@ hipError_t launch_index_topk(int dtype, const void* q_idx, const void* k_idx, in
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (q_idx) {
         e = dtype == kF32 ? launch_score_t<float>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores, w,
-                                                   Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st, kI)
+                                                   Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st, kI, head_w)
                           : launch_score_t<bf16_t>(d_I, q_idx, k_idx, B, q_seq, n_cand, scores,
-                                                   w, Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st, kI);
+                                                   w, Nq, H_I, S_max, k, multi ? 1 : 0, nullptr, st, kI, head_w);
         if (e != hipSuccess) return e;
     } else if (multi) {
         dim3 grid((unsigned)ceil_div(S_max, kFilterChunk), (unsigned)Nq);

@@ -160,8 +160,8 @@ int hsa_compress_append(int dtype, const void *x_tok, const void *g_tok, const v
  *   topk_idx : [Nq, k] int32 output
  *   Sizes    : Nq >= 1, B >= 1, H_I >= 1, d_I*sizeof(dtype) in {128, 256, 512},
  *              1 <= S_max <= 4,194,304 (HSA_ERR_UNSUPPORTED above), 1 <= k <= 2048.
- *              flags must be 0 (reserved for a weighted/activated head
- *              combination).
+ *              flags must be 0 (reserved; the weighted/activated head
+ *              combination is hsa_index_topk_weighted).
  *   workspace: device memory of hsa_index_topk_workspace_size(Nq, S_max, k)
  *              bytes.  It must be zero-filled before its first use; every
  *              call that completes leaves it zero-filled again.
@@ -172,6 +172,30 @@ int hsa_index_topk(int dtype, const void *q_idx, const void *k_idx, int32_t B,
                    int32_t *topk_idx, int32_t Nq, int32_t H_I, int32_t d_I, int32_t S_max,
                    int32_t k, uint32_t flags, void *workspace, size_t workspace_bytes,
                    void *stream);
+
+/*
+ * hsa_index_topk_weighted -- hsa_index_topk with weighted, activated indexer
+ * heads (method variant).
+ *
+ * [KD "Arquitectura del Sistema"] names a DSA indexer; [NK "RL 训练侧"]
+ * likens the attention indexer to an MoE router, whose gate weighs each of
+ * its experts.  The pages define no head combination; this variant takes the
+ * DSA indexer as published with DeepSeek-V3.2: each head's dot product passes
+ * a ReLU and the heads are summed with per-query weights,
+ *   scores[q, s] = sum_{h<H_I} head_w[q, h] * max(0, sum_e q_idx[q, h, e] * k_idx[q_seq[q], s, e])
+ * (a NaN dot product contributes 0).  Each head's dot product runs on MFMA
+ * (bf16 products, fp32 accumulation); identical key rows of a sequence give
+ * bitwise-identical scores.  Select, outputs and workspace: as hsa_index_topk.
+ *
+ *   head_w : [Nq, H_I] fp32 device memory, 4-byte aligned
+ *   Sizes  : dtype HSA_BF16, d_I = 128, H_I a multiple of 16 in [16, 64]
+ *            (other shapes HSA_ERR_UNSUPPORTED); the rest as hsa_index_topk.
+ */
+int hsa_index_topk_weighted(int dtype, const void *q_idx, const float *head_w, const void *k_idx,
+                            int32_t B, const int32_t *q_seq, const int32_t *n_cand, float *scores,
+                            int32_t *topk_idx, int32_t Nq, int32_t H_I, int32_t d_I,
+                            int32_t S_max, int32_t k, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /*
  * hsa_attn_decode -- one query token per sequence, one joint softmax over the
@@ -260,6 +284,22 @@ int hsa_decode_sparse(int dtype, const void *q_idx, const void *k_idx, const int
                       void *out, float *lse, int32_t B, int32_t H_I, int32_t d_I, int32_t H,
                       int32_t d_qk, int32_t d_v, int32_t W, int32_t S_max, int32_t k,
                       float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * hsa_decode_sparse_weighted -- hsa_decode_sparse with the weighted,
+ * activated indexer heads of hsa_index_topk_weighted (head_w [B, H_I] fp32):
+ * results equal hsa_index_topk_weighted followed by hsa_attn_decode, as for
+ * hsa_decode_sparse.  Arguments, limits and workspace: as hsa_decode_sparse,
+ * with the shape limits of hsa_index_topk_weighted.
+ */
+int hsa_decode_sparse_weighted(int dtype, const void *q_idx, const float *head_w,
+                               const void *k_idx, const int32_t *n_cand, float *scores,
+                               int32_t *topk_idx, const void *q, const void *swa_kv,
+                               const int32_t *swa_len, const void *comp_kv,
+                               const int32_t *comp_len, void *out, float *lse, int32_t B,
+                               int32_t H_I, int32_t d_I, int32_t H, int32_t d_qk, int32_t d_v,
+                               int32_t W, int32_t S_max, int32_t k, float scale, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /*
  * hsa_decode_step -- the C4 decode layer-step with its compression-state
