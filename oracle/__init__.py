@@ -57,13 +57,15 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.oracle_compress.argtypes = [I, P, P, P, P, I, I, I, I]
+        lib.oracle_compress_overlap.argtypes = [I, P, P, P, P, I, I, I, I]
         lib.oracle_index_scores.argtypes = [I, P, P, P, P, P, I, I, I, I, I]
         lib.oracle_index_scores_weighted.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I]
         lib.oracle_topk.argtypes = [P, P, P, I, I, I]
         lib.oracle_attn_decode.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, D]
         lib.oracle_attn_prefill.argtypes = [I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I,
                                             I, D, P, I]
-        for f in (lib.oracle_compress, lib.oracle_index_scores, lib.oracle_index_scores_weighted,
+        for f in (lib.oracle_compress, lib.oracle_compress_overlap, lib.oracle_index_scores,
+                  lib.oracle_index_scores_weighted,
                   lib.oracle_topk,
                   lib.oracle_attn_decode, lib.oracle_attn_prefill):
             f.restype = I
@@ -125,6 +127,55 @@ def compress(x, gate, bias, m):
     out = np.empty((B, T // m, D), dtype=np.float64)
     _check(_load().oracle_compress(et, _p(xa), _p(ga), _p(ba), _p(out), B, T, D, m), "compress")
     return out
+
+
+def compress_overlap(x, gate, bias, m):
+    """Overlapping-block compressor (method variant): entry i over tokens
+    m(i-1) .. m(i+1)-1 that exist, bias [2m, D] (row j for token m(i-1)+j).
+
+    x, gate: [B, T, D]; bias: [2m, D] -> float64 [B, T//m, D]."""
+    et, (xa, ga, ba) = _same_et(x, gate, bias)
+    B, T, D = xa.shape
+    if ga.shape != (B, T, D) or ba.shape != (2 * m, D):
+        raise ValueError("compress_overlap: shape mismatch")
+    out = np.empty((B, T // m, D), dtype=np.float64)
+    _check(_load().oracle_compress_overlap(et, _p(xa), _p(ga), _p(ba), _p(out), B, T, D, m),
+           "compress_overlap")
+    return out
+
+
+def compress_append_overlap(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, m):
+    """Decode-time state of the overlapping compressor: the ring keeps the last
+    2m tokens (slot = position mod 2m).  The token of sequence b at p = pos[b]
+    >= 0 is stored in slot p mod 2m; if it completes block i = p div m (and
+    i < S_max) the entry is compress_overlap of tokens m(i-1) .. p, read from
+    the ring (tokens before 0 do not exist).
+    ring_x, ring_g: [B, 2m, D] (updated in place); pool: float64 [B, S_max, D].
+    Returns the (b, row) pairs written."""
+    B = x_tok.shape[0]
+    if tuple(ring_x.shape) != (B, 2 * m, x_tok.shape[1]) or tuple(ring_g.shape) != tuple(ring_x.shape):
+        raise ValueError("compress_append_overlap: ring shape mismatch")
+    written = []
+    for b in range(B):
+        p = int(pos[b])
+        if p < 0:
+            continue
+        ring_x[b, p % (2 * m)] = x_tok[b]
+        ring_g[b, p % (2 * m)] = g_tok[b]
+        i = p // m
+        if p % m != m - 1 or i >= pool.shape[1]:
+            continue
+        t0 = max(0, m * (i - 1))
+        toks = list(range(t0, p + 1))
+        slots = [t % (2 * m) for t in toks]
+        seq_x = ring_x[b][slots][None]
+        seq_g = ring_g[b][slots][None]
+        if i == 0:  # one block: the whole window is entry 0 of a length-m sequence
+            pool[b, i] = compress_overlap(seq_x, seq_g, bias, m)[0, 0]
+        else:       # two blocks: entry 1 of a length-2m sequence is the window
+            pool[b, i] = compress_overlap(seq_x, seq_g, bias, m)[0, 1]
+        written.append((b, i))
+    return written
 
 
 def compress_append(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, m):

@@ -108,6 +108,53 @@ int oracle_compress(int et, const void *x, const void *gate, const void *bias,
 }
 
 /* ------------------------------------------------------------------------ *
+ * Compressor with overlapping blocks (method variant).
+ *
+ * [NK "RL 训练侧"] says the C4 compressor carries an "overlap transform" that
+ * makes a naive context-parallel split wrong (each shard has to gather the
+ * tokens of its neighbour first).  The pages do not define it.  Reading: each
+ * entry covers its own block and the block before it, 2m tokens with stride
+ * m, so an entry at a shard boundary needs the previous shard's last block:
+ *     tokens t_j = m*(i-1) + j,  j = 0 .. 2m-1   (only those with t_j >= 0)
+ *     z_j  = gate[b, t_j, d] + bias[j, d]         bias: [2m, D]
+ *     out[b, i, d] = sum_j softmax_j(z) * x[b, t_j, d]
+ * for every complete block i (tokens m*i .. m*i+m-1 present); entry 0 has no
+ * earlier block, so its softmax runs over its own m tokens (bias rows m..2m-1).
+ * ------------------------------------------------------------------------ */
+int oracle_compress_overlap(int et, const void *x, const void *gate, const void *bias,
+                            double *out, int B, int T, int D, int m)
+{
+    if (bad_et(et) || !x || !gate || !bias || !out) return 1;
+    if (B < 0 || T < 0 || D < 1 || m < 1) return 1;
+    const int nblk = T / m;
+    long units = (long)B * nblk;
+#pragma omp parallel for schedule(static)
+    for (long u = 0; u < units; ++u) {
+        const int b = (int)(u / nblk), i = (int)(u % nblk);
+        const int j0 = i == 0 ? m : 0;  /* first existing token of the window */
+        double *z = (double *)malloc(sizeof(double) * (size_t)(2 * m));
+        for (int d = 0; d < D; ++d) {
+            double zmax = -INFINITY;
+            for (int j = j0; j < 2 * m; ++j) {
+                size_t t = (size_t)b * T + (size_t)m * (i - 1) + j;
+                z[j] = ld(gate, et, t * D + d) + ld(bias, et, (size_t)j * D + d);
+                if (z[j] > zmax) zmax = z[j];
+            }
+            double den = 0.0;
+            for (int j = j0; j < 2 * m; ++j) den += exp(z[j] - zmax);
+            double c = 0.0;
+            for (int j = j0; j < 2 * m; ++j) {
+                size_t t = (size_t)b * T + (size_t)m * (i - 1) + j;
+                c += (exp(z[j] - zmax) / den) * ld(x, et, t * D + d);
+            }
+            out[((size_t)b * nblk + i) * D + d] = c;
+        }
+        free(z);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ *
  * Indexer scores.
  *
  * [KD "Flujo de Inferencia", step "Indexer (TopK)"] the indexer ranks the
