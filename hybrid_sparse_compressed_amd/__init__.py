@@ -14,7 +14,8 @@ _BINDING_NAMES = (
     "EXPORTED", "HSA_BF16", "HSA_F32", "HsaError", "Workspace", "hsa_attn_decode",
     "hsa_attn_prefill", "hsa_compress", "hsa_compress_append", "hsa_index_topk",
     "hsa_decode_sparse", "hsa_decode_step", "hsa_decode_step_noalloc", "hsa_decode_step_paged",
-    "PageMaps", "hsa_index_topk_weighted", "hsa_decode_sparse_weighted", "lib", "strerror",
+    "PageMaps", "hsa_index_topk_weighted", "hsa_decode_sparse_weighted", "hsa_compress_overlap",
+    "hsa_compress_append_overlap", "lib", "strerror",
     "hsa_profile_enable", "hsa_profile_read", "HSA_PROF_COMPRESS", "HSA_PROF_SCORE",
     "HSA_PROF_SELECT", "HSA_PROF_ATTN", "HSA_PROF_MERGE",
 )

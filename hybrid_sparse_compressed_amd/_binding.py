@@ -25,8 +25,8 @@ EXPORTED = (
     "hsa_index_topk", "hsa_attn_decode_workspace_size", "hsa_attn_decode",
     "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
     "hsa_decode_sparse", "hsa_decode_step", "hsa_decode_step_noalloc", "hsa_decode_step_paged",
-    "hsa_index_topk_weighted", "hsa_decode_sparse_weighted", "hsa_profile_enable",
-    "hsa_profile_read",
+    "hsa_index_topk_weighted", "hsa_decode_sparse_weighted", "hsa_compress_overlap",
+    "hsa_compress_append_overlap", "hsa_profile_enable", "hsa_profile_read",
 )
 HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
 
@@ -83,6 +83,10 @@ def _load():
     lib.hsa_decode_step_paged.argtypes = [I] + [P] * 16 + [ctypes.POINTER(PageMaps), P, P] + \
         [I32] * 9 + [F, P, SZ, P]
     lib.hsa_decode_step_paged.restype = I
+    lib.hsa_compress_overlap.argtypes = [I, P, P, P, P, I32, I32, I32, I32, P]
+    lib.hsa_compress_overlap.restype = I
+    lib.hsa_compress_append_overlap.argtypes = [I, P, P, P, P, P, P, P, I32, I32, I32, I32, P]
+    lib.hsa_compress_append_overlap.restype = I
     lib.hsa_index_topk_weighted.argtypes = [I, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, P,
                                             SZ, P]
     lib.hsa_index_topk_weighted.restype = I
@@ -221,6 +225,46 @@ def hsa_compress_append(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, stream=No
            lib.hsa_compress_append(_dt(x_tok), _ptr(x_tok), _ptr(g_tok), _ptr(bias), _ptr(ring_x),
                                    _ptr(ring_g), _ptr(pos), _ptr(pool), B, D, m, S_max,
                                    _stream(stream)))
+    return pool
+
+
+def hsa_compress_overlap(x, gate, bias, m, out=None, stream=None):
+    """Overlapping blocks: out[b,i,:] = sum_j softmax_j(gate[b,t_j,:] + bias[j,:]) * x[b,t_j,:]
+    over the tokens t_j = m*(i-1)+j >= 0, j < 2m; bias: [2m, D]."""
+    B, T, D = x.shape
+    if out is None:
+        out = torch.empty((B, T // m, D), dtype=x.dtype, device=x.device)
+    for t in (gate, bias, out):
+        if t.dtype != x.dtype:
+            raise TypeError("hsa_compress_overlap: all tensors must share one dtype")
+    if gate.shape != x.shape or tuple(bias.shape) != (2 * m, D) or tuple(out.shape) != (B, T // m, D):
+        raise ValueError("hsa_compress_overlap: shape mismatch")
+    _check("hsa_compress_overlap", lib.hsa_compress_overlap(
+        _dt(x), _ptr(x), _ptr(gate), _ptr(bias), _ptr(out), B, T, D, m, _stream(stream)))
+    return out
+
+
+def hsa_compress_append_overlap(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, stream=None):
+    """Decode-time state of the overlapping compressor: ring of the last 2m tokens
+    (slot pos mod 2m); the token completing block i writes entry i (blocks i-1, i).
+
+    x_tok, g_tok: [B, D]; bias: [2m, D]; ring_x, ring_g: [B, 2m, D]; pos: [B] int32;
+    pool: [B, S_max, D]."""
+    B, D = x_tok.shape
+    m = bias.shape[0] // 2
+    S_max = pool.shape[1]
+    for t in (g_tok, bias, ring_x, ring_g, pool):
+        if t.dtype != x_tok.dtype:
+            raise TypeError("hsa_compress_append_overlap: all float tensors must share one dtype")
+    if (bias.shape[0] != 2 * m or tuple(g_tok.shape) != (B, D) or tuple(bias.shape) != (2 * m, D)
+            or tuple(ring_x.shape) != (B, 2 * m, D) or tuple(ring_g.shape) != (B, 2 * m, D)
+            or tuple(pool.shape) != (B, S_max, D) or tuple(pos.shape) != (B,)):
+        raise ValueError("hsa_compress_append_overlap: shape mismatch")
+    if pos.dtype != torch.int32:
+        raise TypeError("hsa_compress_append_overlap: pos must be int32")
+    _check("hsa_compress_append_overlap", lib.hsa_compress_append_overlap(
+        _dt(x_tok), _ptr(x_tok), _ptr(g_tok), _ptr(bias), _ptr(ring_x), _ptr(ring_g), _ptr(pos),
+        _ptr(pool), B, D, m, S_max, _stream(stream)))
     return pool
 
 

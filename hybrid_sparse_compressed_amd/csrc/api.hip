@@ -70,6 +70,43 @@ int hsa_compress_append(int dtype, const void* x_tok, const void* g_tok, const v
     }
 }
 
+int hsa_compress_overlap(int dtype, const void* x, const void* gate, const void* bias, void* out,
+                         int32_t B, int32_t T, int32_t D, int32_t m, void* stream) {
+    try {
+        if (!dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!x || !gate || !bias || !out) return HSA_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(gate) || !aligned16(bias) || !aligned16(out))
+            return HSA_ERR_INVALID_ARG;
+        if (B < 1 || D < 1 || m < 1 || T < m) return HSA_ERR_INVALID_ARG;
+        if (m > 4 || (D * esize(dtype)) % 16 != 0) return HSA_ERR_UNSUPPORTED;
+        return finish(hsa::launch_compress_overlap(dtype, x, gate, bias, out, B, T, D, m,
+                                                   as_stream(stream)));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
+int hsa_compress_append_overlap(int dtype, const void* x_tok, const void* g_tok, const void* bias,
+                                void* ring_x, void* ring_g, const int32_t* pos, void* pool,
+                                int32_t B, int32_t D, int32_t m, int32_t S_max, void* stream) {
+    try {
+        if (!dtype_ok(dtype)) return HSA_ERR_INVALID_ARG;
+        if (!x_tok || !g_tok || !bias || !ring_x || !ring_g || !pos || !pool)
+            return HSA_ERR_INVALID_ARG;
+        if (!aligned16(x_tok) || !aligned16(g_tok) || !aligned16(bias) || !aligned16(ring_x) ||
+            !aligned16(ring_g) || !aligned16(pool))
+            return HSA_ERR_INVALID_ARG;
+        if (B < 1 || D < 1 || m < 1 || S_max < 1) return HSA_ERR_INVALID_ARG;
+        if (m > 4 || (D * esize(dtype)) % 16 != 0) return HSA_ERR_UNSUPPORTED;
+        if ((long long)D * esize(dtype) / 16 > 65535LL * 256) return HSA_ERR_UNSUPPORTED;
+        return finish(hsa::launch_compress_append_overlap(dtype, x_tok, g_tok, bias, ring_x, ring_g,
+                                                          pos, pool, B, D, m, S_max,
+                                                          as_stream(stream)));
+    } catch (...) {
+        return HSA_ERR_HIP;
+    }
+}
+
 size_t hsa_index_topk_workspace_size(int32_t Nq, int32_t S_max, int32_t k) {
     if (Nq < 1 || S_max < 1 || k < 1) return 0;
     return hsa::topk_workspace_bytes(Nq, S_max, k);

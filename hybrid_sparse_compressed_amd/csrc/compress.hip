@@ -472,6 +472,114 @@ hipError_t launch_append_short(const void* x_tok, const void* g_tok, const void*
     return hipGetLastError();
 }
 
+// Overlapping blocks (method variant; [NK "RL 训练侧"], overlap transform):
+// entry i over the 2M tokens of blocks i-1 and i, bias [2M, D], entry 0 over
+// its own block.  One thread per (sequence, entry, 16-byte chunk), units in
+// chunk-major order, so the two entries that read a block run in neighbouring
+// workgroups and the second read of a block is served from L2 (plain loads).
+template <typename T, int M>
+__global__ __launch_bounds__(kCompressThreads) void compress_overlap_kernel(
+    const T* __restrict__ x, const T* __restrict__ gate, const T* __restrict__ bias,
+    T* __restrict__ out, int B, int T_len, int D) {
+    constexpr int V = Elem<T>::kPer16B;
+    constexpr int W2 = 2 * M;
+    const int nchunk = D / V;
+    const int nblk = T_len / M;
+    const long long unit = (long long)blockIdx.x * kCompressThreads + threadIdx.x;
+    if (unit >= (long long)B * nblk * nchunk) return;
+    const int c = (int)(unit % nchunk);
+    const long long bi = unit / nchunk;
+    const int i = (int)(bi % nblk);
+    const size_t row0 = (size_t)(bi / nblk) * T_len + (size_t)M * i;  // the block's first token
+    const int jlo = i == 0 ? M : 0;
+    u32x4 gw[W2], xw[W2], bw[W2];
+#pragma unroll
+    for (int j = 0; j < W2; ++j) {
+        const size_t t = j < jlo ? row0 : row0 - M + j;  // missing tokens: a valid row, unused
+        gw[j] = *reinterpret_cast<const u32x4*>(gate + t * D + (size_t)c * V);
+        xw[j] = *reinterpret_cast<const u32x4*>(x + t * D + (size_t)c * V);
+        bw[j] = *reinterpret_cast<const u32x4*>(bias + (size_t)j * D + (size_t)c * V);
+    }
+    float res[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float z[W2];
+        float gm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < W2; ++j) {
+            z[j] = j < jlo ? -INFINITY : (chunk_elem<T>(gw[j], e) + chunk_elem<T>(bw[j], e)) * kLog2e;
+            gm = fmaxf(gm, z[j]);
+        }
+        float sm = 0.f, acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < W2; ++j) {
+            if (j < jlo) continue;
+            const float w = exp2f(z[j] - gm);
+            sm += w;
+            acc = fmaf(w, chunk_elem<T>(xw[j], e), acc);
+        }
+        res[e] = acc / sm;
+    }
+    *reinterpret_cast<u32x4*>(out + (size_t)bi * D + (size_t)c * V) = pack16<T>(res);
+}
+
+template <typename T, int M>
+__global__ __launch_bounds__(kAppendThreads) void compress_append_overlap_kernel(
+    const T* x_tok, const T* g_tok, const T* bias, T* ring_x, T* ring_g, const int32_t* pos,
+    T* pool, int D, int S_max) {
+    append_overlap_chunk<T, M>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, D, S_max, blockIdx.x,
+                               blockIdx.y * kAppendThreads + threadIdx.x);
+}
+
+template <typename T, int M>
+hipError_t launch_overlap_m(const void* x, const void* g, const void* bias, void* out, int B,
+                            int T_len, int D, hipStream_t st) {
+    const long long nunits = (long long)B * (T_len / M) * (D / Elem<T>::kPer16B);
+    const long long nwg = (nunits + kCompressThreads - 1) / kCompressThreads;
+    if (nwg <= 0) return hipSuccess;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    ProfScope prof(kProfCompress, st);
+    hipLaunchKernelGGL((compress_overlap_kernel<T, M>), dim3((unsigned)nwg), dim3(kCompressThreads), 0,
+                       st, (const T*)x, (const T*)g, (const T*)bias, (T*)out, B, T_len, D);
+    return hipGetLastError();
+}
+
+template <typename T, int M>
+hipError_t launch_append_overlap_m(const void* x_tok, const void* g_tok, const void* bias,
+                                   void* ring_x, void* ring_g, const int32_t* pos, void* pool, int B,
+                                   int D, int S_max, hipStream_t st) {
+    const int nchunk = D / Elem<T>::kPer16B;
+    const int gy = (nchunk + kAppendThreads - 1) / kAppendThreads;
+    ProfScope prof(kProfCompress, st);
+    hipLaunchKernelGGL((compress_append_overlap_kernel<T, M>), dim3((unsigned)B, (unsigned)gy),
+                       dim3(kAppendThreads), 0, st, (const T*)x_tok, (const T*)g_tok,
+                       (const T*)bias, (T*)ring_x, (T*)ring_g, pos, (T*)pool, D, S_max);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_overlap_t(const void* x, const void* g, const void* bias, void* out, int B,
+                            int T_len, int D, int m, hipStream_t st) {
+    switch (m) {
+        case 1: return launch_overlap_m<T, 1>(x, g, bias, out, B, T_len, D, st);
+        case 2: return launch_overlap_m<T, 2>(x, g, bias, out, B, T_len, D, st);
+        case 3: return launch_overlap_m<T, 3>(x, g, bias, out, B, T_len, D, st);
+        default: return launch_overlap_m<T, 4>(x, g, bias, out, B, T_len, D, st);
+    }
+}
+
+template <typename T>
+hipError_t launch_append_overlap_t(const void* x_tok, const void* g_tok, const void* bias,
+                                   void* ring_x, void* ring_g, const int32_t* pos, void* pool,
+                                   int B, int D, int m, int S_max, hipStream_t st) {
+    switch (m) {
+        case 1: return launch_append_overlap_m<T, 1>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+        case 2: return launch_append_overlap_m<T, 2>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+        case 3: return launch_append_overlap_m<T, 3>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+        default: return launch_append_overlap_m<T, 4>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, S_max, st);
+    }
+}
+
 // the paged C4 append (append_short_chunk_paged), one thread per chunk
 template <typename T>
 __global__ __launch_bounds__(kAppendThreads) void compress_append_paged_kernel(AppendJob job) {
@@ -523,6 +631,21 @@ hipError_t launch_compress_append(int dtype, const void* x_tok, const void* g_to
                                                D, m, S_max, st);
     return launch_compress_append_t<bf16_t>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D,
                                             m, S_max, st);
+}
+
+hipError_t launch_compress_overlap(int dtype, const void* x, const void* g, const void* bias,
+                                   void* out, int B, int T_len, int D, int m, hipStream_t st) {
+    if (dtype == kF32) return launch_overlap_t<float>(x, g, bias, out, B, T_len, D, m, st);
+    return launch_overlap_t<bf16_t>(x, g, bias, out, B, T_len, D, m, st);
+}
+
+hipError_t launch_compress_append_overlap(int dtype, const void* x_tok, const void* g_tok,
+                                          const void* bias, void* ring_x, void* ring_g,
+                                          const int32_t* pos, void* pool, int B, int D, int m,
+                                          int S_max, hipStream_t st) {
+    if (dtype == kF32)
+        return launch_append_overlap_t<float>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, m, S_max, st);
+    return launch_append_overlap_t<bf16_t>(x_tok, g_tok, bias, ring_x, ring_g, pos, pool, B, D, m, S_max, st);
 }
 
 hipError_t launch_compress_append_paged(int dtype, const AppendJob& job, hipStream_t st) {

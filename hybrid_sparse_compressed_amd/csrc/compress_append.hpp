@@ -98,6 +98,68 @@ __device__ __forceinline__ void append_short_chunk(const T* x_tok, const T* g_to
         pack16<T>(res);
 }
 
+// Decode-time state of the overlapping compressor (method variant: entry i
+// covers blocks i-1 and i, bias [2M, D]; [NK "RL 训练侧"], overlap transform).
+// The ring keeps the last 2M tokens, slot = position mod 2M.  The token at
+// p = pos[b] goes to slot p mod 2M; when it completes block i = p div M
+// (i < S_max) the entry over tokens M(i-1) .. p (those >= 0) is written to
+// pool row i.  Token M(i-1) + j sits in slot (M(i-1) + j) mod 2M, which is
+// slot j or slot (j + M) mod 2M depending on the parity of i - 1: the ring is
+// loaded before the position is known and its halves swapped by a select.
+template <typename T, int M>
+__device__ __forceinline__ void append_overlap_chunk(const T* x_tok, const T* g_tok, const T* bias,
+                                                     T* ring_x, T* ring_g, const int32_t* pos,
+                                                     T* pool, int D, int S_max, int b, int c) {
+    constexpr int V = Elem<T>::kPer16B;
+    constexpr int W2 = 2 * M;
+    if (c >= D / V) return;
+    const size_t tok = (size_t)b * D + (size_t)c * V;
+    const size_t ring = (size_t)b * W2 * D + (size_t)c * V;
+    u32x4 xr[W2], gr[W2], bw[W2];
+    const u32x4 xt = *reinterpret_cast<const u32x4*>(x_tok + tok);
+    const u32x4 gt = *reinterpret_cast<const u32x4*>(g_tok + tok);
+#pragma unroll
+    for (int r = 0; r < W2; ++r) {
+        xr[r] = *reinterpret_cast<const u32x4*>(ring_x + ring + (size_t)r * D);
+        gr[r] = *reinterpret_cast<const u32x4*>(ring_g + ring + (size_t)r * D);
+        bw[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)r * D + (size_t)c * V);
+    }
+    asm volatile("" ::: "memory");
+    const int p = pos[b];
+    if (p < 0) return;  // idle sequence
+    const int s = p % W2;
+    *reinterpret_cast<u32x4*>(ring_x + ring + (size_t)s * D) = xt;
+    *reinterpret_cast<u32x4*>(ring_g + ring + (size_t)s * D) = gt;
+    const int blk = p / M;
+    if (p % M != M - 1 || blk >= S_max) return;
+    const bool swap = ((blk - 1) & 1) != 0;  // token M(blk-1) sits in slot M
+    const int jlo = blk == 0 ? M : 0;        // entry 0 has no earlier block
+    float res[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float z[W2], xv[W2];
+        float gm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < W2; ++j) {
+            const u32x4& gj = j == W2 - 1 ? gt : (swap ? gr[(j + M) % W2] : gr[j]);
+            const u32x4& xj = j == W2 - 1 ? xt : (swap ? xr[(j + M) % W2] : xr[j]);
+            z[j] = j < jlo ? -INFINITY : (chunk_elem<T>(gj, e) + chunk_elem<T>(bw[j], e)) * kLog2e;
+            xv[j] = chunk_elem<T>(xj, e);
+            gm = fmaxf(gm, z[j]);
+        }
+        float sm = 0.f, acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < W2; ++j) {
+            if (j < jlo) continue;
+            const float w = exp2f(z[j] - gm);
+            sm += w;
+            acc = fmaf(w, xv[j], acc);
+        }
+        res[e] = acc / sm;
+    }
+    *reinterpret_cast<u32x4*>(pool + ((size_t)b * S_max + blk) * D + (size_t)c * V) = pack16<T>(res);
+}
+
 // The same append on paged pools ([KD "Arquitectura del Sistema",
 // ShadowRadix]: the compression-state rings form a pool of their own, reached
 // from the SWA page by an arithmetic second-level map).  Token t's latent and

@@ -69,6 +69,15 @@ hipError_t launch_compress_append(int dtype, const void* x_tok, const void* g_to
                                   const int32_t* pos, void* pool, int B, int D, int m, int S_max,
                                   hipStream_t st);
 
+// Overlapping blocks (method variant), m <= 4: entry i over blocks i-1 and i
+// with a bias of 2m rows; the decode-time ring keeps the last 2m tokens.
+hipError_t launch_compress_overlap(int dtype, const void* x, const void* g, const void* bias,
+                                   void* out, int B, int T_len, int D, int m, hipStream_t st);
+hipError_t launch_compress_append_overlap(int dtype, const void* x_tok, const void* g_tok,
+                                          const void* bias, void* ring_x, void* ring_g,
+                                          const int32_t* pos, void* pool, int B, int D, int m,
+                                          int S_max, hipStream_t st);
+
 // ---- indexer + top-k ----
 // Candidate lists up to this length are selected by one workgroup per query
 // with every key resident in LDS; longer ones use the multi-workgroup path

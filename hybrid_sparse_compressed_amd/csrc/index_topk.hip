@@ -231,19 +231,24 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         return WM ? w * 32 + 16 * (u >> 2) + (lane & 15) : u * RPU + w * RPL + rs;
     };
     auto uoff = [&](int u) { return WM ? 32 * (u & 3) : 0; };
+    // (weighted: a load covers half of each of its 16 rows' 128-byte lines and
+    // the next load the other half, so these loads keep their lines in L2:
+    // plain loads, the second half a hit)
+    auto kload = [](const T* p) {
+        return WM ? *reinterpret_cast<const u32x4*>(p)
+                  : __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    };
     auto load_batch = [&](u32x4 (&buf)[U], int bi, int rlim) {
         const int rb = r0 + bi * RPB;
         if (rb + RPB <= rlim) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                buf[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(krow(rb + urow(u)) + uoff(u)));
+            for (int u = 0; u < U; ++u) buf[u] = kload(krow(rb + urow(u)) + uoff(u));
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = rb + urow(u);
                 const int rc = r < rlim ? r : rlim - 1;  // stay inside the valid rows
-                buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc) + uoff(u)));
+                buf[u] = kload(krow(rc) + uoff(u));
             }
         }
     };
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
         for (int u = 0; u < U; ++u) {
             const int r = r0 + urow(u);
             const int rc = r < r1m ? r : r1m - 1;
-            cur[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow(rc) + uoff(u)));
+            cur[u] = kload(krow(rc) + uoff(u));
         }
     }
     if constexpr (HIST) clear_hist2_slice(ws, q, S_max, k);

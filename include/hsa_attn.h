@@ -127,6 +127,31 @@ int hsa_compress_append(int dtype, const void *x_tok, const void *g_tok, const v
                         int32_t D, int32_t m, int32_t S_max, void *stream);
 
 /*
+ * hsa_compress_overlap, hsa_compress_append_overlap -- the block compressor
+ * with overlapping blocks (method variant).
+ *
+ * [NK "RL 训练侧"]: the C4 compressor carries an "overlap transform" that
+ * breaks a naive context-parallel split (a shard must first gather its
+ * neighbour's tokens).  The pages do not define it.  Reading: entry i covers
+ * its own block and the block before it, tokens m(i-1) .. m(i+1)-1, with a
+ * bias of 2m rows (row j for token m(i-1)+j):
+ *   out[b, i, d] = sum_j softmax_j(gate[b, t_j, d] + bias[j, d]) * x[b, t_j, d]
+ * over the tokens t_j >= 0 (entry 0 has only its own block), for every
+ * complete block i.  The decode-time state keeps the last 2m tokens in a ring
+ * (slot = position mod 2m); the token that completes block i writes entry i.
+ *
+ *   hsa_compress_overlap: x, gate [B, T, D]; bias [2m, D]; out [B, T/m, D]
+ *   hsa_compress_append_overlap: as hsa_compress_append with bias [2m, D] and
+ *       ring_x, ring_g [B, 2m, D]
+ *   Sizes: 1 <= m <= 4 (HSA_ERR_UNSUPPORTED above); the rest as the plain calls.
+ */
+int hsa_compress_overlap(int dtype, const void *x, const void *gate, const void *bias, void *out,
+                         int32_t B, int32_t T, int32_t D, int32_t m, void *stream);
+int hsa_compress_append_overlap(int dtype, const void *x_tok, const void *g_tok, const void *bias,
+                                void *ring_x, void *ring_g, const int32_t *pos, void *pool,
+                                int32_t B, int32_t D, int32_t m, int32_t S_max, void *stream);
+
+/*
  * hsa_index_topk -- indexer scores and exact top-k select.
  *
  * [KD "Flujo de Inferencia", step "Indexer (TopK)"]: top-k over the
