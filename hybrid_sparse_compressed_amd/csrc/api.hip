@@ -181,7 +181,7 @@ int hsa_index_topk_weighted(int dtype, const void* q_idx, const float* head_w, c
 
 size_t hsa_attn_decode_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t max_rows) {
     if (B < 1 || H < 1 || d_v < 1 || max_rows < 1) return 0;
-    return hsa::decode_workspace_bytes(B, H, d_v, max_rows);
+    return hsa::decode_workspace_bytes(B, H, d_v, max_rows, true);
 }
 
 int hsa_attn_decode(int dtype, const void* q, const void* swa_kv, const int32_t* swa_len,
@@ -201,7 +201,7 @@ int hsa_attn_decode(int dtype, const void* q, const void* swa_kv, const int32_t*
         if (!(scale == scale)) return HSA_ERR_INVALID_ARG;
         if (!hsa::attn_shape_supported(dtype, d_qk, d_v)) return HSA_ERR_UNSUPPORTED;
         const int max_rows = W + (comp_idx ? k : S_max);
-        const size_t need = hsa::decode_workspace_bytes(B, H, d_v, max_rows);
+        const size_t need = hsa::decode_workspace_bytes(B, H, d_v, max_rows, comp_idx == nullptr);
         if (need > 0 && (!workspace || workspace_bytes < need)) return HSA_ERR_WORKSPACE;
         return finish(hsa::launch_attn_decode(dtype, q, swa_kv, swa_len, comp_kv, comp_idx,
                                               comp_len, out, lse, B, H, d_qk, d_v, W, S_max,
@@ -217,7 +217,7 @@ static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t hsa_decode_sparse_workspace_size(int32_t B, int32_t H, int32_t d_v, int32_t W,
                                         int32_t S_max, int32_t k) {
     if (B < 1 || H < 1 || d_v < 1 || W < 1 || S_max < 1 || k < 1) return 0;
-    return round256(hsa::topk_workspace_bytes(B, S_max, k)) + hsa::decode_workspace_bytes(B, H, d_v, W + k);
+    return round256(hsa::topk_workspace_bytes(B, S_max, k)) + hsa::decode_workspace_bytes(B, H, d_v, W + k, false);
 }
 
 namespace {

@@ -107,6 +107,10 @@ struct AttnArgs {
     // C4 pools; window row vr of sequence b is token pos[b] - n_swa + 1 + vr
     PoolMap pg_swa, pg_c4;
     const int32_t* pos;
+    // dense 64-head decode with splits planned on the device from comp_len
+    // (n_seq sequences): workgroup g takes split g of the plan
+    int dense_plan, n_seq;
+    int* dense_seq_plan;  // [n_seq]: first split | split count << 16, for the merge
 };
 
 // LDS footprint of one tile, in elements of T: K row-major, V^T (one row per
@@ -658,6 +662,67 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         a.lse[orow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
+// 64-head kernel shape (prefill64_kernel, below)
+constexpr int kP64Threads = 512;
+constexpr int kP64Waves = kP64Threads / kWave;
+constexpr int kP64Heads = 64;
+constexpr int kP64Rows = 64;                    // rows per tile
+constexpr int kP64Chunk = kP64Threads;          // rows listed at once (one per thread)
+
+// ---- dense decode splits planned on the device --------------------------------
+// Sequence b has t_b = ceil((W + comp_len[b]) / 64) tiles (comp_len clamped to
+// [0, S_max]).  With R tiles per split, the smallest R that keeps the total
+// number of splits at most kDenseTarget (plus at most one partial split per
+// sequence) and every sequence at most kMaxSplit splits, sequence b gets
+// n_b = ceil(t_b / R) splits, numbered after the splits of sequences 0 .. b-1.
+// Every workgroup derives the same plan from the lengths, one lane per
+// sequence, and a sequence's first split hands (first, n_b) to the merge: a
+// short sequence no longer waits on the longest one's split length, and the
+// merge reads only the splits a sequence has.
+constexpr int kDenseTarget = 256;  // about one workgroup per compute unit
+constexpr int kMaxSplit = 128;
+
+__device__ inline int dense_tiles(const AttnArgs& a, int i) {
+    int n = a.comp_len[i];
+    n = n < 0 ? 0 : (n > a.S_max ? a.S_max : n);
+    return ceil_div(a.W + n, kP64Rows);
+}
+
+__device__ inline int dense_tiles_per_split(const AttnArgs& a) {
+    int sum = 0, mx = 0;
+    for (int i = lane_id(); i < a.n_seq; i += kWave) {
+        const int t = dense_tiles(a, i);
+        sum += t;
+        mx = max(mx, t);
+    }
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        sum += __shfl_xor(sum, o, kWave);
+        mx = max(mx, __shfl_xor(mx, o, kWave));
+    }
+    return max(1, max(ceil_div(sum, kDenseTarget), ceil_div(mx, kMaxSplit)));
+}
+
+// the sequence and split of split g; false past the last split
+__device__ inline bool dense_locate(const AttnArgs& a, int R, int g, int* b, int* split, int* first) {
+    int base = 0;
+    for (int i0 = 0; i0 < a.n_seq; i0 += kWave) {
+        const int i = i0 + lane_id();
+        const int n = i < a.n_seq ? ceil_div(dense_tiles(a, i), R) : 0;
+        const int incl = base + (int)wave_incl_scan((uint32_t)n);
+        const int excl = incl - n;
+        const unsigned long long hit = __ballot(n > 0 && excl <= g && g < incl);
+        if (hit) {
+            const int src = (int)__ffsll(hit) - 1;
+            *b = i0 + src;
+            *first = __shfl(excl, src, kWave);
+            *split = g - *first;
+            return true;
+        }
+        base = __shfl(incl, kWave - 1, kWave);
+    }
+    return false;
+}
+
 // ---- prefill with all heads of a query in one workgroup --------------------
 //
 // bf16, latent 576 / value 512, 64 heads.  A workgroup (8 waves) owns one
@@ -669,11 +734,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 // rest is the tile pipeline of attn_kernel (same operand layouts).  Rows are
 // listed 512 at a time as device addresses (0: not a row of this query), and
 // the next tile's rows are loaded into registers while a tile is computed.
-constexpr int kP64Threads = 512;
-constexpr int kP64Waves = kP64Threads / kWave;
-constexpr int kP64Heads = 64;
-constexpr int kP64Rows = 64;                    // rows per tile
-constexpr int kP64Chunk = kP64Threads;          // rows listed at once (one per thread)
 
 // K rows (row-major; the PV product reads the value columns out of them with
 // transposing LDS loads) and P^T (one row per head, in p_pos order).
@@ -712,11 +772,26 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     const bool head_ok = head < a.H;
 
     int b, pq = 0, qpos = 0, n_comp, n_swa = 0, vr0 = 0, vr1 = a.max_rows;
+    int part = 0;  // decode: this split's partial slot
     if constexpr (DEC) {
-        // decode split: workgroup (split x, sequence y) takes rows [vr0, vr1)
-        b = blockIdx.y;
-        vr0 = (int)blockIdx.x * a.rows_per_split;
-        vr1 = min(a.max_rows, vr0 + a.rows_per_split);
+        if (a.dense_plan) {
+            // split g of the device plan: R tiles of sequence b from tile R * split
+            const int R = dense_tiles_per_split(a);
+            int split, first;
+            if (!dense_locate(a, R, (int)blockIdx.x, &b, &split, &first)) return;  // uniform
+            vr0 = split * R * kP64Rows;
+            vr1 = vr0 + R * kP64Rows;
+            part = first + split;
+            // the sequence's first split hands its (first, count) to the merge
+            if (split == 0 && tid == 0)
+                a.dense_seq_plan[b] = first | (ceil_div(dense_tiles(a, b), R) << 16);
+        } else {
+            // decode split: workgroup (split x, sequence y) takes rows [vr0, vr1)
+            b = blockIdx.y;
+            vr0 = (int)blockIdx.x * a.rows_per_split;
+            vr1 = min(a.max_rows, vr0 + a.rows_per_split);
+            part = b * a.n_split + (int)blockIdx.x;
+        }
         n_swa = a.swa_len[b];
         n_swa = n_swa < 0 ? 0 : (n_swa > a.W ? a.W : n_swa);
         n_comp = a.comp_len[b];
@@ -926,8 +1001,8 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     // ---- epilogue.  acc[t][r] = O^T[256*half + 16t + 4quad + r][head]
     if (!head_ok) return;
     if constexpr (DEC) {
-        if (a.n_split > 1) {  // unnormalised partials for the merge kernel
-            const size_t prow = ((size_t)b * a.n_split + blockIdx.x) * a.H + head;
+        if (a.n_split > 1 || a.dense_plan) {  // unnormalised partials for the merge kernel
+            const size_t prow = (size_t)part * a.H + head;
             if (half == 0 && quad == 0)
                 *reinterpret_cast<float2*>(a.part_ml + prow * 2) = float2{m_run, l_run};
             float* po = a.part_o + prow * DV + half * DW;
@@ -954,8 +1029,8 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 // Merge the split partials of one (sequence, head) in a fixed split order.
 // All (max, sum) pairs are loaded at once, the weights go through LDS, and
 // each thread then issues the loads of its 4 channels for every split before
-// combining them.
-constexpr int kMaxSplit = 128;
+// combining them.  With a device plan (plan.dense_plan) the sequence's splits
+// are the ones the attention launch recorded for it.
 
 template <typename T, int DV, int kBatch>
 __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_ml,
@@ -963,14 +1038,20 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
                                                          void* __restrict__ out,
                                                          float* __restrict__ lse, int H,
                                                          int n_split, uint8_t* __restrict__ sel_ws,
-                                                         int S_max, int k) {
+                                                         int S_max, int k, AttnArgs plan) {
     // kBatch: split partials loaded per round (the launch picks the
     // smallest of 4, 8, 12, 16 that covers the splits, or 16)
-    auto load4 = [](const float* p) -> f32x4 { return *reinterpret_cast<const f32x4*>(p); };
+    auto load4 = [&](size_t i) -> f32x4 { return *reinterpret_cast<const f32x4*>(part_o + i); };
     __shared__ float wsp[kMaxSplit], lsp[kMaxSplit];
     __shared__ float stat[2];
     const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
-    const float* p0 = part_o + ((size_t)b * n_split * H + h) * DV;
+    int first = b * n_split;
+    if (plan.dense_plan) {  // written by the attention launch's first split of the sequence
+        const int v = plan.dense_seq_plan[b];
+        first = v & 0xffff;
+        n_split = v >> 16;
+    }
+    const size_t p0 = ((size_t)first * H + h) * DV;  // element index of split 0
     const size_t sstride = (size_t)H * DV;
     const int d = tid * 4;           // this thread's 4 channels (DV <= 512)
     const bool has_d = d < DV;
@@ -983,7 +1064,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
     for (int j = 0; j < kBatch; ++j) pv[j] = load4(p0 + (size_t)min(j, n_split - 1) * sstride + dc);
     float ms = -INFINITY, ls = 0.f;
     if (tid < n_split) {
-        const float2 v = *reinterpret_cast<const float2*>(part_ml + (((size_t)b * n_split + tid) * H + h) * 2);
+        const float2 v = *reinterpret_cast<const float2*>(part_ml + (((size_t)first + tid) * H + h) * 2);
         ms = v.x;
         ls = v.y;
     }
@@ -1101,19 +1182,9 @@ bool decode64_applies(int B, int H, int d_v, int max_rows, bool dense) {
     return dense && H == kP64Heads && d_v == 512 && (long long)B * ceil_div(max_rows, kP64Rows) >= 256;
 }
 
-DecodePlan plan_decode64(int B, int max_rows) {
-    DecodePlan p;
-    p.max_rows = max_rows;
-    const int tiles = ceil_div(max_rows, kP64Rows);
-    int n_split = ceil_div(256, B);  // about one workgroup per compute unit
-    if (n_split > tiles) n_split = tiles;
-    if (n_split > kMaxSplit) n_split = kMaxSplit;
-    if (n_split < 1) n_split = 1;
-    p.rows_per_split = ceil_div(tiles, n_split) * kP64Rows;
-    p.n_split = ceil_div(max_rows, p.rows_per_split);
-    if (p.n_split < 1) p.n_split = 1;
-    return p;
-}
+// the 64-head dense decode plans its splits on the device: at most
+// kDenseTarget + B partial slots (partials of slot g at [g][H][...])
+static int dense_parts(int B) { return kDenseTarget + B; }
 
 DecodePlan plan_decode(int B, int H, int max_rows) {
     DecodePlan p;
@@ -1139,16 +1210,14 @@ static size_t ml_bytes(int B, int n_split, int H) {
     return (((size_t)B * n_split * H * 2 * sizeof(float)) + 255) & ~(size_t)255;
 }
 
-size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows) {
-    // enough for either plan (the 64-head one is chosen at launch, by shape)
+size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows, bool dense) {
+    // enough for either plan (the 64-head one, dense only, is chosen at launch, by shape)
     const DecodePlan p = plan_decode(B, H, max_rows);
     size_t bytes = p.n_split <= 1 ? 0 : ml_bytes(B, p.n_split, H) + (size_t)B * p.n_split * H * d_v * sizeof(float);
-    if (decode64_applies(B, H, d_v, max_rows, true)) {
-        const DecodePlan q = plan_decode64(B, max_rows);
-        if (q.n_split > 1) {
-            const size_t b64 = ml_bytes(B, q.n_split, H) + (size_t)B * q.n_split * H * d_v * sizeof(float);
-            bytes = b64 > bytes ? b64 : bytes;
-        }
+    if (decode64_applies(B, H, d_v, max_rows, dense)) {
+        const int P = dense_parts(B);
+        const size_t b64 = ml_bytes(P, 1, H) + (size_t)P * H * d_v * sizeof(float) + (size_t)B * 4;
+        bytes = b64 > bytes ? b64 : bytes;
     }
     return bytes;
 }
@@ -1160,13 +1229,13 @@ static void launch_merge_nb(int dtype, int d_v, const AttnArgs& a, int B, int H,
     if (dtype == kBF16) {
         if (d_v == 512)
             hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 512, NB>), mg, dim3(128), 0, st, a.part_ml,
-                               a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k);
+                               a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k, a);
         else
             hipLaunchKernelGGL((attn_merge_kernel<bf16_t, 128, NB>), mg, dim3(128), 0, st, a.part_ml,
-                               a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k);
+                               a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k, a);
     } else {
         hipLaunchKernelGGL((attn_merge_kernel<float, 128, NB>), mg, dim3(128), 0, st, a.part_ml,
-                           a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k);
+                           a.part_o, a.out, a.lse, H, n_split, a.sel_ws, S_max, k, a);
     }
 }
 
@@ -1210,15 +1279,17 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* swa_kv,
     a.max_rows = max_rows;
     a.scale_log2 = scale * kLog2e;
     if (dtype == kBF16 && d_qk == 576 && decode64_applies(B, H, d_v, max_rows, comp_idx == nullptr)) {
-        const DecodePlan p = plan_decode64(B, max_rows);
-        a.rows_per_split = p.rows_per_split;
-        a.n_split = p.n_split;
-        a.part_o = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ml_bytes(B, p.n_split, H))
-                      : nullptr;
-        if (p.n_split > 1 && !ws) return hipErrorInvalidValue;
-        hipError_t e = launch_p64<true>(a, dim3((unsigned)p.n_split, (unsigned)B, 1u), st);
-        if (e != hipSuccess || p.n_split <= 1) return e;
-        return launch_merge(dtype, d_v, a, B, H, p.n_split, S_max, k, st);
+        // splits planned on the device from comp_len (dense_locate / dense_seq)
+        if (!ws) return hipErrorInvalidValue;
+        const int P = dense_parts(B);
+        a.dense_plan = 1;
+        a.n_seq = B;
+        a.n_split = kMaxSplit;  // the merge takes each sequence's split count from the plan
+        a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ml_bytes(P, 1, H));
+        a.dense_seq_plan = reinterpret_cast<int*>(a.part_o + (size_t)P * H * d_v);
+        hipError_t e = launch_p64<true>(a, dim3((unsigned)P, 1u, 1u), st);
+        if (e != hipSuccess) return e;
+        return launch_merge(dtype, d_v, a, B, H, 8, S_max, k, st);
     }
     const DecodePlan p = plan_decode(B, H, max_rows);
     a.rows_per_split = p.rows_per_split;

@@ -134,7 +134,8 @@ struct DecodePlan {
     int n_split;
 };
 DecodePlan plan_decode(int B, int H, int max_rows);
-size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows);
+// dense: the call may take the dense 64-head path (its device-planned splits)
+size_t decode_workspace_bytes(int B, int H, int d_v, int max_rows, bool dense);
 bool attn_shape_supported(int dtype, int d_qk, int d_v);
 // pg != nullptr (sparse mode only): swa_kv and comp_kv are the paged SWA and
 // C4 pools; the window of sequence b is the swa_len[b] tokens ending at

@@ -126,8 +126,8 @@ def test_decode_dense_64_heads_many_splits(oracle):
 
 
 def test_decode_dense_64_heads_one_split(oracle):
-    """256 sequences of up to 160 rows: the 64-head workgroups need one split each
-    and write the normalised output directly."""
+    """256 sequences of up to 160 rows: the device plan gives each one split of
+    up to three tiles (the merge then only normalises)."""
     g = torch.Generator().manual_seed(654)
     B, W, S = 256, 128, 32
     q = _rand((B, 64, 576), torch.bfloat16, g)
@@ -137,6 +137,21 @@ def test_decode_dense_64_heads_one_split(oracle):
     comp_len = torch.randint(0, S + 1, (B,), generator=g, dtype=torch.int32)
     _check_decode(oracle, q, swa, swa_len, comp, comp_len, 1.0 / 24.0, 512, None,
                   "dense 64-head one split")
+
+
+def test_decode_dense_64_heads_long_and_short(oracle):
+    """Three sequences, one 16,384 rows long: the device plan's tiles per split
+    are set by the split cap of the longest sequence (129 splits of two tiles
+    would exceed 128), the short ones get one or a few splits."""
+    g = torch.Generator().manual_seed(987)
+    B, W, S = 3, 128, 16384
+    q = _rand((B, 64, 576), torch.bfloat16, g)
+    swa = _rand((B, W, 576), torch.bfloat16, g)
+    comp = _rand((B, S, 576), torch.bfloat16, g)
+    swa_len = torch.tensor([128, 7, 128], dtype=torch.int32)
+    comp_len = torch.tensor([16384, 100, 9000], dtype=torch.int32)
+    _check_decode(oracle, q, swa, swa_len, comp, comp_len, 1.0 / 24.0, 512, None,
+                  "dense 64-head long and short")
 
 
 def test_decode_is_deterministic():
