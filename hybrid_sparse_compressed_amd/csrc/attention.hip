@@ -115,12 +115,12 @@ struct AttnArgs {
 
 // LDS footprint of one tile, in elements of T: K row-major, V^T (one row per
 // value channel; fp32 only), P^T (one row per head).  Every row carries a
-// 16-byte skew so that the 16 rows one MFMA operand reads fall on distinct
+// 32-byte skew so that the 16 rows one MFMA operand reads fall on distinct
 // banks.  bf16 tiles keep no V^T: the PV product reads the value columns out
 // of the row-major K rows with transposing LDS loads (kTr).
 template <typename T, int DQK, int DV> struct TileLds {
     static constexpr bool kTr = sizeof(T) == 2;
-    static constexpr int kSkew = 16 / (int)sizeof(T);
+    static constexpr int kSkew = 32 / (int)sizeof(T);  // 32 bytes (16 bytes measured 0.3 us slower per step)
     static constexpr int kStrideK = DQK + kSkew;
     static constexpr int kStrideT = kTile + kSkew;   // V^T and P^T rows
     static constexpr size_t kOffV = (size_t)kTile * kStrideK;
@@ -738,9 +738,13 @@ __device__ inline bool dense_locate(const AttnArgs& a, int R, int g, int* b, int
 // K rows (row-major; the PV product reads the value columns out of them with
 // transposing LDS loads) and P^T (one row per head, in p_pos order).
 template <int DQK, int DV> struct P64Lds {
-    static constexpr int kSkew = 8;             // 16 bytes of bf16
+    // row strides of 296 words (8 mod 32) for K and 36 words for P^T: a K-row
+    // skew of 16 bf16 (32 bytes) instead of 8 took the prefill_32k call from
+    // 3.25 to 2.90 ms in same-box runs (strides of 4, 12 or 20 words mod 32
+    // measured like 8 elements, 8 or 24 mod 32 like 16)
+    static constexpr int kSkew = 16;
     static constexpr int kStrideK = DQK + kSkew;
-    static constexpr int kStrideT = kP64Rows + kSkew;
+    static constexpr int kStrideT = kP64Rows + 8;
     static constexpr size_t kOffP = (size_t)kP64Rows * kStrideK;
     static constexpr size_t kBytes = (kOffP + (size_t)kP64Heads * kStrideT) * sizeof(bf16_t);
 };
