@@ -138,6 +138,31 @@ __device__ __forceinline__ int p_pos(int R) {
     return (R & ~31) + 8 * ((R >> 2) & 3) + 4 * ((R >> 4) & 1) + (R & 3);
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane
+// groups of one head column) with gfx950's row swaps: v_permlane16_swap
+// pairs 16-lane rows 0-1 and 2-3, v_permlane32_swap the two 32-lane halves;
+// each hands every lane its partner's value without an LDS round trip, and
+// both lanes of a pair combine the same two values (bitwise-equal results).
+__device__ __forceinline__ float quad4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// four P values -> bf16 with the hardware conversion (round to nearest even)
+__device__ __forceinline__ uint2 pack_p4(float a, float b, float c, float d) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 lo = {(__bf16)a, (__bf16)b}, hi = {(__bf16)c, (__bf16)d};
+    return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Rows of the PV contraction.  bf16: step ks takes tile rows 32*ks..32*ks+31,
 // lane group q the 8 rows 32*ks + 8*q + j.  fp32: step ks takes 4 rows, lane
 // group q row 16*q + ks, so a lane's rows over the 16 steps are contiguous.
@@ -519,8 +544,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             x[r] = v;
             wmax = fmaxf(wmax, v);
         }
-        wmax = fmaxf(wmax, __shfl_xor(wmax, 16, kWave));
-        wmax = fmaxf(wmax, __shfl_xor(wmax, 32, kWave));
+        wmax = quad4_max(wmax);
         float p[4];
         float wsum = 0.f;
 #pragma unroll
@@ -528,8 +552,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             p[r] = wmax == -INFINITY ? 0.f : exp2f(x[r] - wmax);
             wsum += p[r];
         }
-        wsum += __shfl_xor(wsum, 16, kWave);
-        wsum += __shfl_xor(wsum, 32, kWave);
+        wsum = quad4_sum(wsum);
         if (quad == 0) {
             red_m[wave][hl] = wmax;
             red_s[wave][hl] = wsum;
@@ -553,10 +576,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
         // P^T rows of this wave (bf16: in the PV k-slot order, p_pos; fp32: natural)
         if constexpr (sizeof(T) == 2) {
-            uint2 pk;
-            pk.x = (uint32_t)f32_to_bf16(p[0] * sc) | ((uint32_t)f32_to_bf16(p[1] * sc) << 16);
-            pk.y = (uint32_t)f32_to_bf16(p[2] * sc) | ((uint32_t)f32_to_bf16(p[3] * sc) << 16);
-            *reinterpret_cast<uint2*>(Pt + (size_t)hl * L::kStrideT + p_pos(wave * 16 + quad * 4)) = pk;
+            *reinterpret_cast<uint2*>(Pt + (size_t)hl * L::kStrideT + p_pos(wave * 16 + quad * 4)) =
+                pack_p4(p[0] * sc, p[1] * sc, p[2] * sc, p[3] * sc);
         } else {
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Pt) + (size_t)hl * L::kStrideT + wave * 16 + quad * 4) =
                 f32x4{p[0] * sc, p[1] * sc, p[2] * sc, p[3] * sc};
@@ -766,7 +787,7 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     T* Ks = reinterpret_cast<T*>(lds_raw);
     T* Pt = Ks + L::kOffP;
     __shared__ const T* row_ptr[kP64Chunk];        // row address, nullptr: no row
-    __shared__ int tile_any[kP64Chunk / kP64Rows];
+    __shared__ unsigned long long tile_mask[kP64Chunk / kP64Rows];  // valid rows of each tile
     __shared__ float red_m[2][kP64Heads], red_s[2][kP64Heads];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -783,6 +804,10 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             const int R = dense_tiles_per_split(a);
             int split, first;
             if (!dense_locate(a, R, (int)blockIdx.x, &b, &split, &first)) return;  // uniform
+            // uniform values: scalar registers (the vector ones are all taken by the tiles)
+            b = __builtin_amdgcn_readfirstlane(b);
+            split = __builtin_amdgcn_readfirstlane(split);
+            first = __builtin_amdgcn_readfirstlane(first);
             vr0 = split * R * kP64Rows;
             vr1 = vr0 + R * kP64Rows;
             part = first + split;
@@ -796,9 +821,9 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             vr1 = min(a.max_rows, vr0 + a.rows_per_split);
             part = b * a.n_split + (int)blockIdx.x;
         }
-        n_swa = a.swa_len[b];
+        n_swa = __builtin_amdgcn_readfirstlane(a.swa_len[b]);
         n_swa = n_swa < 0 ? 0 : (n_swa > a.W ? a.W : n_swa);
-        n_comp = a.comp_len[b];
+        n_comp = __builtin_amdgcn_readfirstlane(a.comp_len[b]);
         n_comp = n_comp < 0 ? 0 : (n_comp > a.S_max ? a.S_max : n_comp);
     } else {
         // queries go to XCDs in contiguous ranges (workgroup L runs on XCD L % 8),
@@ -865,19 +890,24 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 
     for (int c0 = vr0; c0 < vr1; c0 += kP64Chunk) {
         const int c1 = min(vr1, c0 + kP64Chunk);
-        {
-            const T* p = c0 == vr0 ? first_row : row_at(c0 + tid);
-            row_ptr[tid] = p;
+        const T* p_row = c0 == vr0 ? first_row : row_at(c0 + tid);
+        row_ptr[tid] = p_row;
+        {   // wave w's 64 threads hold the 64 rows of tile w of the chunk
+            static_assert(kP64Rows == kWave, "one tile per wave");
+            const unsigned long long m = __ballot(p_row != nullptr);
+            if (lane == 0) tile_mask[wave] = m;
         }
-        if (tid < kP64Chunk / kP64Rows) tile_any[tid] = 0;
-        __syncthreads();
-        if (row_ptr[tid] != nullptr) tile_any[tid / kP64Rows] = 1;  // benign race: all write 1
         __syncthreads();
 
         int pre = -1;
         for (int t0 = c0; t0 < c1; t0 += kP64Rows) {
             const int tb = t0 - c0;
-            if (!tile_any[tb / kP64Rows]) continue;  // uniform
+            // the tile's row mask, uniform: in scalar registers
+            const unsigned long long tm0 = tile_mask[tb / kP64Rows];
+            const unsigned long long tm =
+                ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(tm0 >> 32)) << 32) |
+                (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)tm0);
+            if (!tm) continue;  // uniform
             if (pre != tb) issue(tb);
 #pragma unroll
             for (int it = 0; it < kIter; ++it)
@@ -885,7 +915,7 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             __syncthreads();
             pre = -1;
             for (int nb = tb + kP64Rows; nb < c1 - c0; nb += kP64Rows) {
-                if (tile_any[nb / kP64Rows]) {
+                if (tile_mask[nb / kP64Rows]) {
                     issue(nb);
                     pre = nb;
                     break;
@@ -898,7 +928,9 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             for (int rb = 0; rb < 2; ++rb) {
                 f32x4 e0 = f32x4{0.f, 0.f, 0.f, 0.f}, e1 = f32x4{0.f, 0.f, 0.f, 0.f};
                 const T* krow = Ks + (size_t)(32 * half + 16 * rb + hl) * L::kStrideK;
-                constexpr int KG = NKK % 6 == 0 ? 6 : 1;  // K fragments read a group ahead
+                // K fragments read a group ahead (decode mode: groups of 3, its
+                // workgroups' other registers leave less room)
+                constexpr int KG = DEC ? (NKK % 3 == 0 ? 3 : 1) : (NKK % 6 == 0 ? 6 : 1);
 #pragma unroll
                 for (int g0 = 0; g0 < NKK; g0 += KG) {
                     u32x4 v[KG];
@@ -927,13 +959,12 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 32 * half + 16 * rb + 4 * quad + r;
-                    const float v = row_ptr[tb + row] != nullptr ? s[rb][r] * a.scale_log2 : -INFINITY;
+                    const float v = (tm >> row) & 1ull ? s[rb][r] * a.scale_log2 : -INFINITY;
                     x[4 * rb + r] = v;
                     wmax = fmaxf(wmax, v);
                 }
             }
-            wmax = fmaxf(wmax, __shfl_xor(wmax, 16, kWave));
-            wmax = fmaxf(wmax, __shfl_xor(wmax, 32, kWave));
+            wmax = quad4_max(wmax);
             float p[8];
             float wsum = 0.f;
 #pragma unroll
@@ -941,8 +972,7 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
                 p[r] = wmax == -INFINITY ? 0.f : exp2f(x[r] - wmax);
                 wsum += p[r];
             }
-            wsum += __shfl_xor(wsum, 16, kWave);
-            wsum += __shfl_xor(wsum, 32, kWave);
+            wsum = quad4_sum(wsum);
             if (quad == 0) {
                 red_m[half][head] = wmax;
                 red_s[half][head] = wsum;
@@ -961,10 +991,8 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {  // P^T in the PV k-slot order (p_pos)
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(p[4 * rb] * sc) | ((uint32_t)f32_to_bf16(p[4 * rb + 1] * sc) << 16);
-                pk.y = (uint32_t)f32_to_bf16(p[4 * rb + 2] * sc) | ((uint32_t)f32_to_bf16(p[4 * rb + 3] * sc) << 16);
-                *reinterpret_cast<uint2*>(Pt + (size_t)head * L::kStrideT + p_pos(32 * half + 16 * rb + 4 * quad)) = pk;
+                *reinterpret_cast<uint2*>(Pt + (size_t)head * L::kStrideT + p_pos(32 * half + 16 * rb + 4 * quad)) =
+                    pack_p4(p[4 * rb] * sc, p[4 * rb + 1] * sc, p[4 * rb + 2] * sc, p[4 * rb + 3] * sc);
             }
             if (__ballot(move && l_run > 0.f)) {
 #pragma unroll
