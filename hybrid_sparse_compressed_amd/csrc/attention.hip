@@ -688,7 +688,7 @@ constexpr int kP64Threads = 512;
 constexpr int kP64Waves = kP64Threads / kWave;
 constexpr int kP64Heads = 64;
 constexpr int kP64Rows = 64;                    // rows per tile
-constexpr int kP64Chunk = kP64Threads;          // rows listed at once (one per thread)
+constexpr int kP64Chunk = 2 * kP64Threads;      // rows listed at once (two per thread)
 
 // ---- dense decode splits planned on the device --------------------------------
 // Sequence b has t_b = ceil((W + comp_len[b]) / 64) tiles (comp_len clamped to
@@ -756,18 +756,18 @@ __device__ inline bool dense_locate(const AttnArgs& a, int R, int g, int* b, int
 // listed 512 at a time as device addresses (0: not a row of this query), and
 // the next tile's rows are loaded into registers while a tile is computed.
 
-// K rows (row-major; the PV product reads the value columns out of them with
-// transposing LDS loads) and P^T (one row per head, in p_pos order).
+// Two buffers of K rows (row-major; the PV product reads the value columns
+// out of them with transposing LDS loads, and P^T, one row per head in p_pos
+// order, goes into the columns past DV of the buffer's first 64 rows).
 template <int DQK, int DV> struct P64Lds {
-    // row strides of 296 words (8 mod 32) for K and 36 words for P^T: a K-row
-    // skew of 16 bf16 (32 bytes) instead of 8 took the prefill_32k call from
-    // 3.25 to 2.90 ms in same-box runs (strides of 4, 12 or 20 words mod 32
-    // measured like 8 elements, 8 or 24 mod 32 like 16)
+    // row stride of 296 words (8 mod 32): a K-row skew of 16 bf16 (32 bytes)
+    // instead of 8 took the prefill_32k call from 3.25 to 2.90 ms in same-box
+    // runs (strides of 4, 12 or 20 words mod 32 measured like 8 elements, 8
+    // or 24 mod 32 like 16)
     static constexpr int kSkew = 16;
     static constexpr int kStrideK = DQK + kSkew;
-    static constexpr int kStrideT = kP64Rows + 8;
-    static constexpr size_t kOffP = (size_t)kP64Rows * kStrideK;
-    static constexpr size_t kBytes = (kOffP + (size_t)kP64Heads * kStrideT) * sizeof(bf16_t);
+    static constexpr size_t kOffB = (size_t)kP64Rows * kStrideK;  // second buffer
+    static constexpr size_t kBytes = 2 * kOffB * sizeof(bf16_t);
 };
 
 template <int DQK, int DV, bool DEC>
@@ -785,7 +785,6 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 
     extern __shared__ __align__(16) unsigned char lds_raw[];
     T* Ks = reinterpret_cast<T*>(lds_raw);
-    T* Pt = Ks + L::kOffP;
     __shared__ const T* row_ptr[kP64Chunk];        // row address, nullptr: no row
     __shared__ unsigned long long tile_mask[kP64Chunk / kP64Rows];  // valid rows of each tile
     __shared__ float red_m[2][kP64Heads], red_s[2][kP64Heads];
@@ -857,7 +856,12 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             ci = j;
         return (ci >= 0 && ci < n_comp) ? comp + ((size_t)b * a.S_max + ci) * DQK : nullptr;
     };
-    const T* first_row = row_at(vr0 + tid);  // index loads before the Q loads
+    // index loads before the Q loads (decode mode: the first row of each
+    // thread only, its other registers leave less room)
+    constexpr int kFirst = DEC ? 1 : kP64Chunk / kP64Threads;
+    const T* first_row[kFirst];
+#pragma unroll
+    for (int i = 0; i < kFirst; ++i) first_row[i] = row_at(vr0 + i * kP64Threads + tid);
 
     typename M::frag qf[NKK];
     {
@@ -887,47 +891,62 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
         for (int it = 0; it < kIter; ++it)
             ga[it] = pr ? *reinterpret_cast<const u32x4*>(src + 8 * it * V16) : u32x4{0u, 0u, 0u, 0u};
     };
+    auto store = [&](T* buf) {
+#pragma unroll
+        for (int it = 0; it < kIter; ++it)
+            *reinterpret_cast<u32x4*>(buf + (size_t)(tid >> 3) * L::kStrideK + ((tid & 7) + 8 * it) * V16) = ga[it];
+    };
 
+    // Two K buffers: tile j is computed from buffer j mod 2 while tile j + 1,
+    // loaded into registers during tile j - 1, is stored into the other one
+    // between the tile's two barriers (its last reader, the PV product of
+    // tile j - 1, has finished everywhere by the first).  Once the QK product
+    // is done the K columns past DV are free and hold P^T of the tile.
+    static_assert(DQK - DV >= kP64Rows && kP64Heads <= kP64Rows, "P^T in the rope columns");
+    int cur = 0;
     for (int c0 = vr0; c0 < vr1; c0 += kP64Chunk) {
         const int c1 = min(vr1, c0 + kP64Chunk);
-        const T* p_row = c0 == vr0 ? first_row : row_at(c0 + tid);
-        row_ptr[tid] = p_row;
-        {   // wave w's 64 threads hold the 64 rows of tile w of the chunk
+        const int ntile = ceil_div(c1 - c0, kP64Rows);
+#pragma unroll
+        for (int i = 0; i < kP64Chunk / kP64Threads; ++i) {
+            const int r = i * kP64Threads + tid;
+            const T* p_row = c0 == vr0 && i < kFirst ? first_row[i < kFirst ? i : 0] : row_at(c0 + r);
+            row_ptr[r] = p_row;
+            // wave w's 64 threads hold the 64 rows of tile 8 i + w of the chunk
             static_assert(kP64Rows == kWave, "one tile per wave");
             const unsigned long long m = __ballot(p_row != nullptr);
-            if (lane == 0) tile_mask[wave] = m;
+            if (lane == 0) tile_mask[i * kP64Waves + wave] = m;
         }
         __syncthreads();
+        // the chunk's tiles with a row, one bit each (uniform)
+        static_assert(kP64Chunk / kP64Rows <= kWave, "tile bits");
+        const unsigned long long live = __ballot(lane < ntile && tile_mask[lane < ntile ? lane : 0] != 0ull);
+        auto next_tile = [&](int j) -> int {  // first live tile >= j, or -1
+            const unsigned long long r = j < 64 ? live >> j : 0ull;
+            return r ? j + (int)__builtin_ctzll(r) : -1;
+        };
+        int tj = next_tile(0);
+        if (tj < 0) continue;  // uniform
+        issue(tj * kP64Rows);
+        store(Ks + (size_t)cur * L::kOffB);
+        __syncthreads();
+        int nj = next_tile(tj + 1);
+        if (nj >= 0) issue(nj * kP64Rows);
 
-        int pre = -1;
-        for (int t0 = c0; t0 < c1; t0 += kP64Rows) {
-            const int tb = t0 - c0;
+        for (; tj >= 0; cur ^= 1) {
+            T* Kc = Ks + (size_t)cur * L::kOffB;
             // the tile's row mask, uniform: in scalar registers
-            const unsigned long long tm0 = tile_mask[tb / kP64Rows];
+            const unsigned long long tm0 = tile_mask[tj];
             const unsigned long long tm =
                 ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(tm0 >> 32)) << 32) |
                 (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)tm0);
-            if (!tm) continue;  // uniform
-            if (pre != tb) issue(tb);
-#pragma unroll
-            for (int it = 0; it < kIter; ++it)
-                *reinterpret_cast<u32x4*>(Ks + (size_t)(tid >> 3) * L::kStrideK + ((tid & 7) + 8 * it) * V16) = ga[it];
-            __syncthreads();
-            pre = -1;
-            for (int nb = tb + kP64Rows; nb < c1 - c0; nb += kP64Rows) {
-                if (tile_mask[nb / kP64Rows]) {
-                    issue(nb);
-                    pre = nb;
-                    break;
-                }
-            }
 
             // ---- S^T for rows 32*half + 16*rb + 4*quad + r, head hl
             f32x4 s[2];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 f32x4 e0 = f32x4{0.f, 0.f, 0.f, 0.f}, e1 = f32x4{0.f, 0.f, 0.f, 0.f};
-                const T* krow = Ks + (size_t)(32 * half + 16 * rb + hl) * L::kStrideK;
+                const T* krow = Kc + (size_t)(32 * half + 16 * rb + hl) * L::kStrideK;
                 // K fragments read a group ahead (decode mode: groups of 3, its
                 // workgroups' other registers leave less room)
                 constexpr int KG = DEC ? (NKK % 3 == 0 ? 3 : 1) : (NKK % 6 == 0 ? 6 : 1);
@@ -954,12 +973,13 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             // two halves of the head block meet in LDS
             float x[8];
             float wmax = -INFINITY;
+            // bit 16 rb + r: row 32 half + 16 rb + 4 quad + r of the tile
+            const uint32_t tmr = (uint32_t)(tm >> (32 * half + 4 * quad));
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 32 * half + 16 * rb + 4 * quad + r;
-                    const float v = (tm >> row) & 1ull ? s[rb][r] * a.scale_log2 : -INFINITY;
+                    const float v = (tmr >> (16 * rb + r)) & 1u ? s[rb][r] * a.scale_log2 : -INFINITY;
                     x[4 * rb + r] = v;
                     wmax = fmaxf(wmax, v);
                 }
@@ -978,20 +998,32 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
                 red_s[half][head] = wsum;
             }
             __syncthreads();
-            const float tmax = fmaxf(red_m[0][head], red_m[1][head]);
+            float rm[2], rs[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                rm[h2] = red_m[h2][head];
+                rs[h2] = red_s[h2][head];
+            }
+            // the next tile into the other buffer, and the one after it into registers
+            int nn = -1;
+            if (nj >= 0) {
+                store(Ks + (size_t)(cur ^ 1) * L::kOffB);
+                nn = next_tile(nj + 1);
+                if (nn >= 0) issue(nn * kP64Rows);
+            }
+            const float tmax = fmaxf(rm[0], rm[1]);
             const bool move = tmax > m_run + 8.f;   // lazy rescale, p stays <= 2^8
             const float m_new = move ? tmax : m_run;
             const float alpha = move ? exp2f(m_run - m_new) : 1.f;
             float tsum = 0.f;
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const float mw = red_m[h2][head];
-                if (mw != -INFINITY) tsum += red_s[h2][head] * exp2f(mw - m_new);
-            }
+            for (int h2 = 0; h2 < 2; ++h2)
+                if (rm[h2] != -INFINITY) tsum += rs[h2] * exp2f(rm[h2] - m_new);
             const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
+            T* pbase = Kc + (size_t)head * L::kStrideK + DV;  // P^T row of this head
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {  // P^T in the PV k-slot order (p_pos)
-                *reinterpret_cast<uint2*>(Pt + (size_t)head * L::kStrideT + p_pos(32 * half + 16 * rb + 4 * quad)) =
+                *reinterpret_cast<uint2*>(pbase + p_pos(32 * half + 16 * rb + 4 * quad)) =
                     pack_p4(p[4 * rb] * sc, p[4 * rb + 1] * sc, p[4 * rb + 2] * sc, p[4 * rb + 3] * sc);
             }
             if (__ballot(move && l_run > 0.f)) {
@@ -1004,8 +1036,7 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 
             // ---- O^T[channels 256*half + 16t.., head] += V^T * P^T; V^T
             // fragments by transposing reads of the K rows (as attn_kernel)
-            const T* vtr = Ks + (size_t)(4 * quad + ((lane & 15) >> 2)) * L::kStrideK + half * DW + 4 * (lane & 3);
-            const T* pbase = Pt + (size_t)head * L::kStrideT;
+            const T* vtr = Kc + (size_t)(4 * quad + ((lane & 15) >> 2)) * L::kStrideK + half * DW + 4 * (lane & 3);
 #pragma unroll
             for (int ks = 0; ks < kP64Rows / 32; ++ks) {
                 const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(pbase + ks * 32 + quad * 8));
@@ -1026,7 +1057,8 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
                         acc[t0 + j] = M::mma(__builtin_bit_cast(bf16x8, vv[j]), pf, acc[t0 + j]);
                 }
             }
-            __syncthreads();  // the tile buffers are rewritten next
+            tj = nj;
+            nj = nn;
         }
     }
 
