@@ -756,6 +756,10 @@ __device__ inline bool dense_locate(const AttnArgs& a, int R, int g, int* b, int
 // listed 512 at a time as device addresses (0: not a row of this query), and
 // the next tile's rows are loaded into registers while a tile is computed.
 
+// A row of zeros (never written): the gather reads it for a missing row.
+constexpr int kP64ZeroRow = 1024;  // bf16 elements
+__device__ __align__(16) uint16_t g_p64_zero_row[kP64ZeroRow];
+
 // Two buffers of K rows (row-major; the PV product reads the value columns
 // out of them with transposing LDS loads, and P^T, one row per head in p_pos
 // order, goes into the columns past DV of the buffer's first 64 rows).
@@ -884,13 +888,18 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     static_assert(CPR % 8 == 0 && kP64Rows * 8 == kP64Threads, "gather map");
     constexpr int kIter = CPR / 8;
     u32x4 ga[kIter];
-    auto issue = [&](int tb) {
-        const T* pr = row_ptr[tb + (tid >> 3)];
-        const T* src = (pr ? pr : reinterpret_cast<const T*>(a.q)) + (tid & 7) * V16;
+    // loads it0 .. it1 - 1 of this thread's row pr (nullptr: the zero row).
+    // Global (not flat) loads with no select on the data: a flat load also
+    // counts against the LDS wait counter, and a select would wait for it.
+    static_assert(DQK <= kP64ZeroRow, "zero row");
+    typedef const __attribute__((address_space(1))) u32x4 gu32x4;
+    auto issue_part = [&](const T* pr, int it0, int it1) {
+        const T* src = (pr ? pr : reinterpret_cast<const T*>(g_p64_zero_row)) + (tid & 7) * V16;
 #pragma unroll
-        for (int it = 0; it < kIter; ++it)
-            ga[it] = pr ? *reinterpret_cast<const u32x4*>(src + 8 * it * V16) : u32x4{0u, 0u, 0u, 0u};
+        for (int it = it0; it < it1; ++it)
+            ga[it] = *(gu32x4*)(src + 8 * it * V16);
     };
+    auto issue = [&](int tb) { issue_part(row_ptr[tb + (tid >> 3)], 0, kIter); };
     auto store = [&](T* buf) {
 #pragma unroll
         for (int it = 0; it < kIter; ++it)
@@ -1005,11 +1014,17 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
                 rs[h2] = red_s[h2][head];
             }
             // the next tile into the other buffer, and the one after it into registers
+            // the next tile into the other buffer; the tile after it is
+            // loaded into registers during the PV product below, a load per
+            // group of MFMAs, so that the vector memory unit (about 16 cycles
+            // per 1 KB wave load) works under the MFMAs instead of holding up
+            // this phase
             int nn = -1;
+            const T* nn_row = nullptr;
             if (nj >= 0) {
                 store(Ks + (size_t)(cur ^ 1) * L::kOffB);
                 nn = next_tile(nj + 1);
-                if (nn >= 0) issue(nn * kP64Rows);
+                if (nn >= 0) nn_row = row_ptr[nn * kP64Rows + (tid >> 3)];
             }
             const float tmax = fmaxf(rm[0], rm[1]);
             const bool move = tmax > m_run + 8.f;   // lazy rescale, p stays <= 2^8
@@ -1055,6 +1070,10 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
 #pragma unroll
                     for (int j = 0; j < VG; ++j)
                         acc[t0 + j] = M::mma(__builtin_bit_cast(bf16x8, vv[j]), pf, acc[t0 + j]);
+                    // group g of the PV product issues loads [kIter g / G, kIter (g + 1) / G)
+                    constexpr int G = (kP64Rows / 32) * (NMT / VG);
+                    const int g = ks * (NMT / VG) + t0 / VG;
+                    if (nn >= 0) issue_part(nn_row, kIter * g / G, kIter * (g + 1) / G);  // uniform
                 }
             }
             tj = nj;
