@@ -244,12 +244,33 @@ def copy_calibration(torch, dev, mib):
     del src, dst
 
 
+ROW_WARM_MS = 40.0
+
+
+def _warm(torch, fn, warm_ms=ROW_WARM_MS):
+    """Back-to-back calls of fn() for at least warm_ms of wall time.  The GPU's
+    core clock ramps up over a few tens of milliseconds of sustained work (an
+    MI355X prefill attention call measured 2.93 ms right after an idle pause and
+    2.32 ms ten calls later), so every row is timed at its steady-state clock."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+                break
+    torch.cuda.synchronize()
+
+
 def _median_us(torch, fn, reps, inner=1):
     """Median time per call of fn() on the current stream, in microseconds: reps
-    measurements of `inner` back-to-back calls each (one warm-up call first), so that
-    short calls are timed as a stream of calls, not with the host's launch latency."""
-    fn()
-    torch.cuda.synchronize()
+    measurements of `inner` back-to-back calls each (after a steady-state warm-up,
+    _warm), so that short calls are timed as a stream of calls, not with the host's
+    launch latency."""
+    _warm(torch, fn)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     ts = []
@@ -279,8 +300,7 @@ def _graph_us(torch, fn, reps, inner):
     with torch.cuda.graph(g):
         for _ in range(inner):
             fn()
-    g.replay()
-    torch.cuda.synchronize()
+    _warm(torch, g.replay)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     ts = []
@@ -340,7 +360,7 @@ def other_rows(hsa, workloads):
     lse = torch.empty((n_seq, 2048, 64), dtype=torch.float32, device="cuda")
     us = _median_us(torch, lambda: hsa.hsa_attn_prefill(w["q"], w["x"], c4, w["q_start"], 128, 4,
                                                         w["scale"], 512, comp_idx=idx, out=out,
-                                                        lse=lse), 3)
+                                                        lse=lse), 5)
     flop = Nq * 64 * (128 + k) * (576 + 512) * 2
     rows["a5_prefill_attention"] = _row("prefill_32k", us, "mfma", flop, "TFLOP/s", 2500.0)
     del w, c4, c128, scores, idx, out, lse
