@@ -1099,12 +1099,9 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     T* o = reinterpret_cast<T*>(a.out) + orow * DV + half * DW;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-    for (int t = 0; t < NMT; ++t) {
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(acc[t][0] * inv) | ((uint32_t)f32_to_bf16(acc[t][1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(acc[t][2] * inv) | ((uint32_t)f32_to_bf16(acc[t][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(o + t * 16 + quad * 4) = pk;
-    }
+    for (int t = 0; t < NMT; ++t)  // hardware conversion (nearest-even, NaN stays NaN): two per instruction
+        *reinterpret_cast<uint2*>(o + t * 16 + quad * 4) =
+            pack_p4(acc[t][0] * inv, acc[t][1] * inv, acc[t][2] * inv, acc[t][3] * inv);
     if (a.lse && half == 0 && quad == 0)
         a.lse[orow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
