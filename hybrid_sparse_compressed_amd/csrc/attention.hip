@@ -752,9 +752,10 @@ __device__ inline bool dense_locate(const AttnArgs& a, int R, int g, int* b, int
 // column block) and half w / 4 of the work: tile rows 32*half..+31 in the QK
 // product and value channels 256*half..+255 in the PV product.  The two waves
 // of a head block meet in LDS for the per-head (max, sum) of the tile; the
-// rest is the tile pipeline of attn_kernel (same operand layouts).  Rows are
-// listed 512 at a time as device addresses (0: not a row of this query), and
-// the next tile's rows are loaded into registers while a tile is computed.
+// operand layouts are those of attn_kernel.  Rows are listed 1024 at a time
+// as device addresses (0: not a row of this query).  Two tile buffers: tile
+// j + 1 is stored into the free one while tile j is computed, and tile
+// j + 2 is loaded into registers during tile j's PV product.
 
 // A row of zeros (never written): the gather reads it for a missing row.
 constexpr int kP64ZeroRow = 1024;  // bf16 elements
