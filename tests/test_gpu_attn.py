@@ -214,6 +214,29 @@ def test_prefill_dense_many_chunks(oracle):
     compare(lse, rl, (1e-3, 1e-4), "prefill dense chunks lse")
 
 
+def test_prefill_sparse_long_lists_with_empty_tiles(oracle):
+    """64-head prefill with k = 2048 (W + k = 2176 rows: three row-list chunks of
+    1024 / 1024 / 128), an empty 64-row tile inside the first chunk, a second chunk
+    with no row at all (the tile pipeline restarts after it) and the last chunk
+    valid; the tile buffers alternate across all of it."""
+    g = torch.Generator().manual_seed(321)
+    n_seq, T, n_q, W, m, H, k = 1, 9000, 4, 128, 4, 64, 2048
+    q_start = T - n_q
+    S = T // m
+    q = _rand((n_seq, n_q, H, 576), torch.bfloat16, g)
+    kv = _rand((n_seq, T, 576), torch.bfloat16, g)
+    comp = _rand((n_seq, S, 576), torch.bfloat16, g)
+    idx = torch.stack([torch.randperm(S - 10, generator=g)[:k] for _ in range(n_q)]).to(torch.int32)
+    idx[:, 256:320] = -1      # rows W + 256 .. W + 319: tile 6 of the first chunk
+    idx[:, 896:1920] = -1     # every row of the second chunk
+    idx[1, 1920:] = -1        # query 1: the last chunk empty as well
+    note("prefill sparse k=2048 with empty tiles and chunks")
+    o, lse = _prefill(q, kv, comp, q_start, W, m, 0.04, 512, idx)
+    ro, rl = oracle.attn_prefill(q, kv, comp, q_start, W, m, 0.04, 512, comp_idx=idx.numpy())
+    compare(o.reshape(n_q, H, 512), ro, TOL_BF16, "prefill long lists out")
+    compare(lse, rl, (1e-3, 1e-4), "prefill long lists lse")
+
+
 def test_prefill_window_start(oracle):
     """Queries at positions 0..39: windows shorter than W, few visible blocks."""
     g = torch.Generator().manual_seed(99)
