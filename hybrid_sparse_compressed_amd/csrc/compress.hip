@@ -14,9 +14,10 @@
 //    (as many as fit at once) and walk the units tile by tile with the next
 //    tile's rows in flight; a thread keeps its chunk from tile to tile, so its
 //    bias words are loaded once.
-//  * larger m (C128): P = 8 threads split a block's rows into contiguous
-//    ranges, each walking its range two rows at a time with the next two in
-//    flight; the partial (max, sum, weighted sum) triples are merged in LDS
+//  * larger m (C128): P = 4 threads split a block's rows into contiguous
+//    ranges (32 rows each at m = 128), each walking its range two rows at a
+//    time with the next two in flight (4 threads per unit measured faster
+//    than 2, 8 or 16, and two rows per step faster than three or four); the partial (max, sum, weighted sum) triples are merged in LDS
 //    in a fixed order, every thread merging some (unit, channel) pairs.
 // Registers are kept at <= 128 per lane (four waves per SIMD): the latents
 // stay packed until their product is taken, and entries leave as one
@@ -315,7 +316,7 @@ template <typename T>
 hipError_t launch_compress_t(const void* x, const void* g, const void* bias, void* out, int B,
                              int T_len, int D, int m, hipStream_t st) {
     if (m <= 4) return launch_compress_short<T, 4>(x, g, bias, out, B, T_len, D, m, st);
-    return launch_compress_p<T, 8, 2>(x, g, bias, out, B, T_len, D, m, st);
+    return launch_compress_p<T, 4, 2>(x, g, bias, out, B, T_len, D, m, st);
 }
 
 // ---- decode-time compression state ----
