@@ -15,13 +15,14 @@
 //    tile's rows in flight; a thread keeps its chunk from tile to tile, so its
 //    bias words are loaded once.
 //  * larger m (C128): P = 4 threads split a block's rows into contiguous
-//    ranges (32 rows each at m = 128), each walking its range two rows at a
-//    time with the next two in flight (4 threads per unit measured faster
-//    than 2, 8 or 16, and two rows per step faster than three or four); the partial (max, sum, weighted sum) triples are merged in LDS
+//    ranges (32 rows each at m = 128), each walking its range four rows at a
+//    time with the next four in flight (4 threads per unit measured faster
+//    than 2, 8 or 16, and four rows per step faster than two or three); the partial (max, sum, weighted sum) triples are merged in LDS
 //    in a fixed order, every thread merging some (unit, channel) pairs.
-// Registers are kept at <= 128 per lane (four waves per SIMD): the latents
-// stay packed until their product is taken, and entries leave as one
-// 16-byte store per chunk.
+// The short-block kernel keeps its registers at <= 128 per lane (four waves
+// per SIMD; the C128 kernel's four rows in flight take 163, three waves):
+// the latents stay packed until their product is taken, and entries leave as
+// one 16-byte store per chunk.
 #include "compress_append.hpp"
 #include "hsa_common.hpp"
 #include "hsa_internal.hpp"
@@ -73,23 +74,25 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
         const int j0 = part * rp;
         const int j1 = min(m, j0 + rp);
         const size_t row0 = (size_t)b * T_len + (size_t)m * i;
-        // the G rows from j on (rows past j1 are not loaded)
+        // the G rows from j on.  Every load is issued (a row past the part's
+        // range reloads the block's last row and is masked below): a load
+        // under a branch would make the compiler wait for the next group's
+        // loads too before this group's arithmetic.
         auto load = [&](RowGroupB<G>& rg, int j) {
 #pragma unroll
             for (int r = 0; r < G; ++r) {
-                if (j + r < j1) {
-                    const size_t off = (row0 + j + r) * (size_t)D + (size_t)c * V;
-                    rg.g[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gate + off));
-                    rg.x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));
-                    rg.b[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)(j + r) * D + (size_t)c * V);
-                }
+                const int jr = min(j + r, m - 1);
+                const size_t off = (row0 + jr) * (size_t)D + (size_t)c * V;
+                rg.g[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gate + off));
+                rg.x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));
+                rg.b[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)jr * D + (size_t)c * V);
             }
         };
         RowGroupB<G> cur;
-        if (j0 < j1) load(cur, j0);
+        load(cur, j0);
         for (int j = j0; j < j1; j += G) {
             RowGroupB<G> nxt;
-            if (j + G < j1) load(nxt, j + G);  // next group in flight during this one
+            load(nxt, j + G);  // next group in flight during this one
             float z[G][V];
             const int g = min(G, j1 - j);
 #pragma unroll
@@ -184,38 +187,42 @@ __global__ __launch_bounds__(kCompressThreads) void compress_short_kernel(
     const long long nunits = (long long)B * nblk * nchunk;
     const long long ntiles = (nunits + kCompressThreads - 1) / kCompressThreads;
     const long long stride = gridDim.x;
+    // Every load is issued, from a clamped unit and row (a unit past the end
+    // reloads the last unit, a row past m the block's last row; neither is
+    // used): a load under a branch would make the compiler wait for the next
+    // tile's loads too before this tile's arithmetic.
     auto load = [&](RowGroup<G>& rg, long long t) {
-        const long long unit = t * kCompressThreads + threadIdx.x;
-        if (unit >= nunits) return;
+        const long long unit = min(t * kCompressThreads + (long long)threadIdx.x, nunits - 1);
         const int c = (int)(unit % nchunk);
         const long long bi = unit / nchunk;
         const size_t row0 = (size_t)(bi / nblk) * T_len + (size_t)m * (bi % nblk);
 #pragma unroll
         for (int r = 0; r < G; ++r) {
-            if (r < m) {
-                const size_t off = (row0 + r) * (size_t)D + (size_t)c * V;
-                rg.g[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gate + off));
-                rg.x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));
-            }
+            const size_t off = (row0 + min(r, m - 1)) * (size_t)D + (size_t)c * V;
+            rg.g[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gate + off));
+            rg.x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));
         }
     };
     u32x4 bw[G];
     auto load_bias = [&](int c) {
 #pragma unroll
         for (int r = 0; r < G; ++r)
-            if (r < m) bw[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)r * D + (size_t)c * V);
+            bw[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)min(r, m - 1) * D + (size_t)c * V);
     };
     long long t = blockIdx.x;
-    if (fixed_chunk) load_bias((int)((t * kCompressThreads + threadIdx.x) % nchunk));
+    if (fixed_chunk) load_bias((int)(min(t * kCompressThreads + (long long)threadIdx.x, nunits - 1) % nchunk));
     RowGroup<G> cur;
-    if (t < ntiles) load(cur, t);
+    load(cur, t);
     for (; t < ntiles; t += stride) {
+        // a thread whose chunk changes from tile to tile loads this tile's
+        // bias words before the next tile's rows (the count retires in order)
+        if (!fixed_chunk)
+            load_bias((int)(min(t * kCompressThreads + (long long)threadIdx.x, nunits - 1) % nchunk));
         RowGroup<G> nxt;
-        if (t + stride < ntiles) load(nxt, t + stride);
+        load(nxt, min(t + stride, ntiles - 1));
         const long long unit = t * kCompressThreads + threadIdx.x;
         if (unit < nunits) {
             const int c = (int)(unit % nchunk);
-            if (!fixed_chunk) load_bias(c);
             float z[G][V];
 #pragma unroll
             for (int r = 0; r < G; ++r) {
@@ -316,7 +323,7 @@ template <typename T>
 hipError_t launch_compress_t(const void* x, const void* g, const void* bias, void* out, int B,
                              int T_len, int D, int m, hipStream_t st) {
     if (m <= 4) return launch_compress_short<T, 4>(x, g, bias, out, B, T_len, D, m, st);
-    return launch_compress_p<T, 4, 2>(x, g, bias, out, B, T_len, D, m, st);
+    return launch_compress_p<T, 4, 4>(x, g, bias, out, B, T_len, D, m, st);
 }
 
 // ---- decode-time compression state ----
