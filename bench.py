@@ -175,6 +175,25 @@ def main():
     # the dominant kernel's duration come from the same launches
     ms_instr, breakdown = instrumented(sum(fams.values()))
 
+    # what the memory system delivers to the scoring kernel's launch shape: a plain
+    # read of the same key bytes (512 workgroups, one contiguous 512 KB part each;
+    # the two copies alternating as in the steps), timed by the same event pairs
+    stream_us = None
+    kb = [sets[0][1], sets[1][1]]
+    if (kb[0].numel() * kb[0].element_size()) % (16 << 20) == 0:
+        sink = torch.empty(4096, dtype=torch.uint8, device=dev)
+        for i in range(8):
+            hsa.hsa_stream_read(kb[i & 1], sink)
+        torch.cuda.synchronize()
+        hsa.hsa_profile_read(hsa.HSA_PROF_STREAM, reset=True)
+        hsa.hsa_profile_enable(hsa.HSA_PROF_STREAM)
+        for i in range(args.steps):
+            hsa.hsa_stream_read(kb[i & 1], sink)
+        torch.cuda.synchronize()
+        hsa.hsa_profile_enable(0)
+        tot, n = hsa.hsa_profile_read(hsa.HSA_PROF_STREAM, reset=True)
+        stream_us = round(1000.0 * tot / n, 3) if n else None
+
     # roofline of the dominant kernel (indexer scoring): algorithmic bytes per launch
     alg_bytes = B * S * d_I * 2 + B * H_I * d_I * 2
     score_us = breakdown["score"]["avg_us"]
@@ -189,6 +208,12 @@ def main():
                 "scope": "dominant kernel",
                 "kernel": "score_kernel (indexer scores, first-digit histogram, candidate lists)",
                 "avg_us": score_us, "alg_bytes_per_launch": alg_bytes}
+    if stream_us:
+        kbytes = kb[0].numel() * kb[0].element_size()
+        roofline["plain_read"] = {
+            "what": "hsa_stream_read of the same %d key bytes in the same launch shape" % kbytes,
+            "avg_us": stream_us, "GBps": round(kbytes / (stream_us * 1e-6) / 1e9, 1),
+            "score_kernel_vs_plain_read": round(stream_us / score_us, 4)}
 
     # the whole layer-step against the same peak: its algorithmic bytes over the
     # timed step time (the metric's own roofline)

@@ -17,7 +17,7 @@ _BINDING_NAMES = (
     "PageMaps", "hsa_index_topk_weighted", "hsa_decode_sparse_weighted", "hsa_compress_overlap",
     "hsa_compress_append_overlap", "lib", "strerror",
     "hsa_profile_enable", "hsa_profile_read", "HSA_PROF_COMPRESS", "HSA_PROF_SCORE",
-    "HSA_PROF_SELECT", "HSA_PROF_ATTN", "HSA_PROF_MERGE",
+    "HSA_PROF_SELECT", "HSA_PROF_ATTN", "HSA_PROF_MERGE", "HSA_PROF_STREAM", "hsa_stream_read",
 )
 
 __all__ = list(_BINDING_NAMES)

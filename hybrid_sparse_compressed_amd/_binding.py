@@ -26,9 +26,10 @@ EXPORTED = (
     "hsa_attn_prefill_workspace_size", "hsa_attn_prefill", "hsa_decode_sparse_workspace_size",
     "hsa_decode_sparse", "hsa_decode_step", "hsa_decode_step_noalloc", "hsa_decode_step_paged",
     "hsa_index_topk_weighted", "hsa_decode_sparse_weighted", "hsa_compress_overlap",
-    "hsa_compress_append_overlap", "hsa_profile_enable", "hsa_profile_read",
+    "hsa_compress_append_overlap", "hsa_profile_enable", "hsa_profile_read", "hsa_stream_read",
 )
 HSA_PROF_COMPRESS, HSA_PROF_SCORE, HSA_PROF_SELECT, HSA_PROF_ATTN, HSA_PROF_MERGE = 1, 2, 4, 8, 16
+HSA_PROF_STREAM = 32
 
 
 class PageMaps(ctypes.Structure):
@@ -102,6 +103,8 @@ def _load():
     lib.hsa_profile_read.argtypes = [ctypes.c_uint, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_longlong), I]
     lib.hsa_profile_read.restype = I
+    lib.hsa_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.hsa_stream_read.restype = I
     return lib
 
 
@@ -596,3 +599,16 @@ def hsa_profile_read(family: int, reset: bool = False):
     _check("hsa_profile_read", lib.hsa_profile_read(int(family), ctypes.byref(ms), ctypes.byref(n),
                                                     1 if reset else 0))
     return ms.value, n.value
+
+
+def hsa_stream_read(src, sink=None, stream=None):
+    """Plain read of the whole of src (a device tensor whose size is a multiple of
+    16 MiB) in the decode scoring kernel's launch shape: a read-bandwidth reference
+    for that kernel.  sink: 4096-byte device scratch (allocated when None)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("hsa_stream_read: src must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(4096, dtype=torch.uint8, device=src.device)
+    _check("hsa_stream_read", lib.hsa_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                                  _ptr(sink), _stream(stream)))
+    return sink

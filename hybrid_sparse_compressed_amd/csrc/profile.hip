@@ -7,6 +7,7 @@
 // returns the pairs to the pool.  Nothing is recorded while no family is
 // armed, so the hot path pays one relaxed atomic load per launch.
 #include "../../include/hsa_attn.h"
+#include "hsa_common.hpp"
 #include "hsa_internal.hpp"
 
 #include <atomic>
@@ -45,6 +46,32 @@ int family_index(unsigned fam) {
     for (int i = 0; i < kFamilies; ++i)
         if (fam == (1u << i)) return i;
     return -1;
+}
+
+// Calibration read: workgroup g streams the g-th of kStreamWG equal contiguous
+// parts with 16-byte non-temporal loads, eight per lane in flight (one 32 KB
+// run of the workgroup per round).  The loaded words are folded by xor and
+// stored only when the fold equals a fixed improbable value, so the loads
+// cannot be dropped and nothing is written in practice.
+constexpr unsigned kProfStream = 32u;  // HSA_PROF_STREAM
+constexpr int kStreamWG = 512, kStreamThreads = 256, kStreamPerLane = 8;
+constexpr size_t kStreamQuantum = (size_t)kStreamWG * kStreamThreads * kStreamPerLane * 16;
+
+__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                                     size_t rounds,
+                                                                     u32x4* __restrict__ sink) {
+    const u32x4* p = src + (size_t)blockIdx.x * rounds * (kStreamThreads * kStreamPerLane) + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (size_t r = 0; r < rounds; ++r) {
+        u32x4 v[kStreamPerLane];
+#pragma unroll
+        for (int u = 0; u < kStreamPerLane; ++u) v[u] = __builtin_nontemporal_load(p + u * kStreamThreads);
+#pragma unroll
+        for (int u = 0; u < kStreamPerLane; ++u) acc ^= v[u];
+        p += kStreamThreads * kStreamPerLane;
+    }
+    if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u && acc.z == 0x94d049bbu && acc.w == 0x2545f491u)
+        sink[threadIdx.x] = acc;
 }
 
 }  // namespace
@@ -92,6 +119,18 @@ int hsa_profile_enable(unsigned family_mask) {
     }
     hsa::g_mask.store(family_mask, std::memory_order_relaxed);
     return HSA_OK;
+}
+
+int hsa_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+    if (!src || !sink || bytes == 0 || bytes % hsa::kStreamQuantum != 0 ||
+        (reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(sink) & 15u) != 0)
+        return HSA_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t rounds = bytes / hsa::kStreamQuantum;
+    hsa::ProfScope prof(hsa::kProfStream, st);
+    hipLaunchKernelGGL(hsa::stream_read_kernel, dim3(hsa::kStreamWG), dim3(hsa::kStreamThreads), 0, st,
+                       static_cast<const hsa::u32x4*>(src), rounds, static_cast<hsa::u32x4*>(sink));
+    return hipGetLastError() == hipSuccess ? HSA_OK : HSA_ERR_HIP;
 }
 
 int hsa_profile_read(unsigned family, double* total_ms, long long* launches, int reset) {

@@ -518,10 +518,29 @@ enum {
     HSA_PROF_SCORE = 2,    /* indexer scoring (+ first-digit histogram)     */
     HSA_PROF_SELECT = 4,   /* top-k select kernels                          */
     HSA_PROF_ATTN = 8,     /* attention kernels (decode split / prefill)    */
-    HSA_PROF_MERGE = 16    /* decode split merge                            */
+    HSA_PROF_MERGE = 16,   /* decode split merge                            */
+    HSA_PROF_STREAM = 32   /* hsa_stream_read calibration kernel            */
 };
 int hsa_profile_enable(unsigned family_mask);
 int hsa_profile_read(unsigned family, double *total_ms, long long *launches, int reset);
+
+/*
+ * Read-bandwidth calibration (diagnostics, not on the hot path): a plain read
+ * of `bytes` bytes at src (device memory, 16-byte aligned) by 512 workgroups
+ * of 256 threads, workgroup g streaming the g-th of 512 equal contiguous
+ * parts with 16-byte non-temporal loads, eight per lane in flight.  That is
+ * the launch shape of the decode scoring kernel at the 1M-context workload
+ * (512 workgroups, each reading one contiguous 512 KB key slot), so the
+ * scoring kernel's duration can be set against what the memory system
+ * delivers to the same shape and byte count.  bytes: a positive multiple of
+ * 16 MiB (512 x 256 x 8 x 16 bytes).  sink: 4096 bytes of device memory,
+ * 16-byte aligned; the kernel stores to it only if the xor of all loaded
+ * words equals one fixed 128-bit value (this keeps the loads), so its
+ * contents are unspecified.  Timed as family HSA_PROF_STREAM when armed.
+ * Returns HSA_ERR_INVALID_ARG for a null or misaligned pointer or a size
+ * that is not such a multiple (nothing is launched).
+ */
+int hsa_stream_read(const void *src, size_t bytes, void *sink, void *stream);
 
 #ifdef __cplusplus
 }

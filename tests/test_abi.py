@@ -187,3 +187,14 @@ def test_decode_step_paged_rejects_bad_shadows(hsa):
     assert call(maps=False) == 1
     assert call(pos=None) == 1
     assert call() == 3                     # well-formed: only the workspace is missing
+
+
+def test_stream_read_rejects_bad_arguments(hsa):
+    lib = hsa.lib
+    mib16 = 16 << 20
+    assert lib.hsa_stream_read(None, mib16, A, None) == 1
+    assert lib.hsa_stream_read(A, mib16, None, None) == 1
+    assert lib.hsa_stream_read(P(4097), mib16, A, None) == 1  # misaligned source
+    assert lib.hsa_stream_read(A, mib16, P(4100), None) == 1  # misaligned sink
+    assert lib.hsa_stream_read(A, 0, A, None) == 1
+    assert lib.hsa_stream_read(A, mib16 + 4096, A, None) == 1  # not a multiple of 16 MiB
