@@ -75,13 +75,13 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
         const int j1 = min(m, j0 + rp);
         const size_t row0 = (size_t)b * T_len + (size_t)m * i;
         // the G rows from j on.  Every load is issued (a row past the part's
-        // range reloads the block's last row and is masked below): a load
-        // under a branch would make the compiler wait for the next group's
-        // loads too before this group's arithmetic.
+        // range reloads the part's last row, which is still cached, and is
+        // masked below): a load under a branch would make the compiler wait
+        // for the next group's loads too before this group's arithmetic.
         auto load = [&](RowGroupB<G>& rg, int j) {
 #pragma unroll
             for (int r = 0; r < G; ++r) {
-                const int jr = min(j + r, m - 1);
+                const int jr = min(j + r, j1 - 1);
                 const size_t off = (row0 + jr) * (size_t)D + (size_t)c * V;
                 rg.g[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gate + off));
                 rg.x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));

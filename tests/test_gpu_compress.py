@@ -25,6 +25,8 @@ CASES = [
     (2, 9, 3, 8, torch.float32),
     (3, 20, 2, 24, torch.float32),
     (4, 1030, 2, 128, torch.float32),
+    (5, 40, 2, 24, torch.float32),   # four threads per unit: one part of the block empty
+    (7, 50, 1, 16, torch.float32),   # parts of 2, 2, 2 and 1 rows
     (16, 100, 1, 64, torch.float32),
     (17, 70, 2, 32, torch.float32),
     (64, 300, 2, 16, torch.float32),
