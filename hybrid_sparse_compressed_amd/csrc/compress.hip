@@ -37,6 +37,15 @@ namespace {
 
 constexpr int kCompressThreads = 256;
 
+// Softmax weights 2^(z - max) on the hardware base-2 exponential: every
+// argument is <= 0, or -inf for a padded row (weight 0), so the library
+// function's range reduction is not needed; a weight below 2^-126 comes out
+// as 0, far below the fp32 resolution of the sum it joins (which holds the
+// maximum row's weight 1).
+__device__ __forceinline__ float exp2_le0(float x) { return __builtin_amdgcn_exp2f(x); }
+// a / s with the hardware reciprocal (within about 1 ulp); s >= 1 here
+__device__ __forceinline__ float div_ge1(float a, float s) { return a * __builtin_amdgcn_rcpf(s); }
+
 // G rows of one chunk, as loaded: gate and latent words (the short-block
 // kernel holds its bias words apart), and gate, bias and latent words.
 template <int G> struct RowGroup {
@@ -114,11 +123,11 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
 #pragma unroll
                 for (int r = 1; r < G; ++r) gm = fmaxf(gm, z[r][e]);
                 const float mn = fmaxf(M[e], gm);
-                const float sc = exp2f(M[e] - mn);  // 0 on the first group (M = -inf)
+                const float sc = exp2_le0(M[e] - mn);  // 0 on the first group (M = -inf)
                 float s = 0.f, a = 0.f;
 #pragma unroll
                 for (int r = 0; r < G; ++r) {
-                    const float w = exp2f(z[r][e] - mn);  // 0 for padded rows
+                    const float w = exp2_le0(z[r][e] - mn);  // 0 for padded rows
                     s += w;
                     if (r < g) a = fmaf(w, chunk_elem<T>(cur.x[r], e), a);
                 }
@@ -149,11 +158,11 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
             float s = 0.f, a = 0.f;
             for (int p = 0; p < P; ++p) {
                 const float mp = sm[p][uu][e];
-                const float w = (mp == -INFINITY) ? 0.f : exp2f(mp - mx);
+                const float w = (mp == -INFINITY) ? 0.f : exp2_le0(mp - mx);
                 s = fmaf(ss[p][uu][e], w, s);
                 a = fmaf(sa[p][uu][e], w, a);
             }
-            res[uu][e] = a / s;
+            res[uu][e] = div_ge1(a, s);
         }
         __syncthreads();
         if (part != 0 || !active) return;
@@ -167,35 +176,73 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
     if (!active) return;
     float r[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) r[e] = A[e] / S[e];
+    for (int e = 0; e < V; ++e) r[e] = div_ge1(A[e], S[e]);
     const size_t o = ((size_t)b * nblk + i) * (size_t)D + (size_t)c * V;
     *reinterpret_cast<u32x4*>(out + o) = pack16<T>(r);
+}
+
+// Division by a divisor fixed for the launch, for dividends below 2^31: one
+// high multiply and a shift with a precomputed multiplier (the round-up
+// method of Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994: l = ceil(log2 d), mul = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (mulhi(mul, n) + n) >> l; the sum stays below 2^32 for n < 2^31).
+struct MagicDiv {
+    uint32_t d, mul;
+    int shift;
+};
+inline MagicDiv make_magic(uint32_t d) {
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t mul = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return MagicDiv{d, (uint32_t)mul, l};
+}
+__device__ __forceinline__ uint32_t magic_div(uint32_t n, const MagicDiv& m) {
+    return (__umulhi(n, m.mul) + n) >> m.shift;
 }
 
 // Short blocks (m <= G): one thread owns a unit (b, i, c); the workgroups stay
 // resident and walk the units tile by tile (a tile = kCompressThreads
 // consecutive units), the next tile's rows in flight during this one.  When
 // the grid's unit stride is a multiple of the chunk count a thread keeps its
-// chunk, so its bias words are loaded once.
-template <typename T, int G>
+// chunk, so its bias words are loaded (and scaled by log2 e) once.  Unit
+// numbers below 2^31 (W64 false) are split into (chunk, block) with the
+// magic divisions above; the kernel is bound by its arithmetic, and 64-bit
+// divisions cost more than the rest of a unit's work.
+template <typename T, int G, bool W64>
 __global__ __launch_bounds__(kCompressThreads) void compress_short_kernel(
     const T* __restrict__ x, const T* __restrict__ gate, const T* __restrict__ bias,
-    T* __restrict__ out, int B, int T_len, int D, int m, int fixed_chunk) {
+    T* __restrict__ out, int B, int T_len, int D, int m, int fixed_chunk, MagicDiv div_chunk,
+    MagicDiv div_blk) {
     constexpr int V = Elem<T>::kPer16B;
     const int nchunk = D / V;
     const int nblk = T_len / m;
     const long long nunits = (long long)B * nblk * nchunk;
     const long long ntiles = (nunits + kCompressThreads - 1) / kCompressThreads;
     const long long stride = gridDim.x;
+    // unit -> its chunk, its block number b * nblk + i and the block's first row
+    auto split = [&](long long unit, int& c, long long& bi, size_t& row0) {
+        if constexpr (W64) {
+            c = (int)(unit % nchunk);
+            bi = unit / nchunk;
+            row0 = (size_t)(bi / nblk) * T_len + (size_t)m * (bi % nblk);
+        } else {
+            const uint32_t u = (uint32_t)unit;
+            const uint32_t q = magic_div(u, div_chunk);
+            const uint32_t b = magic_div(q, div_blk);
+            c = (int)(u - q * (uint32_t)nchunk);
+            bi = q;
+            row0 = (size_t)b * T_len + (size_t)m * (q - b * (uint32_t)nblk);
+        }
+    };
     // Every load is issued, from a clamped unit and row (a unit past the end
     // reloads the last unit, a row past m the block's last row; neither is
     // used): a load under a branch would make the compiler wait for the next
     // tile's loads too before this tile's arithmetic.
     auto load = [&](RowGroup<G>& rg, long long t) {
-        const long long unit = min(t * kCompressThreads + (long long)threadIdx.x, nunits - 1);
-        const int c = (int)(unit % nchunk);
-        const long long bi = unit / nchunk;
-        const size_t row0 = (size_t)(bi / nblk) * T_len + (size_t)m * (bi % nblk);
+        int c;
+        long long bi;
+        size_t row0;
+        split(min(t * kCompressThreads + (long long)threadIdx.x, nunits - 1), c, bi, row0);
 #pragma unroll
         for (int r = 0; r < G; ++r) {
             const size_t off = (row0 + min(r, m - 1)) * (size_t)D + (size_t)c * V;
@@ -204,34 +251,54 @@ __global__ __launch_bounds__(kCompressThreads) void compress_short_kernel(
         }
     };
     u32x4 bw[G];
-    auto load_bias = [&](int c) {
+    float bl[G][V];  // bias * log2 e
+    auto load_bias = [&](long long unit) {
+        int c;
+        long long bi;
+        size_t row0;
+        split(min(unit, nunits - 1), c, bi, row0);
 #pragma unroll
         for (int r = 0; r < G; ++r)
             bw[r] = *reinterpret_cast<const u32x4*>(bias + (size_t)min(r, m - 1) * D + (size_t)c * V);
     };
+    auto scale_bias = [&]() {
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            float bv[V];
+            Elem<T>::unpack(bw[r], bv);
+#pragma unroll
+            for (int e = 0; e < V; ++e) bl[r][e] = bv[e] * kLog2e;
+        }
+    };
     long long t = blockIdx.x;
-    if (fixed_chunk) load_bias((int)(min(t * kCompressThreads + (long long)threadIdx.x, nunits - 1) % nchunk));
+    if (fixed_chunk) {
+        load_bias(t * kCompressThreads + threadIdx.x);
+        scale_bias();
+    }
     RowGroup<G> cur;
     load(cur, t);
     for (; t < ntiles; t += stride) {
         // a thread whose chunk changes from tile to tile loads this tile's
         // bias words before the next tile's rows (the count retires in order)
-        if (!fixed_chunk)
-            load_bias((int)(min(t * kCompressThreads + (long long)threadIdx.x, nunits - 1) % nchunk));
+        if (!fixed_chunk) load_bias(t * kCompressThreads + threadIdx.x);
         RowGroup<G> nxt;
         load(nxt, min(t + stride, ntiles - 1));
         const long long unit = t * kCompressThreads + threadIdx.x;
         if (unit < nunits) {
-            const int c = (int)(unit % nchunk);
+            int c;
+            long long bi;
+            size_t row0;
+            split(unit, c, bi, row0);
+            if (!fixed_chunk) scale_bias();
+            // z = (g + bias) log2 e as one fma per element
             float z[G][V];
 #pragma unroll
             for (int r = 0; r < G; ++r) {
                 if (r < m) {
-                    float gv[V], bv[V];
+                    float gv[V];
                     Elem<T>::unpack(cur.g[r], gv);
-                    Elem<T>::unpack(bw[r], bv);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) z[r][e] = (gv[e] + bv[e]) * kLog2e;
+                    for (int e = 0; e < V; ++e) z[r][e] = fmaf(gv[e], kLog2e, bl[r][e]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < V; ++e) z[r][e] = -INFINITY;
@@ -246,20 +313,19 @@ __global__ __launch_bounds__(kCompressThreads) void compress_short_kernel(
                 float s = 0.f, a = 0.f;
 #pragma unroll
                 for (int r = 0; r < G; ++r) {
-                    const float w = exp2f(z[r][e] - gm);  // 0 for padded rows
+                    const float w = exp2_le0(z[r][e] - gm);  // 0 for padded rows
                     s += w;
                     if (r < m) a = fmaf(w, chunk_elem<T>(cur.x[r], e), a);
                 }
-                res[e] = a / s;
+                res[e] = div_ge1(a, s);
             }
-            *reinterpret_cast<u32x4*>(out + (size_t)(unit / nchunk) * D + (size_t)c * V) =
-                pack16<T>(res);
+            *reinterpret_cast<u32x4*>(out + (size_t)bi * D + (size_t)c * V) = pack16<T>(res);
         }
         cur = nxt;
     }
 }
 
-// resident workgroups of compress_short_kernel<T, G> on the current device
+// resident workgroups of compress_short_kernel<T, G, false> on the current device
 template <typename T, int G>
 int short_kernel_capacity() {
     static std::mutex mu;
@@ -270,7 +336,7 @@ int short_kernel_capacity() {
     if (cap[dev] == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(&compress_short_kernel<T, G>),
+                &per_cu, reinterpret_cast<const void*>(&compress_short_kernel<T, G, false>),
                 kCompressThreads, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -298,10 +364,17 @@ hipError_t launch_compress_short(const void* x, const void* g, const void* bias,
     } else if (grid == ntiles && ntiles <= 1) {
         fixed = 1;  // one tile: nothing to keep across tiles
     }
+    const MagicDiv dc = make_magic((uint32_t)nchunk), db = make_magic((uint32_t)std::max(1, T_len / m));
     ProfScope prof(kProfCompress, st);
-    hipLaunchKernelGGL((compress_short_kernel<T, G>), dim3((unsigned)grid), dim3(kCompressThreads),
-                       0, st, (const T*)x, (const T*)g, (const T*)bias, (T*)out, B, T_len, D, m,
-                       fixed);
+    // unit numbers (clamped ones included) below 2^31: the 32-bit split
+    if ((ntiles + 1) * kCompressThreads < (1ll << 31))
+        hipLaunchKernelGGL((compress_short_kernel<T, G, false>), dim3((unsigned)grid),
+                           dim3(kCompressThreads), 0, st, (const T*)x, (const T*)g, (const T*)bias,
+                           (T*)out, B, T_len, D, m, fixed, dc, db);
+    else
+        hipLaunchKernelGGL((compress_short_kernel<T, G, true>), dim3((unsigned)grid),
+                           dim3(kCompressThreads), 0, st, (const T*)x, (const T*)g, (const T*)bias,
+                           (T*)out, B, T_len, D, m, fixed, dc, db);
     return hipGetLastError();
 }
 

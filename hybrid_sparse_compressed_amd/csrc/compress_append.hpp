@@ -16,11 +16,16 @@ template <> __device__ __forceinline__ u32x4 pack16<float>(const float* v) {
     return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                  __float_as_uint(v[3])};
 }
+// bf16: gfx950's paired conversion (round to nearest even, NaN kept quiet),
+// two elements per instruction
 template <> __device__ __forceinline__ u32x4 pack16<bf16_t>(const float* v) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     u32x4 r;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-        r[w] = (uint32_t)f32_to_bf16(v[2 * w]) | ((uint32_t)f32_to_bf16(v[2 * w + 1]) << 16);
+    for (int w = 0; w < 4; ++w) {
+        const bf16x2 p = {(__bf16)v[2 * w], (__bf16)v[2 * w + 1]};
+        r[w] = __builtin_bit_cast(uint32_t, p);
+    }
     return r;
 }
 
