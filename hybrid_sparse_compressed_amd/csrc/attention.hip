@@ -156,6 +156,13 @@ __device__ __forceinline__ float quad4_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// 2^x for the softmax weights on the hardware base-2 exponential: every
+// argument is a difference from a running maximum (<= 0, or -inf for a
+// masked row: 0), so the library function's range reduction is not needed; a
+// weight below 2^-126 comes out as 0, far below the resolution of the sum it
+// joins, which holds the maximum row's weight 1.
+__device__ __forceinline__ float exp2_le0(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // four P values -> bf16 with the hardware conversion (round to nearest even)
 __device__ __forceinline__ uint2 pack_p4(float a, float b, float c, float d) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         float wsum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[r] = wmax == -INFINITY ? 0.f : exp2f(x[r] - wmax);
+            p[r] = wmax == -INFINITY ? 0.f : exp2_le0(x[r] - wmax);
             wsum += p[r];
         }
         wsum = quad4_sum(wsum);
@@ -566,14 +573,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         for (int w = 0; w < kNW; ++w) tmax = fmaxf(tmax, red_m[w][hl]);
         const bool move = tmax > m_run + 8.f;
         const float m_new = move ? tmax : m_run;
-        const float alpha = move ? exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
+        const float alpha = move ? exp2_le0(m_run - m_new) : 1.f;  // 0 when m_run = -inf
         float tsum = 0.f;
 #pragma unroll
         for (int w = 0; w < kNW; ++w) {
             const float mw = red_m[w][hl];
-            if (mw != -INFINITY) tsum += red_s[w][hl] * exp2f(mw - m_new);
+            if (mw != -INFINITY) tsum += red_s[w][hl] * exp2_le0(mw - m_new);
         }
-        const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
+        const float sc = wmax == -INFINITY ? 0.f : exp2_le0(wmax - m_new);
         // P^T rows of this wave (bf16: in the PV k-slot order, p_pos; fp32: natural)
         if constexpr (sizeof(T) == 2) {
             *reinterpret_cast<uint2*>(Pt + (size_t)hl * L::kStrideT + p_pos(wave * 16 + quad * 4)) =
@@ -999,7 +1006,7 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             float wsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                p[r] = wmax == -INFINITY ? 0.f : exp2f(x[r] - wmax);
+                p[r] = wmax == -INFINITY ? 0.f : exp2_le0(x[r] - wmax);
                 wsum += p[r];
             }
             wsum = quad4_sum(wsum);
@@ -1030,12 +1037,12 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             const float tmax = fmaxf(rm[0], rm[1]);
             const bool move = tmax > m_run + 8.f;   // lazy rescale, p stays <= 2^8
             const float m_new = move ? tmax : m_run;
-            const float alpha = move ? exp2f(m_run - m_new) : 1.f;
+            const float alpha = move ? exp2_le0(m_run - m_new) : 1.f;
             float tsum = 0.f;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
-                if (rm[h2] != -INFINITY) tsum += rs[h2] * exp2f(rm[h2] - m_new);
-            const float sc = wmax == -INFINITY ? 0.f : exp2f(wmax - m_new);
+                if (rm[h2] != -INFINITY) tsum += rs[h2] * exp2_le0(rm[h2] - m_new);
+            const float sc = wmax == -INFINITY ? 0.f : exp2_le0(wmax - m_new);
             T* pbase = Kc + (size_t)head * L::kStrideK + DV;  // P^T row of this head
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {  // P^T in the PV k-slot order (p_pos)
@@ -1158,7 +1165,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
     }
     __syncthreads();
     const float mx = stat[0];
-    const float wgt = (tid < n_split && ms != -INFINITY) ? exp2f(ms - mx) : 0.f;
+    const float wgt = (tid < n_split && ms != -INFINITY) ? exp2_le0(ms - mx) : 0.f;
     __syncthreads();
     wsp[tid] = wgt;
     lsp[tid] = ls * wgt;
