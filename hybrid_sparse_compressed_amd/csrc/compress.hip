@@ -200,14 +200,14 @@ __device__ __forceinline__ uint32_t magic_div(uint32_t n, const MagicDiv& m) {
     return (__umulhi(n, m.mul) + n) >> m.shift;
 }
 
-// Short blocks (m <= G): one thread owns a unit (b, i, c); the workgroups stay
-// resident and walk the units tile by tile (a tile = kCompressThreads
-// consecutive units), the next tile's rows in flight during this one.  When
-// the grid's unit stride is a multiple of the chunk count a thread keeps its
-// chunk, so its bias words are loaded (and scaled by log2 e) once.  Unit
-// numbers below 2^31 (W64 false) are split into (chunk, block) with the
-// magic divisions above; the kernel is bound by its arithmetic, and 64-bit
-// divisions cost more than the rest of a unit's work.
+// Short blocks (m <= G): one thread owns a unit (b, i, c); a tile is
+// kCompressThreads consecutive units.  Unit numbers below 2^31 (W64 false)
+// are split into (chunk, block) with the magic divisions above (64-bit
+// divisions cost more than the rest of a unit's work) and every workgroup
+// takes one tile.  Larger inputs (W64) keep as many workgroups as fit at once
+// walking the tiles, the next tile's rows in flight during this one; when the
+// grid's unit stride is a multiple of the chunk count a thread keeps its
+// chunk, so its bias words are loaded (and scaled by log2 e) once.
 template <typename T, int G, bool W64>
 __global__ __launch_bounds__(kCompressThreads) void compress_short_kernel(
     const T* __restrict__ x, const T* __restrict__ gate, const T* __restrict__ bias,
@@ -270,62 +270,77 @@ __global__ __launch_bounds__(kCompressThreads) void compress_short_kernel(
             for (int e = 0; e < V; ++e) bl[r][e] = bv[e] * kLog2e;
         }
     };
-    long long t = blockIdx.x;
-    if (fixed_chunk) {
-        load_bias(t * kCompressThreads + threadIdx.x);
-        scale_bias();
-    }
-    RowGroup<G> cur;
-    load(cur, t);
-    for (; t < ntiles; t += stride) {
-        // a thread whose chunk changes from tile to tile loads this tile's
-        // bias words before the next tile's rows (the count retires in order)
-        if (!fixed_chunk) load_bias(t * kCompressThreads + threadIdx.x);
-        RowGroup<G> nxt;
-        load(nxt, min(t + stride, ntiles - 1));
+    // the tile's entries from its rows (cur) and the scaled bias (bl)
+    auto tile = [&](long long t, const RowGroup<G>& cur) {
         const long long unit = t * kCompressThreads + threadIdx.x;
-        if (unit < nunits) {
-            int c;
-            long long bi;
-            size_t row0;
-            split(unit, c, bi, row0);
-            if (!fixed_chunk) scale_bias();
-            // z = (g + bias) log2 e as one fma per element
-            float z[G][V];
+        if (unit >= nunits) return;
+        int c;
+        long long bi;
+        size_t row0;
+        split(unit, c, bi, row0);
+        // z = (g + bias) log2 e as one fma per element
+        float z[G][V];
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            if (r < m) {
+                float gv[V];
+                Elem<T>::unpack(cur.g[r], gv);
+#pragma unroll
+                for (int e = 0; e < V; ++e) z[r][e] = fmaf(gv[e], kLog2e, bl[r][e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) z[r][e] = -INFINITY;
+            }
+        }
+        float res[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            float gm = z[0][e];
+#pragma unroll
+            for (int r = 1; r < G; ++r) gm = fmaxf(gm, z[r][e]);
+            float s = 0.f, a = 0.f;
 #pragma unroll
             for (int r = 0; r < G; ++r) {
-                if (r < m) {
-                    float gv[V];
-                    Elem<T>::unpack(cur.g[r], gv);
-#pragma unroll
-                    for (int e = 0; e < V; ++e) z[r][e] = fmaf(gv[e], kLog2e, bl[r][e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < V; ++e) z[r][e] = -INFINITY;
-                }
+                const float w = exp2_le0(z[r][e] - gm);  // 0 for padded rows
+                s += w;
+                if (r < m) a = fmaf(w, chunk_elem<T>(cur.x[r], e), a);
             }
-            float res[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                float gm = z[0][e];
-#pragma unroll
-                for (int r = 1; r < G; ++r) gm = fmaxf(gm, z[r][e]);
-                float s = 0.f, a = 0.f;
-#pragma unroll
-                for (int r = 0; r < G; ++r) {
-                    const float w = exp2_le0(z[r][e] - gm);  // 0 for padded rows
-                    s += w;
-                    if (r < m) a = fmaf(w, chunk_elem<T>(cur.x[r], e), a);
-                }
-                res[e] = div_ge1(a, s);
-            }
-            *reinterpret_cast<u32x4*>(out + (size_t)bi * D + (size_t)c * V) = pack16<T>(res);
+            res[e] = div_ge1(a, s);
         }
-        cur = nxt;
+        *reinterpret_cast<u32x4*>(out + (size_t)bi * D + (size_t)c * V) = pack16<T>(res);
+    };
+    long long t = blockIdx.x;
+    if constexpr (!W64) {
+        // one tile per workgroup (the launch covers every tile): its rows and
+        // bias go out together, and the hardware keeps each CU's share of the
+        // grid in flight
+        RowGroup<G> cur;
+        load(cur, t);
+        load_bias(t * kCompressThreads + threadIdx.x);
+        scale_bias();
+        tile(t, cur);
+    } else {
+        // resident workgroups walk the tiles, the next tile's rows in flight
+        if (fixed_chunk) {
+            load_bias(t * kCompressThreads + threadIdx.x);
+            scale_bias();
+        }
+        RowGroup<G> cur;
+        load(cur, t);
+        for (; t < ntiles; t += stride) {
+            // a thread whose chunk changes from tile to tile loads this tile's
+            // bias words before the next tile's rows (the count retires in order)
+            if (!fixed_chunk) load_bias(t * kCompressThreads + threadIdx.x);
+            RowGroup<G> nxt;
+            load(nxt, min(t + stride, ntiles - 1));
+            if (!fixed_chunk) scale_bias();
+            tile(t, cur);
+            cur = nxt;
+        }
     }
 }
 
-// resident workgroups of compress_short_kernel<T, G, false> on the current device
+// resident workgroups of compress_short_kernel<T, G, true> on the current device
 template <typename T, int G>
 int short_kernel_capacity() {
     static std::mutex mu;
@@ -336,7 +351,7 @@ int short_kernel_capacity() {
     if (cap[dev] == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(&compress_short_kernel<T, G, false>),
+                &per_cu, reinterpret_cast<const void*>(&compress_short_kernel<T, G, true>),
                 kCompressThreads, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -352,6 +367,18 @@ hipError_t launch_compress_short(const void* x, const void* g, const void* bias,
     const long long nunits = (long long)B * (T_len / m) * nchunk;
     const long long ntiles = (nunits + kCompressThreads - 1) / kCompressThreads;
     if (ntiles <= 0) return hipSuccess;
+    const MagicDiv dc = make_magic((uint32_t)nchunk), db = make_magic((uint32_t)std::max(1, T_len / m));
+    if ((ntiles + 1) * kCompressThreads < (1ll << 31)) {
+        // unit numbers (clamped ones included) below 2^31: the 32-bit split and
+        // one tile per workgroup (faster than the resident walk below once the
+        // kernel's arithmetic stopped bounding it: 112 against 121 us for the
+        // prefill_32k C4 call)
+        ProfScope prof(kProfCompress, st);
+        hipLaunchKernelGGL((compress_short_kernel<T, G, false>), dim3((unsigned)ntiles),
+                           dim3(kCompressThreads), 0, st, (const T*)x, (const T*)g, (const T*)bias,
+                           (T*)out, B, T_len, D, m, 0, dc, db);
+        return hipGetLastError();
+    }
     const int cap = short_kernel_capacity<T, G>();
     if (cap <= 0) return hipErrorInvalidDevice;
     long long grid = std::min<long long>(ntiles, cap);
@@ -364,17 +391,10 @@ hipError_t launch_compress_short(const void* x, const void* g, const void* bias,
     } else if (grid == ntiles && ntiles <= 1) {
         fixed = 1;  // one tile: nothing to keep across tiles
     }
-    const MagicDiv dc = make_magic((uint32_t)nchunk), db = make_magic((uint32_t)std::max(1, T_len / m));
     ProfScope prof(kProfCompress, st);
-    // unit numbers (clamped ones included) below 2^31: the 32-bit split
-    if ((ntiles + 1) * kCompressThreads < (1ll << 31))
-        hipLaunchKernelGGL((compress_short_kernel<T, G, false>), dim3((unsigned)grid),
-                           dim3(kCompressThreads), 0, st, (const T*)x, (const T*)g, (const T*)bias,
-                           (T*)out, B, T_len, D, m, fixed, dc, db);
-    else
-        hipLaunchKernelGGL((compress_short_kernel<T, G, true>), dim3((unsigned)grid),
-                           dim3(kCompressThreads), 0, st, (const T*)x, (const T*)g, (const T*)bias,
-                           (T*)out, B, T_len, D, m, fixed, dc, db);
+    hipLaunchKernelGGL((compress_short_kernel<T, G, true>), dim3((unsigned)grid),
+                       dim3(kCompressThreads), 0, st, (const T*)x, (const T*)g, (const T*)bias,
+                       (T*)out, B, T_len, D, m, fixed, dc, db);
     return hipGetLastError();
 }
 
