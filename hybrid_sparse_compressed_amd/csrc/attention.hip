@@ -264,17 +264,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
         vr0 = blockIdx.x * a.rows_per_split;
         vr1 = min(a.max_rows, vr0 + a.rows_per_split);
     }
-    int n_swa, n_comp;
+    int n_swa, n_comp, n_fc = 0;  // n_fc (fused): the sequence's candidates, clamped to [0, S_max]
     if constexpr (PREFILL) {
         n_swa = 0;
         int vis = (qpos + 1) / a.m;
         n_comp = vis < a.S_max ? vis : a.S_max;
     } else {
-        n_swa = a.swa_len[b];
-        n_swa = n_swa < 0 ? 0 : (n_swa > a.W ? a.W : n_swa);
-        if (a.pg_swa.map && a.pos[b] < 0) n_swa = 0;  // paged: no query token, no window
-        n_comp = a.comp_len[b];
-        n_comp = n_comp < 0 ? 0 : (n_comp > a.S_max ? a.S_max : n_comp);
+        // The sequence's counts are read together, in one memory round trip
+        // ahead of the select (the asm statement uses all four, so none of the
+        // loads is moved behind the wait for another).
+        int sw = a.swa_len[b];
+        int cl = a.comp_len[b];
+        int ps = (a.pg_swa.map ? a.pos : a.swa_len)[b];  // paged: the query token's position
+        int nc = FUSED ? a.n_cand[b] : 0;
+        asm volatile("" : "+s"(sw), "+s"(cl), "+s"(ps), "+s"(nc));
+        n_swa = sw < 0 ? 0 : (sw > a.W ? a.W : sw);
+        if (a.pg_swa.map && ps < 0) n_swa = 0;  // paged: no query token, no window
+        n_comp = cl < 0 ? 0 : (cl > a.S_max ? a.S_max : cl);
+        n_fc = nc < 0 ? 0 : (nc > a.S_max ? a.S_max : nc);
     }
 
     // Fused: finish the sequence's select and keep this workgroup's list
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     if constexpr (FUSED) {
         const sel::QWs Wq = sel::ws_of(a.sel_ws, b, a.S_max, a.k);
         const sel::SelLds SL = sel_lds_at(lds_raw);
-        const int n = sel::clamp_n(a.n_cand, b, a.S_max);
+        const int n = n_fc;
         if ((int)blockIdx.x == a.n_split) {  // the sequence's ascending top-k output
             if (hb != 0) return;
             const sel::SelResult R = sel::select_query_lists(
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     if constexpr (FUSED) {
         const sel::QWs Wq = sel::ws_of(a.sel_ws, b, a.S_max, a.k);
         const sel::SelLds SL = sel_lds_at(lds_raw);
-        const int n = sel::clamp_n(a.n_cand, b, a.S_max);
+        const int n = n_fc;
         if (vr1 > a.W) {  // uniform: this workgroup has compressed rows
             f_j0 = max(0, vr0 - a.W);
             const int j1 = min(a.k, vr1 - a.W);
@@ -730,6 +737,43 @@ __device__ inline int dense_tiles_per_split(const AttnArgs& a) {
     return max(1, max(ceil_div(sum, kDenseTarget), ceil_div(mx, kMaxSplit)));
 }
 
+// Up to one wave of sequences: lane i reads sequence i's two lengths (both
+// loads in one round trip), and the plan, the search for split g and that
+// split's own lengths all come from the lanes, with no further memory read.
+// Same plan as dense_tiles_per_split + dense_locate.  False past the last
+// split; otherwise *b, *split, *first, *R, *count (the sequence's splits),
+// *comp (its comp_len, clamped) and *swa (its swa_len, unclamped).
+struct DenseSplit { int b, split, first, R, count, comp, swa; };
+__device__ inline bool dense_locate_wave(const AttnArgs& a, int g, DenseSplit* d) {
+    const int lane = lane_id();
+    const int i = min(lane, a.n_seq - 1);  // unconditional loads: no wait between them
+    int cl = a.comp_len[i];
+    int sl = a.swa_len[i];
+    asm volatile("" : "+v"(cl), "+v"(sl));  // both used here: the swa load is not sunk to its late use
+    const int cc = cl < 0 ? 0 : (cl > a.S_max ? a.S_max : cl);
+    const int t = lane < a.n_seq ? ceil_div(a.W + cc, kP64Rows) : 0;
+    int sum = t, mx = t;
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        sum += __shfl_xor(sum, o, kWave);
+        mx = max(mx, __shfl_xor(mx, o, kWave));
+    }
+    const int R = max(1, max(ceil_div(sum, kDenseTarget), ceil_div(mx, kMaxSplit)));
+    const int n = ceil_div(t, R);
+    const int incl = (int)wave_incl_scan((uint32_t)n);
+    const int excl = incl - n;
+    const unsigned long long hit = __ballot(n > 0 && excl <= g && g < incl);
+    if (!hit) return false;
+    const int src = (int)__ffsll(hit) - 1;
+    d->b = src;
+    d->first = __shfl(excl, src, kWave);
+    d->split = g - d->first;
+    d->R = R;
+    d->count = __shfl(n, src, kWave);
+    d->comp = __shfl(cc, src, kWave);
+    d->swa = __shfl(sl, src, kWave);
+    return true;
+}
+
 // the sequence and split of split g; false past the last split
 __device__ inline bool dense_locate(const AttnArgs& a, int R, int g, int* b, int* split, int* first) {
     int base = 0;
@@ -807,24 +851,45 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     const int head = hb * 16 + hl;
     const bool head_ok = head < a.H;
 
+    // The zero row's address is read from the global offset table.  Decode
+    // splits gather a tile or two: they take it here, beside the kernel
+    // arguments, instead of in front of their first gather.
+    const T* zrow = reinterpret_cast<const T*>(g_p64_zero_row);
+    if constexpr (DEC) asm volatile("" : "+s"(zrow));
+
     int b, pq = 0, qpos = 0, n_comp, n_swa = 0, vr0 = 0, vr1 = a.max_rows;
     int part = 0;  // decode: this split's partial slot
     if constexpr (DEC) {
+        bool have_len = false;
         if (a.dense_plan) {
             // split g of the device plan: R tiles of sequence b from tile R * split
-            const int R = dense_tiles_per_split(a);
-            int split, first;
-            if (!dense_locate(a, R, (int)blockIdx.x, &b, &split, &first)) return;  // uniform
+            int R, split, first, count;
+            if (a.n_seq <= kWave) {
+                DenseSplit d;
+                if (!dense_locate_wave(a, (int)blockIdx.x, &d)) return;  // uniform
+                b = d.b;
+                split = d.split;
+                first = d.first;
+                R = d.R;
+                count = d.count;
+                n_comp = d.comp;
+                n_swa = d.swa;
+                have_len = true;
+            } else {
+                R = dense_tiles_per_split(a);
+                if (!dense_locate(a, R, (int)blockIdx.x, &b, &split, &first)) return;  // uniform
+                count = ceil_div(dense_tiles(a, b), R);
+            }
             // uniform values: scalar registers (the vector ones are all taken by the tiles)
             b = __builtin_amdgcn_readfirstlane(b);
             split = __builtin_amdgcn_readfirstlane(split);
             first = __builtin_amdgcn_readfirstlane(first);
+            R = __builtin_amdgcn_readfirstlane(R);
             vr0 = split * R * kP64Rows;
             vr1 = vr0 + R * kP64Rows;
             part = first + split;
             // the sequence's first split hands its (first, count) to the merge
-            if (split == 0 && tid == 0)
-                a.dense_seq_plan[b] = first | (ceil_div(dense_tiles(a, b), R) << 16);
+            if (split == 0 && tid == 0) a.dense_seq_plan[b] = first | (count << 16);
         } else {
             // decode split: workgroup (split x, sequence y) takes rows [vr0, vr1)
             b = blockIdx.y;
@@ -832,9 +897,13 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
             vr1 = min(a.max_rows, vr0 + a.rows_per_split);
             part = b * a.n_split + (int)blockIdx.x;
         }
-        n_swa = __builtin_amdgcn_readfirstlane(a.swa_len[b]);
+        if (!have_len) {
+            n_swa = a.swa_len[b];
+            n_comp = a.comp_len[b];
+        }
+        n_swa = __builtin_amdgcn_readfirstlane(n_swa);
         n_swa = n_swa < 0 ? 0 : (n_swa > a.W ? a.W : n_swa);
-        n_comp = __builtin_amdgcn_readfirstlane(a.comp_len[b]);
+        n_comp = __builtin_amdgcn_readfirstlane(n_comp);
         n_comp = n_comp < 0 ? 0 : (n_comp > a.S_max ? a.S_max : n_comp);
     } else {
         // queries go to XCDs in contiguous ranges (workgroup L runs on XCD L % 8),
@@ -902,7 +971,8 @@ __global__ __launch_bounds__(kP64Threads) void prefill64_kernel(AttnArgs a) {
     static_assert(DQK <= kP64ZeroRow, "zero row");
     typedef const __attribute__((address_space(1))) u32x4 gu32x4;
     auto issue_part = [&](const T* pr, int it0, int it1) {
-        const T* src = (pr ? pr : reinterpret_cast<const T*>(g_p64_zero_row)) + (tid & 7) * V16;
+        const T* z = DEC ? zrow : reinterpret_cast<const T*>(g_p64_zero_row);
+        const T* src = (pr ? pr : z) + (tid & 7) * V16;
 #pragma unroll
         for (int it = it0; it < it1; ++it)
             ga[it] = *(gu32x4*)(src + 8 * it * V16);
