@@ -154,6 +154,26 @@ def test_decode_dense_64_heads_long_and_short(oracle):
                   "dense 64-head long and short")
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_decode_dense_64_heads_plan_lane_boundary(oracle, B):
+    """64 sequences: each lane of one wave reads one sequence's lengths and the
+    split's own lengths come from the lanes; 65: the plan loops over the
+    sequences and each split reads its lengths again.  Ragged lengths with
+    empty windows and empty compressed pools at both ends of the batch."""
+    g = torch.Generator().manual_seed(4100 + B)
+    W, S = 128, 192
+    q = _rand((B, 64, 576), torch.bfloat16, g)
+    swa = _rand((B, W, 576), torch.bfloat16, g)
+    comp = _rand((B, S, 576), torch.bfloat16, g)
+    swa_len = torch.randint(0, W + 1, (B,), generator=g, dtype=torch.int32)
+    comp_len = torch.randint(0, S + 1, (B,), generator=g, dtype=torch.int32)
+    swa_len[0], comp_len[0] = 0, S
+    swa_len[-1], comp_len[-1] = W, 0
+    swa_len[B // 2], comp_len[B // 2] = 1, 1
+    _check_decode(oracle, q, swa, swa_len, comp, comp_len, 1.0 / 24.0, 512, None,
+                  "dense 64-head plan, %d sequences" % B)
+
+
 def test_decode_is_deterministic():
     from hybrid_sparse_compressed_amd import workloads
 
